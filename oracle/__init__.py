@@ -1,0 +1,24 @@
+"""CPU fp64 oracle of the TokenGate gated-prefill path.
+
+TEST INFRASTRUCTURE ONLY.  Only the test suite, the package smoke check and the
+benchmark's CPU-baseline leg may import this package.  The product path (the
+HIP kernels behind the C ABI and their Python binding) never calls it, and this
+package never imports the product.
+
+Source: "Researchers from Stanford and UC Berkeley Introduce TokenGate:
+Token-Gated Attention Makes Long-Context Prefill Up to 11.3x Faster"
+(MarkTechPost, October 2026), cited below as "the article" with its section
+headings.  Every function is pinned by tests against something other than
+itself (library routines, brute force, closed forms, invariants); none is
+"parity unpinned".
+"""
+
+from .tokengate import (  # noqa: F401
+    attention_rows_for_check,
+    compact,
+    gate_scores,
+    gated_attention,
+    plan,
+    round_f32,
+    select_topk,
+)

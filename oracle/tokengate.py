@@ -1,0 +1,216 @@
+"""Plain, slow, obviously correct fp64 definitions of the gated-prefill steps.
+
+TEST INFRASTRUCTURE ONLY (see the package docstring): never called by the
+product path.
+
+Citations name sections of the article "Researchers from Stanford and UC
+Berkeley Introduce TokenGate: Token-Gated Attention Makes Long-Context Prefill
+Up to 11.3x Faster" (MarkTechPost).  Where the article is silent the reading
+taken is stated at the function; the article gives the ingredients of the
+attention bias but no formula, so the formula used is
+``logit_ij = tau * q_i . k_j / sqrt(d) + g_h * s_j`` with ``s_j = 0`` for keys
+outside the document.
+
+All floating-point work is numpy float64.  Inputs may be any real dtype
+(bf16/fp32 values upcast exactly).  Integer and index results are exact.
+"""
+
+from __future__ import annotations
+
+import math
+from typing import Optional, Sequence, Tuple
+
+import numpy as np
+
+_ROW_CHUNK = 1024  # output rows evaluated per numpy call (memory bound only)
+
+
+def _f64(x) -> np.ndarray:
+    return np.asarray(x, dtype=np.float64)
+
+
+def _i64(x) -> np.ndarray:
+    return np.asarray(x, dtype=np.int64)
+
+
+def plan(cu_seqlens, doc_begin, doc_end, budget) -> Tuple[np.ndarray, int]:
+    """Kept-token count of every prompt, as an exclusive prefix ``cu_kept``.
+
+    Article, "How does TokenGate learned token pruning work?": only the
+    document may be pruned and the question is always kept; "How do you deploy
+    TokenGate?": ``generate`` takes a budget on kept prefill tokens.  Reading:
+    the budget counts document tokens, so prompt b keeps
+    ``min(budget_b, doc_len_b)`` document tokens plus every token outside its
+    document.  Returns (cu_kept int64 [B+1], longest kept prompt).
+    """
+    cu = _i64(cu_seqlens)
+    db, de, bud = _i64(doc_begin), _i64(doc_end), _i64(budget)
+    B = bud.shape[0]
+    cu_kept = np.zeros(B + 1, dtype=np.int64)
+    longest = 0
+    for b in range(B):
+        n = cu[b + 1] - cu[b]
+        doc = de[b] - db[b]
+        kept = min(bud[b], doc) + (n - doc)
+        cu_kept[b + 1] = cu_kept[b] + kept
+        longest = max(longest, int(kept))
+    return cu_kept, longest
+
+
+def gate_scores(hidden, W1, b1, w2, b2: float) -> np.ndarray:
+    """Gate score of every token: ``s_t = b2 + sum_f w2_f SiLU(b1_f + W1[f] . h_t)``.
+
+    Article, "How does TokenGate learned token pruning work?": an MLP scores
+    each token from its post-attention residual at the gate layer; TL;DR: the
+    gate is a small MLP.  Reading: one hidden layer with SiLU
+    (``z = a / (1 + e^-a)``), biases on both linear maps, raw scalar output.
+    Returns fp64 [T].  ``b1=None`` means zero bias.
+    """
+    h = _f64(hidden)
+    W = _f64(W1)
+    F = W.shape[0]
+    bias1 = np.zeros(F) if b1 is None else _f64(b1)
+    w = _f64(w2)
+    out = np.empty(h.shape[0], dtype=np.float64)
+    with np.errstate(over="ignore"):
+        for lo in range(0, h.shape[0], 8192):
+            a = h[lo:lo + 8192] @ W.T + bias1[None, :]
+            z = a / (1.0 + np.exp(-a))
+            out[lo:lo + 8192] = z @ w + float(b2)
+    return out
+
+
+def round_f32(x) -> np.ndarray:
+    """Round to float32, nearest-even (the scores' storage precision)."""
+    return np.asarray(x, dtype=np.float64).astype(np.float32)
+
+
+def select_topk(scores, cu_seqlens, doc_begin, doc_end, budget) -> np.ndarray:
+    """Keep flags: per prompt the ``min(budget, doc_len)`` best document tokens
+    plus every non-document token.
+
+    Article, "How does TokenGate learned token pruning work?": a top-K selector
+    keeps the highest-scoring tokens, and only the document is prunable.
+    Readings: ``doc_begin``/``doc_end`` are prompt-relative; order is (score
+    descending, token index ascending), so equal scores go to the lower index;
+    -0.0 equals +0.0; NaN ranks below every number (NaNs tied by index).
+    ``scores`` is the fp32 array actually being selected on.  Returns uint8 [T].
+    """
+    s = np.asarray(scores)
+    cu = _i64(cu_seqlens)
+    db, de, bud = _i64(doc_begin), _i64(doc_end), _i64(budget)
+    keep = np.zeros(s.shape[0], dtype=np.uint8)
+    for b in range(bud.shape[0]):
+        lo, hi = cu[b], cu[b + 1]
+        keep[lo:hi] = 1
+        dlo, dhi = lo + db[b], lo + de[b]
+        keep[dlo:dhi] = 0
+        idx = np.arange(dlo, dhi, dtype=np.int64)
+        v = s[dlo:dhi].astype(np.float64) + 0.0  # -0.0 -> +0.0
+        # lexsort: last key is primary.  -v ascending == v descending; NaN
+        # stays NaN and numpy sorts NaN last.
+        order = np.lexsort((idx, -v))
+        k = int(min(bud[b], dhi - dlo))
+        keep[idx[order[:k]]] = 1
+    return keep
+
+
+def compact(hidden, pos, scores, keep, cu_seqlens, doc_begin, doc_end):
+    """Stable gather of the kept tokens.
+
+    Article, "How does TokenGate learned token pruning work?": layers above
+    the gate process only the kept tokens; "What is token-gated attention?":
+    each kept token's score becomes its attention bias.  Readings: kept tokens
+    keep their original order (prompt by prompt, ascending index) and original
+    positions; a kept token outside the document has bias +0.0.
+    Returns (hidden_k [Kt, D] same dtype as ``hidden``, pos_k int32 [Kt],
+    bias_s float32 [Kt], kept_idx int64 [Kt]).
+    """
+    keep = np.asarray(keep)
+    cu = _i64(cu_seqlens)
+    db, de = _i64(doc_begin), _i64(doc_end)
+    T = keep.shape[0]
+    in_doc = np.zeros(T, dtype=bool)
+    for b in range(db.shape[0]):
+        in_doc[cu[b] + db[b]:cu[b] + de[b]] = True
+    kept_idx = np.nonzero(keep)[0].astype(np.int64)
+    hidden_k = np.asarray(hidden)[kept_idx]
+    pos_k = np.asarray(pos, dtype=np.int32)[kept_idx]
+    sc = np.asarray(scores, dtype=np.float32)[kept_idx]
+    bias = np.where(in_doc[kept_idx], sc, np.float32(0.0)).astype(np.float32)
+    return hidden_k, pos_k, bias, kept_idx
+
+
+def gated_attention(q, k, v, bias, gain, tau: float, cu_kept,
+                    rows: Optional[Sequence[int]] = None):
+    """Causal GQA attention over the kept tokens with a per-key score bias.
+
+    Article, "What is token-gated attention?": the kept token's gate score is
+    an additive bias on attention logits, scaled by a learnable per-head gain,
+    and a learnable temperature acts on the logits.  For prompt b, query head
+    h (KV head ``h // (Hq / Hkv)``) and kept row i of that prompt:
+    ``x_j = tau * q_i . k_j / sqrt(d) + gain_h * bias_j`` for the prompt's kept
+    rows ``j <= i``; ``o_i = sum_j softmax(x)_j v_j``;
+    ``lse_i = log sum_j exp(x_j)``.  ``gain=None`` drops the bias term.
+
+    ``q`` [Kt, Hq, d], ``k``/``v`` [Kt, Hkv, d], ``bias`` [Kt].  ``rows``
+    restricts evaluation to those global rows (others are NaN).  Returns fp64
+    (o [Kt, Hq, d], lse [Hq, Kt]).
+    """
+    Q, K, V = _f64(q), _f64(k), _f64(v)
+    Kt, Hq, d = Q.shape
+    Hkv = K.shape[1]
+    if Hq % Hkv:
+        raise ValueError("Hq must be a multiple of Hkv")
+    group = Hq // Hkv
+    s = np.zeros(Kt) if bias is None else _f64(bias)
+    g = None if gain is None else _f64(gain)
+    cu = _i64(cu_kept)
+    o = np.full((Kt, Hq, d), np.nan)
+    lse = np.full((Hq, Kt), np.nan)
+    want = None if rows is None else np.unique(_i64(rows))
+    scale = float(tau) / math.sqrt(d)
+    for b in range(cu.shape[0] - 1):
+        lo, hi = int(cu[b]), int(cu[b + 1])
+        if hi == lo:
+            continue
+        if want is None:
+            r = np.arange(lo, hi)
+        else:
+            r = want[(want >= lo) & (want < hi)]
+        for c0 in range(0, r.shape[0], _ROW_CHUNK):
+            rr = r[c0:c0 + _ROW_CHUNK]
+            if rr.size == 0:
+                continue
+            i_rel = rr - lo
+            n_keys = int(i_rel.max()) + 1
+            visible = np.arange(n_keys)[None, :] <= i_rel[:, None]
+            for h in range(Hq):
+                kv = h // group
+                x = scale * (Q[rr, h, :] @ K[lo:lo + n_keys, kv, :].T)
+                if g is not None:
+                    x = x + g[h] * s[lo:lo + n_keys][None, :]
+                x = np.where(visible, x, -np.inf)
+                m = x.max(axis=1)
+                e = np.exp(x - m[:, None])
+                z = e.sum(axis=1)
+                o[rr, h, :] = (e @ V[lo:lo + n_keys, kv, :]) / z[:, None]
+                lse[h, rr] = m + np.log(z)
+    return o, lse
+
+
+def attention_rows_for_check(cu_kept, per_prompt: int, seed: int = 0) -> np.ndarray:
+    """A seeded sample of kept rows: each prompt's first and last row plus
+    ``per_prompt`` rows drawn uniformly (for sizes too large to evaluate whole).
+    Pure index sampling; it computes nothing of the method."""
+    cu = _i64(cu_kept)
+    g = np.random.default_rng(np.random.SeedSequence([int(seed), 7]))
+    out = []
+    for b in range(cu.shape[0] - 1):
+        lo, hi = int(cu[b]), int(cu[b + 1])
+        if hi == lo:
+            continue
+        out.extend([lo, hi - 1])
+        n = min(per_prompt, hi - lo)
+        out.extend(g.choice(np.arange(lo, hi), size=n, replace=False).tolist())
+    return np.unique(np.asarray(out, dtype=np.int64))

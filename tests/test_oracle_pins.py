@@ -1,0 +1,391 @@
+"""Pins of the CPU oracle against things other than itself.
+
+Each test ties one oracle function to a library routine, a brute force, a
+closed form, a hand-worked fixture or an invariant that the TokenGate article
+("Researchers from Stanford and UC Berkeley Introduce TokenGate: Token-Gated
+Attention Makes Long-Context Prefill Up to 11.3x Faster") or plain mathematics
+fixes.  Plausible slips each fail at least one test here: a dropped bias term,
+a wrong SiLU, ties broken the wrong way, -0.0/NaN mishandled, a pruned
+question token, a wrong bias for non-document keys, temperature applied to the
+bias, an off-by-one causal mask, a wrong GQA head map, a wrong softmax scale.
+"""
+
+import itertools
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+import torch
+import torch.nn.functional as F
+from hypothesis import given, settings, strategies as st
+
+import oracle
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _load(name):
+    with open(os.path.join(GOLDEN, name)) as f:
+        return json.load(f)
+
+
+def _num(x):
+    return float(x) if isinstance(x, str) else x
+
+
+# ----------------------------------------------------------------- gate score
+
+def test_gate_hand_worked():
+    g = _load("gate_hand_worked.json")
+    s = oracle.gate_scores(np.array(g["hidden"]), np.array(g["W1"]), np.array(g["b1"]),
+                           np.array(g["w2"]), g["b2"])
+    ln3 = math.log(3.0)
+    want = [c + k * ln3 for c, k in zip(g["expected"]["const"], g["expected"]["ln3_coeff"])]
+    np.testing.assert_allclose(s, want, rtol=0, atol=g["tolerance"])
+
+
+def test_gate_matches_torch_silu_matmul():
+    rng = np.random.default_rng(1)
+    T, D, Fh = 37, 24, 16
+    h = rng.standard_normal((T, D))
+    W1 = rng.standard_normal((Fh, D)) / math.sqrt(D)
+    b1 = rng.standard_normal(Fh) * 0.3
+    w2 = rng.standard_normal(Fh)
+    b2 = -0.7
+    s = oracle.gate_scores(h, W1, b1, w2, b2)
+    th = torch.from_numpy(h)
+    ref = F.silu(th @ torch.from_numpy(W1).T + torch.from_numpy(b1)) @ torch.from_numpy(w2) + b2
+    np.testing.assert_allclose(s, ref.numpy(), rtol=1e-12, atol=1e-12)
+
+
+def test_gate_single_unit_closed_form():
+    # F = 1: s = b2 + w2 * SiLU(b1 + w.h), written with math.exp per token.
+    rng = np.random.default_rng(2)
+    h = rng.standard_normal((9, 5)) * 3
+    w = rng.standard_normal((1, 5))
+    b1, w2, b2 = 0.4, -1.3, 0.2
+    s = oracle.gate_scores(h, w, np.array([b1]), np.array([w2]), b2)
+    for t in range(9):
+        a = b1 + float(np.dot(w[0], h[t]))
+        assert abs(s[t] - (b2 + w2 * a / (1.0 + math.exp(-a)))) < 1e-12
+
+
+def test_gate_large_negative_preactivation_is_finite():
+    # SiLU(a) -> 0 as a -> -inf; the definition stays finite.
+    s = oracle.gate_scores(np.array([[-2000.0]]), np.array([[1.0]]), None, np.array([1.0]), 0.0)
+    assert s[0] == 0.0
+
+
+def test_round_f32_is_nearest_even():
+    # 1 + 2^-24 is halfway between 1 and 1 + 2^-23: ties to even -> 1.
+    x = np.array([1.0 + 2.0 ** -24, 1.0 + 3 * 2.0 ** -24])
+    r = oracle.round_f32(x)
+    assert r.dtype == np.float32
+    assert r[0] == np.float32(1.0) and r[1] == np.float32(1.0 + 2.0 ** -22)
+
+
+# ------------------------------------------------------------------ selection
+
+def _rank_key(v, i):
+    # Independent statement of the order: higher score first, NaN last, equal
+    # scores (including -0.0 == +0.0) by lower index.
+    if v != v:
+        return (1, 0.0, i)
+    return (0, -v, i)
+
+
+def _brute_keep(scores, cu, db, de, bud):
+    keep = [0] * len(scores)
+    for b in range(len(bud)):
+        lo, hi = cu[b], cu[b + 1]
+        doc = list(range(lo + db[b], lo + de[b]))
+        for t in range(lo, hi):
+            if t not in doc:
+                keep[t] = 1
+        ranked = sorted(doc, key=lambda t: _rank_key(float(scores[t]), t))
+        for t in ranked[:min(bud[b], len(doc))]:
+            keep[t] = 1
+    return keep
+
+
+def test_select_hand_worked():
+    g = _load("select_hand_worked.json")
+    s = np.array([_num(x) for x in g["scores"]], dtype=np.float32)
+    assert math.copysign(1.0, s[3]) < 0  # the fixture really holds -0.0
+    for case in g["cases"]:
+        keep = oracle.select_topk(s, g["cu_seqlens"], g["doc_begin"], g["doc_end"], case["budget"])
+        assert np.nonzero(keep)[0].tolist() == case["kept"], case
+
+
+@pytest.mark.parametrize("n", [1, 2, 3, 4, 5, 6])
+def test_select_exhaustive_small(n):
+    alphabet = [-1.0, -0.0, 0.0, 1.0, float("nan")] if n <= 4 else [-1.0, -0.0, 0.0, 1.0]
+    for vals in itertools.product(alphabet, repeat=n):
+        s = np.array(vals, dtype=np.float32)
+        for k in range(0, n + 3):
+            keep = oracle.select_topk(s, [0, n], [0], [n], [k])
+            assert keep.tolist() == _brute_keep(s, [0, n], [0], [n], [k]), (vals, k)
+
+
+def test_select_matches_library_stable_sort():
+    # numpy's stable argsort on the negated scores is the same order.
+    rng = np.random.default_rng(3)
+    s = rng.integers(-20, 20, size=3000).astype(np.float32) / 4
+    for k in [0, 1, 17, 1499, 3000, 4000]:
+        keep = oracle.select_topk(s, [0, 3000], [0], [3000], [k])
+        order = np.argsort(-s.astype(np.float64), kind="stable")
+        want = np.zeros(3000, np.uint8)
+        want[order[:min(k, 3000)]] = 1
+        assert np.array_equal(keep, want)
+
+
+@st.composite
+def _batches(draw):
+    B = draw(st.integers(1, 4))
+    lens = [draw(st.integers(0, 12)) for _ in range(B)]
+    db, de, bud = [], [], []
+    for n in lens:
+        a = draw(st.integers(0, n))
+        e = draw(st.integers(a, n))
+        db.append(a)
+        de.append(e)
+        bud.append(draw(st.integers(0, e - a + 2)))
+    cu = [0]
+    for n in lens:
+        cu.append(cu[-1] + n)
+    vals = draw(st.lists(st.sampled_from([-2.0, -0.5, -0.0, 0.0, 0.5, 2.0, float("inf"),
+                                          float("-inf"), float("nan"), 1e-38, -1e-45]),
+                         min_size=cu[-1], max_size=cu[-1]))
+    return np.array(vals, dtype=np.float32), cu, db, de, bud
+
+
+@settings(max_examples=400, deadline=None)
+@given(_batches())
+def test_select_invariants(batch):
+    s, cu, db, de, bud = batch
+    keep = oracle.select_topk(s, cu, db, de, bud)
+    assert keep.tolist() == _brute_keep(s, cu, db, de, bud)
+    for b in range(len(bud)):
+        lo, hi = cu[b], cu[b + 1]
+        doc = set(range(lo + db[b], lo + de[b]))
+        kept_doc = [t for t in doc if keep[t]]
+        assert len(kept_doc) == min(bud[b], len(doc))
+        assert all(keep[t] for t in range(lo, hi) if t not in doc)  # question never pruned
+        dropped = [t for t in doc if not keep[t]]
+        for kt in kept_doc:
+            for dt in dropped:
+                a, c = _rank_key(float(s[kt]), kt), _rank_key(float(s[dt]), dt)
+                assert a < c
+
+
+# ------------------------------------------------------------ plan, compaction
+
+def test_plan_closed_form():
+    cu = [0, 10, 10, 25]
+    db, de = [2, 0, 0], [8, 0, 15]
+    cu_kept, longest = oracle.plan(cu, db, de, [3, 5, 100])
+    # prompt 0: 3 doc + 4 non-doc; prompt 1 empty; prompt 2 keeps all 15.
+    assert cu_kept.tolist() == [0, 7, 7, 22] and longest == 15
+    cu_kept, _ = oracle.plan(cu, db, de, [0, 0, 0])
+    assert cu_kept.tolist() == [0, 4, 4, 4]
+
+
+def test_plan_agrees_with_selection_counts():
+    rng = np.random.default_rng(4)
+    for _ in range(50):
+        B = int(rng.integers(1, 6))
+        lens = rng.integers(0, 40, size=B)
+        cu = np.concatenate([[0], np.cumsum(lens)])
+        db = np.array([rng.integers(0, n + 1) for n in lens])
+        de = np.array([rng.integers(a, n + 1) for a, n in zip(db, lens)])
+        bud = rng.integers(0, 50, size=B)
+        s = rng.standard_normal(int(cu[-1])).astype(np.float32)
+        keep = oracle.select_topk(s, cu, db, de, bud)
+        cu_kept, longest = oracle.plan(cu, db, de, bud)
+        for b in range(B):
+            assert int(keep[cu[b]:cu[b + 1]].sum()) == cu_kept[b + 1] - cu_kept[b]
+        assert longest == max(int(x) for x in np.diff(cu_kept))
+
+
+def test_compact_invariants():
+    rng = np.random.default_rng(5)
+    cu = np.array([0, 50, 51, 130])
+    db, de = np.array([3, 0, 10]), np.array([40, 1, 79])
+    bud = np.array([7, 0, 30])
+    T = 130
+    s = rng.standard_normal(T).astype(np.float32)
+    s[5] = -0.0
+    hidden = rng.standard_normal((T, 6)).astype(np.float32)
+    pos = np.concatenate([np.arange(50), np.arange(1), np.arange(79)]).astype(np.int32)
+    keep = oracle.select_topk(s, cu, db, de, bud)
+    hk, pk, bias, idx = oracle.compact(hidden, pos, s, keep, cu, db, de)
+    cu_kept, _ = oracle.plan(cu, db, de, bud)
+    assert hk.shape[0] == cu_kept[-1]
+    assert np.array_equal(hk, hidden[idx]) and hk.dtype == hidden.dtype
+    assert np.all(np.diff(idx) > 0)
+    for b in range(3):
+        rows = slice(cu_kept[b], cu_kept[b + 1])
+        assert np.all(np.diff(pk[rows]) > 0)  # positions preserved, increasing
+        assert np.all((idx[rows] >= cu[b]) & (idx[rows] < cu[b + 1]))
+        for t in range(cu[b], cu[b + 1]):
+            in_doc = cu[b] + db[b] <= t < cu[b] + de[b]
+            if not in_doc:
+                assert t in idx  # every question token present
+    for r, t in enumerate(idx):
+        b = int(np.searchsorted(cu, t, side="right") - 1)
+        in_doc = cu[b] + db[b] <= t < cu[b] + de[b]
+        if in_doc:
+            assert bias[r].view(np.uint32) == s[t].view(np.uint32)
+        else:
+            assert bias[r].view(np.uint32) == np.uint32(0)  # +0.0 exactly
+
+
+# ------------------------------------------------------------------ attention
+
+def _rand_attn(rng, lens, Hq, Hkv, d):
+    Kt = int(sum(lens))
+    cu = np.concatenate([[0], np.cumsum(lens)]).astype(np.int64)
+    q = rng.standard_normal((Kt, Hq, d))
+    k = rng.standard_normal((Kt, Hkv, d))
+    v = rng.standard_normal((Kt, Hkv, d))
+    bias = rng.standard_normal(Kt) * 2
+    gain = rng.uniform(0.5, 2.0, Hq)
+    return cu, q, k, v, bias, gain
+
+
+def test_attention_hand_worked():
+    g = _load("attn_hand_worked.json")
+    o, lse = oracle.gated_attention(np.array(g["q"], float), np.array(g["k"], float),
+                                    np.array(g["v"], float), np.array(g["bias"]),
+                                    np.array(g["gain"]), g["tau"], g["cu_kept"])
+    np.testing.assert_allclose(o, np.array(g["expected_o"], float), atol=g["tolerance"], rtol=0)
+    np.testing.assert_allclose(lse, np.log(np.array(g["expected_lse_ln_of"], float)),
+                               atol=g["tolerance"], rtol=0)
+
+
+def _sdpa(q, k, v, lo, hi, scale, mask_bias=None):
+    Q = torch.from_numpy(q[lo:hi]).permute(1, 0, 2)[None]
+    K = torch.from_numpy(k[lo:hi]).permute(1, 0, 2)[None]
+    V = torch.from_numpy(v[lo:hi]).permute(1, 0, 2)[None]
+    if mask_bias is None:
+        out = F.scaled_dot_product_attention(Q, K, V, is_causal=True, enable_gqa=True, scale=scale)
+    else:
+        out = F.scaled_dot_product_attention(Q, K, V, attn_mask=mask_bias[None], enable_gqa=True,
+                                             scale=scale)
+    return out[0].permute(1, 0, 2).numpy()
+
+
+@pytest.mark.parametrize("Hq,Hkv,d", [(4, 2, 16), (4, 4, 8), (6, 2, 32), (2, 1, 64)])
+def test_attention_plain_equals_sdpa(Hq, Hkv, d):
+    # gain = 0 (or no bias), tau = 1, nothing pruned: plain causal GQA attention.
+    rng = np.random.default_rng(6)
+    lens = [1, 17, 40, 3]
+    cu, q, k, v, bias, gain = _rand_attn(rng, lens, Hq, Hkv, d)
+    for gg in [None, np.zeros(Hq)]:
+        o, _ = oracle.gated_attention(q, k, v, bias, gg, 1.0, cu)
+        for b in range(len(lens)):
+            ref = _sdpa(q, k, v, cu[b], cu[b + 1], None)
+            np.testing.assert_allclose(o[cu[b]:cu[b + 1]], ref, atol=1e-12, rtol=0)
+
+
+@pytest.mark.parametrize("tau", [1.0, 1.1, 1.15, 0.37])
+def test_attention_with_bias_equals_sdpa_float_mask(tau):
+    # SDPA with an additive float mask (causal -inf + g_h * s_j) and
+    # scale = tau / sqrt(d): temperature on q.k only, bias added unscaled.
+    Hq, Hkv, d = 6, 3, 16
+    rng = np.random.default_rng(7)
+    lens = [9, 33]
+    cu, q, k, v, bias, gain = _rand_attn(rng, lens, Hq, Hkv, d)
+    o, _ = oracle.gated_attention(q, k, v, bias, gain, tau, cu)
+    for b in range(len(lens)):
+        lo, hi = cu[b], cu[b + 1]
+        n = hi - lo
+        causal = torch.full((n, n), float("-inf"), dtype=torch.float64).triu(1)
+        m = causal[None] + torch.from_numpy(gain)[:, None, None] * torch.from_numpy(bias[lo:hi])[None, None, :]
+        ref = _sdpa(q, k, v, lo, hi, tau / math.sqrt(d), m)
+        np.testing.assert_allclose(o[lo:hi], ref, atol=1e-12, rtol=0)
+
+
+def test_attention_lse_closed_forms():
+    # q = 0 and a constant bias c: every visible logit is g_h * c, so
+    # lse_i = g_h * c + ln(i + 1) and o_i is the mean of v_0..v_i.
+    Hq, Hkv, d = 4, 2, 8
+    n = 25
+    rng = np.random.default_rng(8)
+    q = np.zeros((n, Hq, d))
+    k = rng.standard_normal((n, Hkv, d))
+    v = rng.standard_normal((n, Hkv, d))
+    c = -1.75
+    gain = np.array([0.5, 1.0, 1.5, 2.0])
+    o, lse = oracle.gated_attention(q, k, v, np.full(n, c), gain, 1.3, [0, n])
+    for h in range(Hq):
+        for i in range(n):
+            assert abs(lse[h, i] - (gain[h] * c + math.log(i + 1))) < 1e-12
+            np.testing.assert_allclose(o[i, h], v[:i + 1, h // 2].mean(axis=0), atol=1e-12)
+
+
+def test_attention_single_visible_key():
+    # The first kept row of every prompt sees only itself: o = v, lse = x_00.
+    Hq, Hkv, d = 4, 2, 16
+    rng = np.random.default_rng(9)
+    cu, q, k, v, bias, gain = _rand_attn(rng, [5, 1, 12], Hq, Hkv, d)
+    tau = 1.15
+    o, lse = oracle.gated_attention(q, k, v, bias, gain, tau, cu)
+    for b in range(3):
+        r = cu[b]
+        for h in range(Hq):
+            np.testing.assert_allclose(o[r, h], v[r, h // 2], atol=1e-14, rtol=0)
+            x00 = tau * float(np.dot(q[r, h], k[r, h // 2])) / math.sqrt(d) + gain[h] * bias[r]
+            assert abs(lse[h, r] - x00) < 1e-12
+
+
+def test_attention_ones_value_rows_sum_to_one():
+    Hq, Hkv, d = 4, 2, 16
+    rng = np.random.default_rng(10)
+    cu, q, k, v, bias, gain = _rand_attn(rng, [30, 7], Hq, Hkv, d)
+    o, _ = oracle.gated_attention(q, k, np.ones_like(v), bias, gain, 1.1, cu)
+    np.testing.assert_allclose(o, 1.0, atol=1e-12, rtol=0)
+
+
+@pytest.mark.parametrize("c", [-7.5, 3.0])
+def test_attention_bias_shift_invariance(c):
+    # Adding c to every key's bias (question keys included) shifts each head's
+    # logits by g_h * c: o unchanged, lse shifted by g_h * c.
+    Hq, Hkv, d = 4, 2, 16
+    rng = np.random.default_rng(11)
+    cu, q, k, v, bias, gain = _rand_attn(rng, [20, 13], Hq, Hkv, d)
+    o0, l0 = oracle.gated_attention(q, k, v, bias, gain, 1.15, cu)
+    o1, l1 = oracle.gated_attention(q, k, v, bias + c, gain, 1.15, cu)
+    np.testing.assert_allclose(o1, o0, atol=1e-12, rtol=0)
+    np.testing.assert_allclose(l1 - l0, gain[:, None] * c + 0 * l0, atol=1e-12, rtol=0)
+
+
+def test_attention_gqa_equals_mha_with_repeated_kv():
+    Hq, Hkv, d = 6, 2, 8
+    rng = np.random.default_rng(12)
+    cu, q, k, v, bias, gain = _rand_attn(rng, [11, 19], Hq, Hkv, d)
+    o, l = oracle.gated_attention(q, k, v, bias, gain, 1.1, cu)
+    kr = np.repeat(k, Hq // Hkv, axis=1)
+    vr = np.repeat(v, Hq // Hkv, axis=1)
+    o2, l2 = oracle.gated_attention(q, kr, vr, bias, gain, 1.1, cu)
+    np.testing.assert_allclose(o, o2, atol=1e-12, rtol=0)
+    np.testing.assert_allclose(l, l2, atol=1e-12, rtol=0)
+
+
+def test_attention_rows_subset_and_prompt_isolation():
+    Hq, Hkv, d = 4, 2, 8
+    rng = np.random.default_rng(13)
+    cu, q, k, v, bias, gain = _rand_attn(rng, [15, 0, 40], Hq, Hkv, d)
+    o, l = oracle.gated_attention(q, k, v, bias, gain, 1.1, cu)
+    rows = oracle.attention_rows_for_check(cu, 5, seed=1)
+    o2, l2 = oracle.gated_attention(q, k, v, bias, gain, 1.1, cu, rows=rows)
+    np.testing.assert_array_equal(o2[rows], o[rows])
+    np.testing.assert_array_equal(l2[:, rows], l[:, rows])
+    # Changing the second non-empty prompt leaves the first untouched.
+    k2 = k.copy()
+    k2[15:] += rng.standard_normal(k2[15:].shape)
+    o3, _ = oracle.gated_attention(q, k2, v, bias, gain, 1.1, cu)
+    np.testing.assert_array_equal(o3[:15], o[:15])
+    assert not np.allclose(o3[15:], o[15:])
