@@ -1,0 +1,240 @@
+"""Gated-prefill throughput on one MI355X.
+
+One step = one pass of the whole gated prefill over one synthetic batch:
+gate MLP score of every token -> per-prompt top-K over the document ->
+stable compaction of kept rows, positions and biases -> the stacked
+token-gated causal GQA attention layers over the kept tokens.  Inputs are
+resident in HBM before the timed region; every step re-runs all of it.
+
+Prints one JSON line (stdout).  Progress goes to stderr.
+"""
+
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2500.0  # MI355X dense bf16 MFMA
+PEAK_HBM_GBS = 8000.0      # MI355X HBM3E
+
+
+def log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=20)
+    p.add_argument("--warmup", type=int, default=3)
+    p.add_argument("--workload", default="qwen3_1p7b_128k")
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--no-phase-events", action="store_true",
+                   help="time only whole steps (no per-phase events inside the timed region)")
+    return p.parse_args()
+
+
+def algorithmic_work(w, Kt, cu_kept):
+    s = w.spec
+    e = 2 if s.dtype == "bf16" else 4
+    T, D, F = w.T, s.D, s.F
+    lens = np.diff(cu_kept).astype(np.float64)
+    attn_flop = 2.0 * s.d * s.Hq * float(np.sum(lens * (lens + 1)))
+    return {
+        "gate_bytes": T * D * e + F * D * e + 4 * T,
+        "gate_flop": 2.0 * T * D * F,
+        "select_bytes": 5 * T,
+        "compact_bytes": T + 2 * Kt * D * e + 16 * Kt,
+        "attn_flop_per_layer": attn_flop,
+        "attn_bytes_per_layer": (2 * s.Hq + 2 * s.Hkv) * s.d * Kt * e,
+    }
+
+
+def cpu_baseline(w, q_layers, cu_kept, Kt):
+    """The fp64 oracle on a bounded sample of the same workload, scaled to the
+    whole step: gate, top-K and compaction on all tokens; attention for one
+    KV group (Hq/Hkv query heads) of one layer over every kept row, scaled by
+    the number of KV groups and layers."""
+    import torch
+    import oracle
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+    except Exception:  # pragma: no cover
+        cores = os.cpu_count() or 1
+    s = w.spec
+    f64 = lambda t: t.to(torch.float64).numpy()  # noqa: E731
+    W1, b1, w2 = f64(w.W1), f64(w.b1), f64(w.w2)
+    t0 = time.perf_counter()
+    s_full = oracle.round_f32(oracle.gate_scores(f64(w.hidden), W1, b1, w2, w.b2))
+    t_gate = time.perf_counter() - t0
+    t0 = time.perf_counter()
+    keep = oracle.select_topk(s_full, w.cu_seqlens, w.doc_begin, w.doc_end, w.budget)
+    t_sel = time.perf_counter() - t0
+    t0 = time.perf_counter()
+    bits = w.hidden.view(torch.int16 if s.dtype == "bf16" else torch.int32).numpy()
+    _, _, bias, _ = oracle.compact(bits, w.positions(), s_full, keep, w.cu_seqlens, w.doc_begin,
+                                   w.doc_end)
+    t_cmp = time.perf_counter() - t0
+    q, k, v, gain = q_layers[0]
+    grp = s.Hq // s.Hkv
+    t0 = time.perf_counter()
+    oracle.gated_attention(f64(q[:, :grp]), f64(k[:, :1]), f64(v[:, :1]), bias,
+                           f64(gain[:grp]), s.tau, cu_kept)
+    t_attn = (time.perf_counter() - t0) * s.Hkv * s.layers
+    total = t_gate + t_sel + t_cmp + t_attn
+    return {
+        "value": w.T / total, "unit": "tokens/s", "cores": int(cores), "kind": "oracle",
+        "sample": (f"fp64 numpy oracle on the same workload: gate, top-K and compaction on all "
+                   f"{w.T} tokens; attention for 1 of {s.Hkv} KV groups of 1 of {s.layers} "
+                   f"layers over all {Kt} kept rows, scaled x{s.Hkv * s.layers}; estimated "
+                   f"step {total:.1f} s"),
+        "seconds": {"gate": t_gate, "select": t_sel, "compact": t_cmp, "attention": t_attn},
+    }
+
+
+def main():
+    args = parse()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py runs on exactly one GPU: the gated prefill is measured on one MI355X; "
+              "multi-GPU runs are not part of this build.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import synth
+    import learned_token_pruning_score_amd as tg
+
+    if not torch.cuda.is_available():
+        raise RuntimeError("bench.py needs a GPU")
+    dev = "cuda:0"
+    t_setup = time.perf_counter()
+    w = synth.make_workload(args.workload, seed=0)
+    s = w.spec
+    gp = tg.GatedPrefill(w.cu_seqlens, w.doc_begin, w.doc_end, w.budget, s.D, w.dtype, device=dev)
+    Kt = gp.Kt
+    hidden, W1, b1, w2 = w.hidden.to(dev), w.W1.to(dev), w.b1.to(dev), w.w2.to(dev)
+    layers_cpu = [synth.attention_inputs(s, l, Kt, seed=0) for l in range(s.layers)]
+    layers = [tuple(t.to(dev) for t in L) for L in layers_cpu]
+    outs = [torch.empty((Kt, s.Hq, s.d), dtype=w.dtype, device=dev) for _ in range(s.layers)]
+    torch.cuda.synchronize()
+    log(f"[bench] workload {s.name}: T={w.T} Kt={Kt} B={w.B} layers={s.layers} "
+        f"setup {time.perf_counter() - t_setup:.1f}s")
+
+    stream = torch.cuda.current_stream()
+    phase_events = not args.no_phase_events
+
+    def step(ev=None):
+        if ev is not None:
+            ev[0].record(stream)
+        tg.tg_gate_score(hidden, W1, b1, w2, w.b2, scores=gp.scores)
+        if ev is not None:
+            ev[1].record(stream)
+        tg.tg_select_topk(gp.scores, gp.cu_seqlens, gp.doc_begin, gp.doc_end, gp.budget,
+                          keep=gp.keep, workspace=gp.ws_select)
+        if ev is not None:
+            ev[2].record(stream)
+        tg.tg_compact(hidden, None, gp.scores, gp.keep, gp.cu_seqlens, gp.doc_begin, gp.doc_end,
+                      Kt, out=(gp.hidden_k, gp.pos_k, gp.bias_s, gp.kept_idx),
+                      workspace=gp.ws_compact)
+        if ev is not None:
+            ev[3].record(stream)
+        for l in range(s.layers):
+            q, k, v, gain = layers[l]
+            tg.tg_gated_attn_fwd(q, k, v, gp.bias_s, gain, s.tau, gp.cu_kept, gp.max_kept_len,
+                                 out=outs[l])
+            if ev is not None:
+                ev[4 + l].record(stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    n_ev = 4 + s.layers
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(n_ev)] for _ in range(args.steps)]
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record(stream)
+    for i in range(args.steps):
+        step(evs[i] if phase_events else None)
+    end.record(stream)
+    torch.cuda.synchronize()
+    total_ms = start.elapsed_time(end)
+    ms_per_step = total_ms / args.steps
+    value = w.T * args.steps / (total_ms / 1e3)
+    log(f"[bench] {args.steps} steps: {ms_per_step:.4f} ms/step, {value:.4g} tokens/s")
+
+    work = algorithmic_work(w, Kt, gp.cu_kept_h)
+    phases = None
+    roof = None
+    if phase_events:
+        def avg(i, j):
+            return float(np.mean([evs[k][i].elapsed_time(evs[k][j]) for k in range(args.steps)]))
+        gate_ms = avg(0, 1)
+        sel_ms = avg(1, 2)
+        cmp_ms = avg(2, 3)
+        attn_ms = [avg(3 + l, 4 + l) for l in range(s.layers)]
+        attn_avg = float(np.mean(attn_ms))
+        sel_phase_ms = gate_ms + sel_ms + cmp_ms
+        phases = {
+            "gate_us": gate_ms * 1e3,
+            "gate_GBps": work["gate_bytes"] / (gate_ms / 1e3) / 1e9,
+            "gate_TFLOPs": work["gate_flop"] / (gate_ms / 1e3) / 1e12,
+            "select_us": sel_ms * 1e3,
+            "compact_us": cmp_ms * 1e3,
+            "compact_GBps": work["compact_bytes"] / (cmp_ms / 1e3) / 1e9,
+            "selection_phase_us": sel_phase_ms * 1e3,
+            "selection_phase_GBps": (work["gate_bytes"] + work["select_bytes"] +
+                                     work["compact_bytes"]) / (sel_phase_ms / 1e3) / 1e9,
+            "attn_us_per_layer": attn_avg * 1e3,
+            "attn_TFLOPs": work["attn_flop_per_layer"] / (attn_avg / 1e3) / 1e12,
+            "attn_layers": s.layers,
+        }
+        achieved = work["attn_flop_per_layer"] / (attn_avg / 1e3) / 1e12
+        roof = {"bound": "mfma", "kernel": "attn_bf16_kernel<128>",
+                "achieved": achieved, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                "frac": achieved / PEAK_BF16_TFLOPS, "traffic": None,
+                "per_launch_flop": work["attn_flop_per_layer"],
+                "avg_launch_us": attn_avg * 1e3}
+        log(f"[bench] phases: {json.dumps(phases)}")
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        log("[bench] timing the CPU oracle on a bounded sample ...")
+        cpu = cpu_baseline(w, layers_cpu, gp.cu_kept_h, Kt)
+        log(f"[bench] cpu baseline: {cpu['value']:.4g} tokens/s ({cpu['sample']})")
+
+    line = {
+        "metric": "gated prefill tokens/s at 128k (score+topK+compact+attn); % MFMA/HBM peak",
+        "value": value,
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if s.dtype == "bf16" else "f32",
+        "data": "synthetic",
+        "config": {"workload": s.name, "T": w.T, "kept": Kt, "prompts": w.B,
+                   "hidden": s.D, "gate_hidden": s.F, "q_heads": s.Hq, "kv_heads": s.Hkv,
+                   "head_dim": s.d, "gated_layers": s.layers, "tau": s.tau},
+        "roofline": roof,
+        "cpu_baseline": cpu,
+        "phases": phases,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,186 @@
+/*
+ * tg.h -- C ABI of the TokenGate gated-prefill library (libtokengate.so).
+ *
+ * TokenGate ("Researchers from Stanford and UC Berkeley Introduce TokenGate:
+ * Token-Gated Attention Makes Long-Context Prefill Up to 11.3x Faster",
+ * MarkTechPost) splits prefill into three phases (section "How does TokenGate
+ * learned token pruning work?"): a standard forward below the gate layer, a
+ * gate module (an MLP scores every token, a top-K selector keeps the best
+ * document tokens, the question is never pruned), and a pruned forward that
+ * sees only the kept tokens.  Section "What is token-gated attention?" turns
+ * each kept token's score into an additive bias on the attention logits, with
+ * a per-head gain and a temperature.  The calls below are the device side of
+ * phases two and three:
+ *
+ *   tg_plan            host-only sizes of the kept set (no device work)
+ *   tg_gate_score      gate MLP score of every token
+ *   tg_select_topk     per-prompt top-K over the document span -> keep flags
+ *   tg_compact         stable gather of kept rows, positions and biases
+ *   tg_gated_attn_fwd  causal GQA attention over the kept tokens with the
+ *                      score bias: logit = tau * q.k / sqrt(d) + g_h * s_j
+ *
+ * Conventions (every call):
+ *   - Pointers are device pointers unless the parameter name ends in _h
+ *     (host).  The caller owns every buffer; the library allocates nothing
+ *     and keeps no state between calls.
+ *   - A call checks its arguments on the host first.  An invalid call
+ *     returns a negative tg_status before any device work and has no side
+ *     effect.  A valid call enqueues its kernels on `stream` (a hipStream_t;
+ *     NULL means the default stream) and returns TG_OK without waiting.  A
+ *     failed launch returns TG_ERR_HIP.
+ *   - Outputs never alias inputs.  Token indices are int32, sizes int64.
+ *   - Packed prompts: prompt b owns tokens [cu_seqlens[b], cu_seqlens[b+1]);
+ *     cu_seqlens[0] == 0, non-decreasing, cu_seqlens[B] == T.  Its document
+ *     is the prompt-relative span [doc_begin[b], doc_end[b]).
+ *   - Every output is bit-reproducible from run to run (no float atomics).
+ */
+#ifndef TOKENGATE_TG_H
+#define TOKENGATE_TG_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define TG_ABI_VERSION 1
+
+typedef enum {
+  TG_OK = 0,
+  TG_ERR_NULL = -1,        /* a required pointer is NULL */
+  TG_ERR_SHAPE = -2,       /* a size or stride is negative or inconsistent */
+  TG_ERR_DTYPE = -3,       /* unknown dtype code */
+  TG_ERR_RANGE = -4,       /* a scalar argument is out of range (e.g. tau not finite) */
+  TG_ERR_ALIGN = -5,       /* a pointer or stride breaks the 16-byte rule */
+  TG_ERR_UNSUPPORTED = -6, /* valid, but a shape this build has no kernel for */
+  TG_ERR_WORKSPACE = -7,   /* workspace NULL or smaller than the *_workspace size */
+  TG_ERR_HIP = -8          /* the HIP runtime reported an error at launch */
+} tg_status;
+
+typedef enum { TG_F32 = 0, TG_BF16 = 1 } tg_dtype;
+
+/* TG_ABI_VERSION of the built library. */
+int tg_abi_version(void);
+
+/* Static, NUL-terminated description of a status code (never NULL). */
+const char* tg_status_string(int status);
+
+/*
+ * Kept-set sizes, on the host (article, "How does TokenGate learned token
+ * pruning work?": only the document is prunable; "How do you deploy
+ * TokenGate?": generation takes a budget on kept prefill tokens).  The budget
+ * counts document tokens: prompt b keeps min(budget_h[b], doc length) document
+ * tokens plus all its other tokens.
+ *
+ * In (host, [B] or [B+1]): cu_seqlens_h, doc_begin_h, doc_end_h, budget_h.
+ * Out (host): cu_kept_h[B+1] exclusive prefix of kept counts (cu_kept_h[B] is
+ * the total Kt), *max_kept_len_h the longest kept prompt.
+ * Errors: TG_ERR_NULL, TG_ERR_SHAPE (B < 0, cu_seqlens not a prefix, a doc span
+ * outside its prompt, a negative budget, Kt > INT32_MAX).
+ */
+int tg_plan(int B, const int32_t* cu_seqlens_h, const int32_t* doc_begin_h,
+            const int32_t* doc_end_h, const int32_t* budget_h,
+            int32_t* cu_kept_h, int32_t* max_kept_len_h);
+
+/*
+ * Gate score of every token (article, "How does TokenGate learned token
+ * pruning work?": an MLP scores each token from its post-attention residual):
+ *     s_t = b2 + sum_f w2[f] * SiLU(b1[f] + sum_k W1[f,k] * hidden[t,k])
+ * with SiLU(a) = a / (1 + exp(-a)), fp32 accumulation and an fp32 epilogue.
+ *
+ * hidden  [T, D] row-major, row stride ld_hidden elements (>= D), dtype.
+ * W1      [F, D] row-major, dtype.   b1 [F] fp32 or NULL (zero).
+ * w2      [F] fp32.  b2 scalar.      scores [T] fp32 out.
+ * Supported: TG_BF16 with D % 64 == 0 and F in {64, 128, 256}, or
+ * TG_F32 with any D >= 1 and 1 <= F <= 1024.  bf16 needs hidden, W1 and the
+ * row stride aligned to 16 bytes.  T == 0 is a no-op.
+ */
+int tg_gate_score(const void* hidden, int64_t ld_hidden, int64_t T, int D,
+                  const void* W1, const float* b1, const float* w2, float b2,
+                  int F, int dtype, float* scores, void* stream);
+
+/* Workspace bytes that tg_select_topk needs for B prompts over T tokens. */
+int tg_select_topk_workspace(int B, int64_t T, size_t* bytes);
+
+/*
+ * Document-only top-K (article, "How does TokenGate learned token pruning
+ * work?": a top-K selector keeps the highest-scoring tokens; only the
+ * document part is prunable).  For each prompt b keeps the k = min(budget[b],
+ * doc length) document tokens ranked first by (score descending, token index
+ * ascending) and every token outside the document.  -0.0 ranks equal to
+ * +0.0; NaN ranks below every number, NaNs tied by index.
+ *
+ * scores [T] fp32; cu_seqlens [B+1], doc_begin/doc_end/budget [B] int32 (all
+ * device, same values as given to tg_plan); keep [T] uint8 out (1 = kept).
+ * workspace: device memory of at least tg_select_topk_workspace() bytes, any
+ * contents on entry, clobbered.  Device arguments are trusted to satisfy the
+ * rules tg_plan checks; T must equal cu_seqlens[B].
+ */
+int tg_select_topk(const float* scores, const int32_t* cu_seqlens,
+                   const int32_t* doc_begin, const int32_t* doc_end,
+                   const int32_t* budget, int B, int64_t T, uint8_t* keep,
+                   void* workspace, size_t workspace_bytes, void* stream);
+
+/* Workspace bytes that tg_compact needs for B prompts over T tokens. */
+int tg_compact_workspace(int B, int64_t T, size_t* bytes);
+
+/*
+ * Stable compaction of the kept tokens (article, "How does TokenGate learned
+ * token pruning work?": layers above the gate process only the kept tokens;
+ * "What is token-gated attention?": the kept token's score becomes its bias).
+ * Kept token t (ascending t, so prompt by prompt) goes to row r = number of
+ * kept tokens before t:
+ *     hidden_out[r, :] = hidden[t, :]            (bytes copied exactly)
+ *     pos_out[r]       = pos[t], or t - cu_seqlens[b] when pos == NULL
+ *     bias_out[r]      = scores[t] inside the document, +0.0 outside
+ *     kept_idx_out[r]  = t                       (optional, may be NULL)
+ *
+ * hidden [T, D] row stride ld_hidden; hidden_out [Kt, D] packed; dtype gives
+ * the element size (the copy is a byte copy).  Kt must equal the number of
+ * kept flags (tg_plan's total).  hidden and hidden_out need element
+ * alignment only; rows move in 16-byte units when the row size, the row
+ * stride and both base pointers are multiples of 16 bytes, else element by
+ * element.  workspace as for tg_select_topk.
+ */
+int tg_compact(const void* hidden, int64_t ld_hidden, int D, int dtype,
+               const int32_t* pos, const float* scores, const uint8_t* keep,
+               const int32_t* cu_seqlens, const int32_t* doc_begin,
+               const int32_t* doc_end, int B, int64_t T, int64_t Kt,
+               void* hidden_out, int32_t* pos_out, float* bias_out,
+               int32_t* kept_idx_out, void* workspace, size_t workspace_bytes,
+               void* stream);
+
+/*
+ * Token-gated causal GQA attention over the kept tokens (article, "What is
+ * token-gated attention?": the kept token's score is an additive logit bias,
+ * refined by a per-head gain and a temperature).  For prompt b (kept rows
+ * [cu_kept[b], cu_kept[b+1])), query head h, KV head h / (Hq / Hkv), and
+ * kept row i:
+ *     x_j  = tau * (q_i . k_j) / sqrt(d) + gain[h] * bias_s[j],  j <= i in b
+ *     o_i  = sum_j softmax(x)_j * v_j
+ *     lse_i = ln sum_j exp(x_j)
+ * gain == NULL drops the bias term (plain causal attention with temperature).
+ *
+ * q [Kt, Hq, d], k and v [Kt, Hkv, d]: heads contiguous inside a token, token
+ * strides in elements (>= heads * d).  bias_s [Kt] fp32 (may be NULL only when
+ * gain is NULL), gain [Hq] fp32, cu_kept [B+1] int32 (device copy of
+ * tg_plan's output), max_kept_len its longest prompt.  out [Kt, Hq, d]
+ * packed, same dtype as q.  lse [Hq, Kt] fp32, or NULL.
+ * Supported: d in {64, 128}, Hq % Hkv == 0.  bf16 runs on MFMA with fp32
+ * accumulation and rounds the softmax weights to bf16 before the value
+ * product; fp32 runs on vector ALUs throughout.  bf16 needs q, k, v, out and
+ * the token strides aligned to 16 bytes.
+ */
+int tg_gated_attn_fwd(const void* q, const void* k, const void* v,
+                      int64_t q_tok_stride, int64_t k_tok_stride,
+                      int64_t v_tok_stride, const float* bias_s,
+                      const float* gain, float tau, const int32_t* cu_kept,
+                      int B, int max_kept_len, int64_t Kt, int Hq, int Hkv,
+                      int d, int dtype, void* out, float* lse, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* TOKENGATE_TG_H */

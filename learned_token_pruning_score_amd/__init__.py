@@ -1,0 +1,29 @@
+"""TokenGate gated-prefill hot path on MI355X (gfx950).
+
+Python face of libtokengate.so: the C ABI calls under the same names
+(``tg_plan``, ``tg_gate_score``, ``tg_select_topk``, ``tg_compact``,
+``tg_gated_attn_fwd``) taking torch device tensors, and ``GatedPrefill``,
+which strings them together the way the three-phase prefill of the TokenGate
+article ("How does TokenGate learned token pruning work?") does.  Every step
+runs in the library's HIP kernels; without the built library or a GPU these
+functions raise.
+"""
+
+from ._lib import (  # noqa: F401
+    LIB_PATH,
+    TG_BF16,
+    TG_F32,
+    SIGNATURES,
+    TokenGateError,
+    load_library,
+    status_string,
+    tg_abi_version,
+    tg_compact,
+    tg_compact_workspace,
+    tg_gate_score,
+    tg_gated_attn_fwd,
+    tg_plan,
+    tg_select_topk,
+    tg_select_topk_workspace,
+)
+from .pipeline import GatedPrefill  # noqa: F401

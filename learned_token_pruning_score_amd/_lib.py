@@ -1,0 +1,267 @@
+"""ctypes binding of libtokengate.so (C ABI declared in include/tg.h).
+
+Argument marshalling only: every function takes torch tensors (device memory
+that torch allocated), checks dtypes and shapes that ctypes cannot see, and
+passes raw pointers plus the current HIP stream.  All computation happens in
+the library's HIP kernels; nothing here has a CPU fallback.  A missing
+library or a missing GPU raises.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional, Tuple
+
+import numpy as np
+import torch
+
+_PKG_DIR = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG_DIR, "libtokengate.so")
+
+TG_OK = 0
+TG_F32 = 0
+TG_BF16 = 1
+
+_c_i64 = ctypes.c_int64
+_c_i32 = ctypes.c_int32
+_c_int = ctypes.c_int
+_c_f32 = ctypes.c_float
+_c_vp = ctypes.c_void_p
+_c_size_p = ctypes.POINTER(ctypes.c_size_t)
+_c_i32_p = ctypes.POINTER(ctypes.c_int32)
+
+# Every exported symbol of include/tg.h with its ctypes signature.
+SIGNATURES = {
+    "tg_abi_version": (_c_int, []),
+    "tg_status_string": (ctypes.c_char_p, [_c_int]),
+    "tg_plan": (_c_int, [_c_int, _c_i32_p, _c_i32_p, _c_i32_p, _c_i32_p, _c_i32_p, _c_i32_p]),
+    "tg_gate_score": (_c_int, [_c_vp, _c_i64, _c_i64, _c_int, _c_vp, _c_vp, _c_vp, _c_f32,
+                               _c_int, _c_int, _c_vp, _c_vp]),
+    "tg_select_topk_workspace": (_c_int, [_c_int, _c_i64, _c_size_p]),
+    "tg_select_topk": (_c_int, [_c_vp, _c_vp, _c_vp, _c_vp, _c_vp, _c_int, _c_i64, _c_vp,
+                                _c_vp, ctypes.c_size_t, _c_vp]),
+    "tg_compact_workspace": (_c_int, [_c_int, _c_i64, _c_size_p]),
+    "tg_compact": (_c_int, [_c_vp, _c_i64, _c_int, _c_int, _c_vp, _c_vp, _c_vp, _c_vp, _c_vp,
+                            _c_vp, _c_int, _c_i64, _c_i64, _c_vp, _c_vp, _c_vp, _c_vp, _c_vp,
+                            ctypes.c_size_t, _c_vp]),
+    "tg_gated_attn_fwd": (_c_int, [_c_vp, _c_vp, _c_vp, _c_i64, _c_i64, _c_i64, _c_vp, _c_vp,
+                                   _c_f32, _c_vp, _c_int, _c_int, _c_i64, _c_int, _c_int, _c_int,
+                                   _c_int, _c_vp, _c_vp, _c_vp]),
+}
+
+_lib = None
+
+
+class TokenGateError(RuntimeError):
+    def __init__(self, fn: str, status: int):
+        self.status = status
+        super().__init__(f"{fn} failed: {status} ({status_string(status)})")
+
+
+def load_library(path: Optional[str] = None) -> ctypes.CDLL:
+    """Load (once) and type the shared library; raises if it was not built."""
+    global _lib
+    if _lib is not None and path is None:
+        return _lib
+    p = path or LIB_PATH
+    if not os.path.exists(p):
+        raise RuntimeError(
+            f"{p} not found: build it with `python -m learned_token_pruning_score_amd.build`")
+    lib = ctypes.CDLL(p)
+    for name, (res, args) in SIGNATURES.items():
+        fn = getattr(lib, name)
+        fn.restype = res
+        fn.argtypes = args
+    if path is None:
+        _lib = lib
+    return lib
+
+
+def status_string(status: int) -> str:
+    return load_library().tg_status_string(int(status)).decode()
+
+
+def _check(fn: str, status: int) -> None:
+    if status != TG_OK:
+        raise TokenGateError(fn, status)
+
+
+def _dtype_code(t: torch.Tensor) -> int:
+    if t.dtype == torch.bfloat16:
+        return TG_BF16
+    if t.dtype == torch.float32:
+        return TG_F32
+    raise TypeError(f"unsupported dtype {t.dtype}")
+
+
+def _dev(t: Optional[torch.Tensor], name: str, dtype=None) -> int:
+    if t is None:
+        return 0
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a GPU tensor")
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    return t.data_ptr()
+
+
+def _stream(stream) -> int:
+    if stream is None:
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, int):
+        return stream
+    return stream.cuda_stream
+
+
+def _require_gpu() -> None:
+    if not torch.cuda.is_available():
+        raise RuntimeError("the TokenGate kernels need a ROCm GPU (gfx950); none is visible")
+
+
+# ---------------------------------------------------------------- entry points
+
+def tg_abi_version() -> int:
+    return int(load_library().tg_abi_version())
+
+
+def tg_plan(cu_seqlens, doc_begin, doc_end, budget) -> Tuple[np.ndarray, int]:
+    """Host-only kept sizes: returns (cu_kept int32 [B+1], max kept length)."""
+    lib = load_library()
+    cu = np.ascontiguousarray(cu_seqlens, dtype=np.int32)
+    db = np.ascontiguousarray(doc_begin, dtype=np.int32)
+    de = np.ascontiguousarray(doc_end, dtype=np.int32)
+    bud = np.ascontiguousarray(budget, dtype=np.int32)
+    B = int(bud.shape[0])
+    if cu.shape[0] != B + 1 or db.shape[0] != B or de.shape[0] != B:
+        raise ValueError("cu_seqlens must have B+1 entries and the others B")
+    out = np.zeros(B + 1, dtype=np.int32)
+    mx = ctypes.c_int32(0)
+    p = lambda a: a.ctypes.data_as(_c_i32_p)  # noqa: E731
+    _check("tg_plan", lib.tg_plan(B, p(cu), p(db), p(de), p(bud), p(out), ctypes.byref(mx)))
+    return out, int(mx.value)
+
+
+def tg_gate_score(hidden: torch.Tensor, W1: torch.Tensor, b1: Optional[torch.Tensor],
+                  w2: torch.Tensor, b2: float, scores: Optional[torch.Tensor] = None,
+                  stream=None) -> torch.Tensor:
+    """Gate scores [T] fp32 of ``hidden`` [T, D] (row stride may exceed D)."""
+    _require_gpu()
+    lib = load_library()
+    T, D = hidden.shape
+    F = W1.shape[0]
+    if hidden.stride(1) != 1 or not W1.is_contiguous() or W1.shape[1] != D:
+        raise ValueError("hidden must have unit column stride and W1 must be [F, D] contiguous")
+    if W1.dtype != hidden.dtype:
+        raise TypeError("W1 and hidden must share a dtype")
+    if scores is None:
+        scores = torch.empty(T, dtype=torch.float32, device=hidden.device)
+    _check("tg_gate_score", lib.tg_gate_score(
+        _dev(hidden, "hidden"), hidden.stride(0) if T > 0 else D, T, D, _dev(W1, "W1"),
+        _dev(b1, "b1", torch.float32), _dev(w2, "w2", torch.float32), float(b2), F,
+        _dtype_code(hidden), _dev(scores, "scores", torch.float32), _stream(stream)))
+    return scores
+
+
+def tg_select_topk_workspace(B: int, T: int) -> int:
+    n = ctypes.c_size_t(0)
+    _check("tg_select_topk_workspace", load_library().tg_select_topk_workspace(B, T, ctypes.byref(n)))
+    return int(n.value)
+
+
+def tg_compact_workspace(B: int, T: int) -> int:
+    n = ctypes.c_size_t(0)
+    _check("tg_compact_workspace", load_library().tg_compact_workspace(B, T, ctypes.byref(n)))
+    return int(n.value)
+
+
+def _workspace(nbytes: int, device) -> torch.Tensor:
+    return torch.empty(max(nbytes, 16), dtype=torch.uint8, device=device)
+
+
+def tg_select_topk(scores: torch.Tensor, cu_seqlens: torch.Tensor, doc_begin: torch.Tensor,
+                   doc_end: torch.Tensor, budget: torch.Tensor, keep: Optional[torch.Tensor] = None,
+                   workspace: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """Keep flags uint8 [T] (metadata tensors are int32 on the device)."""
+    _require_gpu()
+    lib = load_library()
+    T = scores.shape[0]
+    B = budget.shape[0]
+    if keep is None:
+        keep = torch.empty(T, dtype=torch.uint8, device=scores.device)
+    need = tg_select_topk_workspace(B, T)
+    if workspace is None:
+        workspace = _workspace(need, scores.device)
+    _check("tg_select_topk", lib.tg_select_topk(
+        _dev(scores, "scores", torch.float32), _dev(cu_seqlens, "cu_seqlens", torch.int32),
+        _dev(doc_begin, "doc_begin", torch.int32), _dev(doc_end, "doc_end", torch.int32),
+        _dev(budget, "budget", torch.int32), B, T, _dev(keep, "keep", torch.uint8),
+        _dev(workspace, "workspace"), workspace.numel() * workspace.element_size(),
+        _stream(stream)))
+    return keep
+
+
+def tg_compact(hidden: torch.Tensor, pos: Optional[torch.Tensor], scores: torch.Tensor,
+               keep: torch.Tensor, cu_seqlens: torch.Tensor, doc_begin: torch.Tensor,
+               doc_end: torch.Tensor, Kt: int, out: Optional[tuple] = None,
+               with_index: bool = True, workspace: Optional[torch.Tensor] = None, stream=None):
+    """Returns (hidden_k [Kt, D], pos_k int32 [Kt], bias_s fp32 [Kt], kept_idx int32 [Kt] or None)."""
+    _require_gpu()
+    lib = load_library()
+    T, D = hidden.shape
+    B = doc_begin.shape[0]
+    dev = hidden.device
+    if hidden.stride(1) != 1:
+        raise ValueError("hidden must have unit column stride")
+    if out is None:
+        hk = torch.empty((Kt, D), dtype=hidden.dtype, device=dev)
+        pk = torch.empty(Kt, dtype=torch.int32, device=dev)
+        bk = torch.empty(Kt, dtype=torch.float32, device=dev)
+        ik = torch.empty(Kt, dtype=torch.int32, device=dev) if with_index else None
+    else:
+        hk, pk, bk, ik = out
+    need = tg_compact_workspace(B, T)
+    if workspace is None:
+        workspace = _workspace(need, dev)
+    _check("tg_compact", lib.tg_compact(
+        _dev(hidden, "hidden"), hidden.stride(0) if T > 0 else D, D, _dtype_code(hidden),
+        _dev(pos, "pos", torch.int32), _dev(scores, "scores", torch.float32),
+        _dev(keep, "keep", torch.uint8), _dev(cu_seqlens, "cu_seqlens", torch.int32),
+        _dev(doc_begin, "doc_begin", torch.int32), _dev(doc_end, "doc_end", torch.int32), B, T, Kt,
+        _dev(hk, "hidden_out"), _dev(pk, "pos_out", torch.int32),
+        _dev(bk, "bias_out", torch.float32), _dev(ik, "kept_idx_out", torch.int32),
+        _dev(workspace, "workspace"), workspace.numel() * workspace.element_size(),
+        _stream(stream)))
+    return hk, pk, bk, ik
+
+
+def tg_gated_attn_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
+                      bias_s: Optional[torch.Tensor], gain: Optional[torch.Tensor], tau: float,
+                      cu_kept: torch.Tensor, max_kept_len: int, out: Optional[torch.Tensor] = None,
+                      lse: Optional[torch.Tensor] = None, want_lse: bool = False, stream=None):
+    """Token-gated causal GQA attention; q [Kt, Hq, d], k/v [Kt, Hkv, d].
+
+    Returns (out [Kt, Hq, d], lse [Hq, Kt] fp32 or None).
+    """
+    _require_gpu()
+    lib = load_library()
+    Kt, Hq, d = q.shape
+    Hkv = k.shape[1]
+    for name, t, H in (("q", q, Hq), ("k", k, Hkv), ("v", v, Hkv)):
+        if t.dim() != 3 or t.shape[0] != Kt or t.shape[2] != d or t.shape[1] != H:
+            raise ValueError(f"{name} has shape {tuple(t.shape)}")
+        if t.stride(2) != 1 or t.stride(1) != d:
+            raise ValueError(f"{name} must have heads contiguous inside a token")
+        if t.dtype != q.dtype:
+            raise TypeError("q, k, v must share a dtype")
+    B = cu_kept.shape[0] - 1
+    if out is None:
+        out = torch.empty((Kt, Hq, d), dtype=q.dtype, device=q.device)
+    if lse is None and want_lse:
+        lse = torch.empty((Hq, Kt), dtype=torch.float32, device=q.device)
+    _check("tg_gated_attn_fwd", lib.tg_gated_attn_fwd(
+        _dev(q, "q"), _dev(k, "k"), _dev(v, "v"), q.stride(0) if Kt else Hq * d,
+        k.stride(0) if Kt else Hkv * d, v.stride(0) if Kt else Hkv * d,
+        _dev(bias_s, "bias_s", torch.float32), _dev(gain, "gain", torch.float32), float(tau),
+        _dev(cu_kept, "cu_kept", torch.int32), B, int(max_kept_len), Kt, Hq, Hkv, d,
+        _dtype_code(q), _dev(out, "out"), _dev(lse, "lse", torch.float32), _stream(stream)))
+    return out, lse

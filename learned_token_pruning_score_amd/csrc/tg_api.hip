@@ -1,0 +1,187 @@
+// C ABI of the gated-prefill library: argument checks on the host, then
+// asynchronous launches on the caller's stream.  The declarations, with the
+// meaning, layout, ownership and error behaviour of every argument, are in
+// include/tg.h.
+#include <limits.h>
+#include <math.h>
+#include <stdint.h>
+
+#include "../../include/tg.h"
+#include "tg_common.h"
+
+namespace {
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+int elem_bytes(int dtype) { return dtype == TG_BF16 ? 2 : (dtype == TG_F32 ? 4 : 0); }
+
+int from_hip(hipError_t e) { return e == hipSuccess ? TG_OK : TG_ERR_HIP; }
+
+hipStream_t as_stream(void* s) { return reinterpret_cast<hipStream_t>(s); }
+
+}  // namespace
+
+extern "C" {
+
+int tg_abi_version(void) { return TG_ABI_VERSION; }
+
+const char* tg_status_string(int status) {
+  switch (status) {
+    case TG_OK: return "ok";
+    case TG_ERR_NULL: return "a required pointer is NULL";
+    case TG_ERR_SHAPE: return "a size or stride is negative or inconsistent";
+    case TG_ERR_DTYPE: return "unknown dtype code";
+    case TG_ERR_RANGE: return "a scalar argument is out of range";
+    case TG_ERR_ALIGN: return "a pointer or stride is misaligned";
+    case TG_ERR_UNSUPPORTED: return "shape not supported by this build";
+    case TG_ERR_WORKSPACE: return "workspace missing or too small";
+    case TG_ERR_HIP: return "HIP runtime error at launch";
+    default: return "unknown status";
+  }
+}
+
+int tg_plan(int B, const int32_t* cu_seqlens_h, const int32_t* doc_begin_h,
+            const int32_t* doc_end_h, const int32_t* budget_h, int32_t* cu_kept_h,
+            int32_t* max_kept_len_h) {
+  if (B < 0) return TG_ERR_SHAPE;
+  if (!cu_seqlens_h || !cu_kept_h || !max_kept_len_h) return TG_ERR_NULL;
+  if (B > 0 && (!doc_begin_h || !doc_end_h || !budget_h)) return TG_ERR_NULL;
+  if (cu_seqlens_h[0] != 0) return TG_ERR_SHAPE;
+  int64_t acc = 0;
+  int32_t longest = 0;
+  for (int b = 0; b < B; ++b) {
+    const int64_t len = (int64_t)cu_seqlens_h[b + 1] - cu_seqlens_h[b];
+    if (len < 0) return TG_ERR_SHAPE;
+    if (doc_begin_h[b] < 0 || doc_end_h[b] < doc_begin_h[b] || doc_end_h[b] > len)
+      return TG_ERR_SHAPE;
+    if (budget_h[b] < 0) return TG_ERR_SHAPE;
+    const int64_t doc = (int64_t)doc_end_h[b] - doc_begin_h[b];
+    const int64_t kept = (budget_h[b] < doc ? budget_h[b] : doc) + (len - doc);
+    acc += kept;
+    if (acc > INT32_MAX) return TG_ERR_SHAPE;
+    if (kept > longest) longest = (int32_t)kept;
+  }
+  // outputs only after every check passed
+  cu_kept_h[0] = 0;
+  acc = 0;
+  for (int b = 0; b < B; ++b) {
+    const int64_t len = (int64_t)cu_seqlens_h[b + 1] - cu_seqlens_h[b];
+    const int64_t doc = (int64_t)doc_end_h[b] - doc_begin_h[b];
+    acc += (budget_h[b] < doc ? budget_h[b] : doc) + (len - doc);
+    cu_kept_h[b + 1] = (int32_t)acc;
+  }
+  *max_kept_len_h = longest;
+  return TG_OK;
+}
+
+int tg_gate_score(const void* hidden, int64_t ld_hidden, int64_t T, int D, const void* W1,
+                  const float* b1, const float* w2, float b2, int F, int dtype, float* scores,
+                  void* stream) {
+  const int eb = elem_bytes(dtype);
+  if (!eb) return TG_ERR_DTYPE;
+  if (T < 0 || D <= 0 || F <= 0 || ld_hidden < D) return TG_ERR_SHAPE;
+  if (T > INT32_MAX) return TG_ERR_SHAPE;
+  if (!isfinite(b2)) return TG_ERR_RANGE;
+  if (T == 0) return TG_OK;
+  if (!hidden || !W1 || !w2 || !scores) return TG_ERR_NULL;
+  if (dtype == TG_BF16) {
+    if (D % 64 != 0 || !(F == 64 || F == 128 || F == 256)) return TG_ERR_UNSUPPORTED;
+    if (!aligned16(hidden) || !aligned16(W1) || (ld_hidden * 2) % 16 != 0) return TG_ERR_ALIGN;
+    return from_hip(tg::launch_gate_bf16(hidden, ld_hidden, T, D, W1, b1, w2, b2, F, scores,
+                                         as_stream(stream)));
+  }
+  if (F > 1024) return TG_ERR_UNSUPPORTED;
+  return from_hip(tg::launch_gate_f32(static_cast<const float*>(hidden), ld_hidden, T, D,
+                                      static_cast<const float*>(W1), b1, w2, b2, F, scores,
+                                      as_stream(stream)));
+}
+
+int tg_select_topk_workspace(int B, int64_t T, size_t* bytes) {
+  if (!bytes) return TG_ERR_NULL;
+  if (B < 0 || T < 0) return TG_ERR_SHAPE;
+  *bytes = tg::select_workspace_bytes(B, T);
+  return TG_OK;
+}
+
+int tg_select_topk(const float* scores, const int32_t* cu_seqlens, const int32_t* doc_begin,
+                   const int32_t* doc_end, const int32_t* budget, int B, int64_t T, uint8_t* keep,
+                   void* workspace, size_t workspace_bytes, void* stream) {
+  if (B < 0 || T < 0 || T > INT32_MAX) return TG_ERR_SHAPE;
+  if (B == 0 && T != 0) return TG_ERR_SHAPE;
+  if (T == 0 && B == 0) return TG_OK;
+  if (!cu_seqlens || !doc_begin || !doc_end || !budget) return TG_ERR_NULL;
+  if (T > 0 && (!scores || !keep)) return TG_ERR_NULL;
+  if (!workspace || workspace_bytes < tg::select_workspace_bytes(B, T)) return TG_ERR_WORKSPACE;
+  if (!aligned16(workspace)) return TG_ERR_ALIGN;
+  if (T == 0) return TG_OK;
+  return from_hip(tg::launch_select(scores, cu_seqlens, doc_begin, doc_end, budget, B, T, keep,
+                                    workspace, as_stream(stream)));
+}
+
+int tg_compact_workspace(int B, int64_t T, size_t* bytes) {
+  if (!bytes) return TG_ERR_NULL;
+  if (B < 0 || T < 0) return TG_ERR_SHAPE;
+  *bytes = tg::compact_workspace_bytes(B, T);
+  return TG_OK;
+}
+
+int tg_compact(const void* hidden, int64_t ld_hidden, int D, int dtype, const int32_t* pos,
+               const float* scores, const uint8_t* keep, const int32_t* cu_seqlens,
+               const int32_t* doc_begin, const int32_t* doc_end, int B, int64_t T, int64_t Kt,
+               void* hidden_out, int32_t* pos_out, float* bias_out, int32_t* kept_idx_out,
+               void* workspace, size_t workspace_bytes, void* stream) {
+  const int eb = elem_bytes(dtype);
+  if (!eb) return TG_ERR_DTYPE;
+  if (B < 0 || T < 0 || Kt < 0 || Kt > T || D <= 0 || ld_hidden < D || T > INT32_MAX)
+    return TG_ERR_SHAPE;
+  if (B == 0 && T != 0) return TG_ERR_SHAPE;
+  if (T == 0) return TG_OK;
+  if (!hidden || !scores || !keep || !cu_seqlens || !doc_begin || !doc_end) return TG_ERR_NULL;
+  if (Kt > 0 && (!hidden_out || !pos_out || !bias_out)) return TG_ERR_NULL;
+  if (!workspace || workspace_bytes < tg::compact_workspace_bytes(B, T)) return TG_ERR_WORKSPACE;
+  if (!aligned16(workspace)) return TG_ERR_ALIGN;
+  // element alignment only; the copy widens to 16-byte units when rows allow
+  if ((reinterpret_cast<uintptr_t>(hidden) % eb) != 0 ||
+      (Kt > 0 && (reinterpret_cast<uintptr_t>(hidden_out) % eb) != 0))
+    return TG_ERR_ALIGN;
+  return from_hip(tg::launch_compact(hidden, ld_hidden, D, eb, pos, scores, keep, cu_seqlens,
+                                     doc_begin, doc_end, B, T, Kt, hidden_out, pos_out, bias_out,
+                                     kept_idx_out, workspace, as_stream(stream)));
+}
+
+int tg_gated_attn_fwd(const void* q, const void* k, const void* v, int64_t q_tok_stride,
+                      int64_t k_tok_stride, int64_t v_tok_stride, const float* bias_s,
+                      const float* gain, float tau, const int32_t* cu_kept, int B,
+                      int max_kept_len, int64_t Kt, int Hq, int Hkv, int d, int dtype, void* out,
+                      float* lse, void* stream) {
+  const int eb = elem_bytes(dtype);
+  if (!eb) return TG_ERR_DTYPE;
+  if (B < 0 || Kt < 0 || Kt > INT32_MAX || max_kept_len < 0 || max_kept_len > Kt || Hq <= 0 ||
+      Hkv <= 0 || d <= 0)
+    return TG_ERR_SHAPE;
+  if (Hq % Hkv != 0) return TG_ERR_SHAPE;
+  if (q_tok_stride < (int64_t)Hq * d || k_tok_stride < (int64_t)Hkv * d ||
+      v_tok_stride < (int64_t)Hkv * d)
+    return TG_ERR_SHAPE;
+  if (!isfinite(tau)) return TG_ERR_RANGE;
+  if (d != 64 && d != 128) return TG_ERR_UNSUPPORTED;
+  if (B == 0 || Kt == 0) return TG_OK;
+  if (!q || !k || !v || !cu_kept || !out) return TG_ERR_NULL;
+  if (gain && !bias_s) return TG_ERR_NULL;
+  if (dtype == TG_BF16) {
+    if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out) ||
+        (q_tok_stride * 2) % 16 != 0 || (k_tok_stride * 2) % 16 != 0 ||
+        (v_tok_stride * 2) % 16 != 0)
+      return TG_ERR_ALIGN;
+    return from_hip(tg::launch_attn_bf16(q, k, v, q_tok_stride, k_tok_stride, v_tok_stride,
+                                         bias_s, gain, tau, cu_kept, B, max_kept_len, Kt, Hq,
+                                         Hkv, d, out, lse, as_stream(stream)));
+  }
+  return from_hip(tg::launch_attn_f32(static_cast<const float*>(q), static_cast<const float*>(k),
+                                      static_cast<const float*>(v), q_tok_stride, k_tok_stride,
+                                      v_tok_stride, bias_s, gain, tau, cu_kept, B, max_kept_len,
+                                      Kt, Hq, Hkv, d, static_cast<float*>(out), lse,
+                                      as_stream(stream)));
+}
+
+}  // extern "C"

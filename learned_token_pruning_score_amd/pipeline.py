@@ -1,0 +1,74 @@
+"""Host orchestration of the gated prefill: gate -> top-K -> compaction ->
+token-gated attention, on one stream, with every buffer allocated once.
+
+The TokenGate article ("How does TokenGate learned token pruning work?")
+splits prefill into a standard forward below the gate layer, the gate module
+(score every token, keep the top-K document tokens and the whole question),
+and a pruned forward over the kept tokens whose attention carries the score
+bias ("What is token-gated attention?").  This class runs the gate module
+and the pruned attention; the layers' projections are not part of it.
+The kept count is known on the host from the metadata (``tg_plan``), so no
+step waits on the device.
+"""
+
+from __future__ import annotations
+
+from typing import Optional, Sequence
+
+import numpy as np
+import torch
+
+from . import _lib
+
+
+class GatedPrefill:
+    def __init__(self, cu_seqlens, doc_begin, doc_end, budget, D: int,
+                 dtype: torch.dtype, device="cuda", with_index: bool = True):
+        self.cu_seqlens_h = np.ascontiguousarray(cu_seqlens, dtype=np.int32)
+        self.doc_begin_h = np.ascontiguousarray(doc_begin, dtype=np.int32)
+        self.doc_end_h = np.ascontiguousarray(doc_end, dtype=np.int32)
+        self.budget_h = np.ascontiguousarray(budget, dtype=np.int32)
+        self.cu_kept_h, self.max_kept_len = _lib.tg_plan(
+            self.cu_seqlens_h, self.doc_begin_h, self.doc_end_h, self.budget_h)
+        self.B = int(self.budget_h.shape[0])
+        self.T = int(self.cu_seqlens_h[-1])
+        self.Kt = int(self.cu_kept_h[-1])
+        self.D = D
+        self.dtype = dtype
+        dev = torch.device(device)
+        self.device = dev
+        i32 = dict(dtype=torch.int32, device=dev)
+        self.cu_seqlens = torch.from_numpy(self.cu_seqlens_h).to(dev)
+        self.doc_begin = torch.from_numpy(self.doc_begin_h).to(dev)
+        self.doc_end = torch.from_numpy(self.doc_end_h).to(dev)
+        self.budget = torch.from_numpy(self.budget_h).to(dev)
+        self.cu_kept = torch.from_numpy(self.cu_kept_h).to(dev)
+        self.scores = torch.empty(self.T, dtype=torch.float32, device=dev)
+        self.keep = torch.empty(self.T, dtype=torch.uint8, device=dev)
+        self.hidden_k = torch.empty((self.Kt, D), dtype=dtype, device=dev)
+        self.pos_k = torch.empty(self.Kt, **i32)
+        self.bias_s = torch.empty(self.Kt, dtype=torch.float32, device=dev)
+        self.kept_idx = torch.empty(self.Kt, **i32) if with_index else None
+        self.ws_select = torch.empty(max(16, _lib.tg_select_topk_workspace(self.B, self.T)),
+                                     dtype=torch.uint8, device=dev)
+        self.ws_compact = torch.empty(max(16, _lib.tg_compact_workspace(self.B, self.T)),
+                                      dtype=torch.uint8, device=dev)
+
+    def gate_and_select(self, hidden: torch.Tensor, W1: torch.Tensor, b1: Optional[torch.Tensor],
+                        w2: torch.Tensor, b2: float, pos: Optional[torch.Tensor] = None,
+                        stream=None) -> None:
+        """Score every token, pick the kept set, compact rows/positions/biases."""
+        _lib.tg_gate_score(hidden, W1, b1, w2, b2, scores=self.scores, stream=stream)
+        _lib.tg_select_topk(self.scores, self.cu_seqlens, self.doc_begin, self.doc_end,
+                            self.budget, keep=self.keep, workspace=self.ws_select, stream=stream)
+        _lib.tg_compact(hidden, pos, self.scores, self.keep, self.cu_seqlens, self.doc_begin,
+                        self.doc_end, self.Kt,
+                        out=(self.hidden_k, self.pos_k, self.bias_s, self.kept_idx),
+                        workspace=self.ws_compact, stream=stream)
+
+    def attend(self, q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, gain: torch.Tensor,
+               tau: float, out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None,
+               stream=None):
+        """Token-gated causal GQA attention of one layer over the kept tokens."""
+        return _lib.tg_gated_attn_fwd(q, k, v, self.bias_s, gain, tau, self.cu_kept,
+                                      self.max_kept_len, out=out, lse=lse, stream=stream)
