@@ -92,7 +92,8 @@ int tg_plan(int B, const int32_t* cu_seqlens_h, const int32_t* doc_begin_h,
  * hidden  [T, D] row-major, row stride ld_hidden elements (>= D), dtype.
  * W1      [F, D] row-major, dtype.   b1 [F] fp32 or NULL (zero).
  * w2      [F] fp32.  b2 scalar.      scores [T] fp32 out.
- * Supported: TG_BF16 with D % 64 == 0 and F in {64, 128, 256}, or
+ * Supported: TG_BF16 with D % 64 == 0, F in {64, 128, 256} and a row stride
+ * up to 2^22 elements, or
  * TG_F32 with any D >= 1 and 1 <= F <= 1024.  bf16 needs hidden, W1 and the
  * row stride aligned to 16 bytes.  T == 0 is a no-op.
  */
@@ -167,7 +168,8 @@ int tg_compact(const void* hidden, int64_t ld_hidden, int D, int dtype,
  * gain is NULL), gain [Hq] fp32, cu_kept [B+1] int32 (device copy of
  * tg_plan's output), max_kept_len its longest prompt.  out [Kt, Hq, d]
  * packed, same dtype as q.  lse [Hq, Kt] fp32, or NULL.
- * Supported: d in {64, 128}, Hq % Hkv == 0.  bf16 runs on MFMA with fp32
+ * Supported: d in {64, 128}, Hq % Hkv == 0, k and v token strides up to
+ * 2^23 elements.  bf16 runs on MFMA with fp32
  * accumulation and rounds the softmax weights to bf16 before the value
  * product; fp32 runs on vector ALUs throughout.  bf16 needs q, k, v, out and
  * the token strides aligned to 16 bytes.

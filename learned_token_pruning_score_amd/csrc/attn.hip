@@ -16,13 +16,17 @@
 //    operand layout of O^T += V^T P^T once keys are relabelled (within each
 //    16-key MFMA step, lane half G holds keys 4G..4G+3 and 8+4G..8+4G+3), so
 //    V is staged transposed in LDS and read as two 8-byte runs.
-//  * K rows and V^T rows are XOR-swizzled in LDS so fragment reads of 32
-//    rows spread over all banks.
+//  * K rows and V^T rows are padded in LDS (odd multiples of the read
+//    width) so fragment reads of 32 rows spread over the banks.
+//  * Two LDS stages: the next tile's global loads are issued before the
+//    current tile's MFMAs and written to the other stage after them.
 //  * Causal masking only on tiles that cross the wave's diagonal; tiles are
 //    launched longest-first (tile index is the slowest grid dimension,
 //    reversed); the heads of one GQA group land on the same XCD.
 // fp32 path: one thread per (row, head), online softmax on vector ALUs.
 #include <math.h>
+
+#include <type_traits>
 
 #include "tg_common.h"
 
@@ -31,35 +35,47 @@ namespace {
 
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
-constexpr int kBQ = 128;  // query rows per workgroup
 constexpr int kBK = 64;   // keys per tile
+constexpr float kRescale = 8.0f;
+// Fourth word of a raw buffer descriptor (32-bit data format, no swizzle):
+// accesses at or past num_records read as zero.
+constexpr int kBufFlags = 0x00020000;  // lazy-rescale threshold on the running max (log2 units)
+#ifndef TG_ATTN_WAVES
+#define TG_ATTN_WAVES 8   // waves per workgroup; 32 query rows each
+#endif
 
-template <int HD>
-__device__ __forceinline__ int kswz(int r, int c) {
-  // K rows are HD*2 bytes: 256 B (HD=128) or 128 B (HD=64).
-  return HD == 128 ? (c ^ (r & 15)) : (c ^ ((r >> 1) & 7));
-}
-// V^T rows are 64 keys * 2 B = 128 B = 16 units of 8 B.
-__device__ __forceinline__ int vswz(int d, int u) { return u ^ ((d >> 1) & 15); }
+// LDS rows are padded so that a fragment read of 32 consecutive rows at one
+// column spreads over the banks, and every per-step offset is a constant:
+// a K row is HD*2 + 16 bytes (an odd number of 16-byte units), a V^T row is
+// 64 keys * 2 + 8 = 136 bytes (an odd number of 8-byte units).
 
 __device__ __forceinline__ unsigned elem16(const uint4& v, int e) {
   const unsigned w = (e < 2) ? v.x : (e < 4) ? v.y : (e < 6) ? v.z : v.w;
   return (e & 1) ? (w >> 16) : (w & 0xffffu);
 }
 
-template <int HD>
-__global__ __launch_bounds__(256, 2) void attn_bf16_kernel(
+template <int HD, int NW>
+__global__ __launch_bounds__(NW * 64, NW == 4 ? 2 : 1) void attn_bf16_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
     const uint16_t* __restrict__ v, int64_t qs, int64_t ks, int64_t vs,
     const float* __restrict__ bias, const float* __restrict__ gain, float qk_scale,
     const int32_t* __restrict__ cu, int Hq, int group, int head_swizzle, int n_qtiles,
     int64_t Kt, uint16_t* __restrict__ out, float* __restrict__ lse) {
-  constexpr int KCH = HD / 8;   // 16-byte chunks per K row
-  constexpr int NKS = HD / 16;  // MFMA k-steps over the head dim
-  constexpr int NDB = HD / 32;  // 32-row blocks of O^T
-  __shared__ uint4 sK[kBK * KCH];
-  __shared__ uint2 sVt[HD * (kBK / 4)];
-  __shared__ float sB[kBK];
+  constexpr int NT = NW * 64;
+  constexpr int BQ = 32 * NW;       // query rows per workgroup
+  constexpr int KCH = HD / 8;       // 16-byte chunks per K row
+  constexpr int NKS = HD / 16;      // MFMA k-steps over the head dim
+  constexpr int NDB = HD / 32;      // 32-row blocks of O^T
+  constexpr int K_ITEMS = kBK * KCH;
+  constexpr int K_PER_T = (K_ITEMS + NT - 1) / NT;
+  constexpr int V_ITEMS = (kBK / 2) * KCH;  // (key pair, 8-wide d chunk)
+  constexpr int V_PER_T = (V_ITEMS + NT - 1) / NT;
+  constexpr int KROW = KCH + 1;     // 16-byte units per padded K row
+  constexpr int VROW = kBK / 2 + 2; // 32-bit words per padded V^T row (two keys each)
+  // Two LDS stages: the next tile is written while the current one is read.
+  __shared__ uint4 sK[2][kBK * KROW];
+  __shared__ uint32_t sVt[2][HD * VROW];
+  __shared__ float sB[2][kBK];
 
   const int x = blockIdx.x;
   const int h = head_swizzle ? (x % 8) * (Hq / 8) + x / 8 : x;
@@ -67,10 +83,11 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_kernel(
   const int tile = n_qtiles - 1 - (int)blockIdx.z;
   const int lo = cu[b];
   const int n = cu[b + 1] - lo;
-  const int q0 = tile * kBQ;
+  const int q0 = tile * BQ;
   if (q0 >= n) return;
   const int kvh = h / group;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
   const int G = lane >> 5;
   const int qw = q0 + wave * 32;
   const int my_q = qw + (lane & 31);
@@ -93,44 +110,90 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_kernel(
     for (int i = 0; i < 16; ++i) o[db][i] = 0.0f;
   float m_run = -INFINITY, l_run = 0.0f;
 
-  const int kv_end = min(q0 + kBQ, n);
+  const int kv_end = min(q0 + BQ, n);
   const int n_kt = (kv_end + kBK - 1) / kBK;
   const bool wave_active = qw < n;
   const int n_kt_w = wave_active ? min(qw + 31, n - 1) / kBK + 1 : 0;
   const uint16_t* kbase = k + (int64_t)lo * ks + (int64_t)kvh * HD;
   const uint16_t* vbase = v + (int64_t)lo * vs + (int64_t)kvh * HD;
 
-  for (int kt = 0; kt < n_kt; ++kt) {
-    const int k0 = kt * kBK;
-    __syncthreads();
-    for (int id = tid; id < kBK * KCH; id += 256) {
-      const int r = id / KCH, c = id % KCH;
-      uint4 val = make_uint4(0, 0, 0, 0);
-      if (k0 + r < n) val = *reinterpret_cast<const uint4*>(kbase + (int64_t)(k0 + r) * ks + c * 8);
-      sK[r * KCH + kswz<HD>(r, c)] = val;
-    }
-    for (int id = tid; id < 16 * KCH; id += 256) {
-      const int kg = id % 16, dc = id / 16;
-      uint4 rows[4];
+  static_assert(K_ITEMS % NT == 0 && V_ITEMS % NT == 0, "tile split");
+  // Buffer-resource loads: the descriptor of each tile starts at its first
+  // key and ends at the prompt's last key (or 64 keys on), so rows past the
+  // prompt read as zero without a branch.  Such keys only occur in a tile
+  // that crosses the causal diagonal of every wave reading it, where they
+  // are masked.  Per-thread byte offsets are loop-invariant.
+  int k_off[K_PER_T];
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int key = k0 + 4 * kg + j;
-        rows[j] = make_uint4(0, 0, 0, 0);
-        if (key < n) rows[j] = *reinterpret_cast<const uint4*>(vbase + (int64_t)key * vs + dc * 8);
-      }
+  for (int j = 0; j < K_PER_T; ++j) {
+    const int id = tid + j * NT;
+    k_off[j] = ((id / KCH) * (int)ks + (id % KCH) * 8) * 2;
+  }
+  int v_off[V_PER_T][2];
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const int d = dc * 8 + e;
-        uint2 u;
-        u.x = elem16(rows[0], e) | (elem16(rows[1], e) << 16);
-        u.y = elem16(rows[2], e) | (elem16(rows[3], e) << 16);
-        sVt[d * 16 + vswz(d, kg)] = u;
-      }
-    }
-    if (tid < kBK) sB[tid] = (bias != nullptr && k0 + tid < n) ? bias[lo + k0 + tid] * gmul : 0.0f;
-    __syncthreads();
-    if (kt >= n_kt_w) continue;
+  for (int j = 0; j < V_PER_T; ++j) {
+    const int id = tid + j * NT;
+#pragma unroll
+    for (int e = 0; e < 2; ++e) v_off[j][e] = ((2 * (id / KCH) + e) * (int)vs + (id % KCH) * 8) * 2;
+  }
+  const float* bias_p = bias ? bias + lo : nullptr;
 
+  uint4 kreg[K_PER_T];
+  uint4 vreg[V_PER_T][2];
+  float breg = 0.0f;
+  auto prefetch = [&](int k0) {
+    const int rows = min(n - k0, kBK);
+    const __amdgpu_buffer_rsrc_t rk = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)(kbase + (int64_t)k0 * ks), (short)0, rows * (int)ks * 2, kBufFlags);
+    const __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)(vbase + (int64_t)k0 * vs), (short)0, rows * (int)vs * 2, kBufFlags);
+#pragma unroll
+    for (int j = 0; j < K_PER_T; ++j)
+      kreg[j] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rk, k_off[j], 0, 0));
+#pragma unroll
+    for (int j = 0; j < V_PER_T; ++j)
+#pragma unroll
+      for (int e = 0; e < 2; ++e)
+        vreg[j][e] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rv, v_off[j][e], 0, 0));
+    if (bias_p != nullptr) {
+      const __amdgpu_buffer_rsrc_t rb = __builtin_amdgcn_make_buffer_rsrc(
+          (void*)(bias_p + k0), (short)0, rows * 4, kBufFlags);
+      breg = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rb, (tid & (kBK - 1)) * 4, 0, 0));
+    }
+  };
+  // Registers -> LDS stage `buf`: K rows padded, V transposed to V^T (two
+  // keys per 32-bit word, packed with byte permutes), bias pre-scaled.
+  auto stage = [&](int buf) {
+#pragma unroll
+    for (int j = 0; j < K_PER_T; ++j) {
+      const int id = tid + j * NT;
+      sK[buf][(id / KCH) * KROW + (id % KCH)] = kreg[j];
+    }
+#pragma unroll
+    for (int j = 0; j < V_PER_T; ++j) {
+      const int id = tid + j * NT;
+      const int dc = id % KCH, p = id / KCH;
+      uint32_t* dst = &sVt[buf][(dc * 8) * VROW + p];
+      const uint4 a = vreg[j][0], c2 = vreg[j][1];
+      // word (d, key pair p) = (V[2p][d], V[2p+1][d]) for d = 8 dc + 0..7
+      dst[0 * VROW] = __builtin_amdgcn_perm(c2.x, a.x, 0x05040100u);
+      dst[1 * VROW] = __builtin_amdgcn_perm(c2.x, a.x, 0x07060302u);
+      dst[2 * VROW] = __builtin_amdgcn_perm(c2.y, a.y, 0x05040100u);
+      dst[3 * VROW] = __builtin_amdgcn_perm(c2.y, a.y, 0x07060302u);
+      dst[4 * VROW] = __builtin_amdgcn_perm(c2.z, a.z, 0x05040100u);
+      dst[5 * VROW] = __builtin_amdgcn_perm(c2.z, a.z, 0x07060302u);
+      dst[6 * VROW] = __builtin_amdgcn_perm(c2.w, a.w, 0x05040100u);
+      dst[7 * VROW] = __builtin_amdgcn_perm(c2.w, a.w, 0x07060302u);
+    }
+    if (tid < kBK) sB[buf][tid] = breg * gmul;
+  };
+
+  // One 64-key tile for this wave's 32 rows.  MASK: the tile crosses the
+  // wave's causal diagonal.  The running max is only moved when a row's max
+  // grows by more than kRescale (log2 units): until then p <= 2^kRescale,
+  // harmless in fp32 and bf16, and the O/l rescale is skipped.
+  auto tile_step = [&](int buf, int k0, auto mask_tag) {
+    constexpr bool MASK = decltype(mask_tag)::value;
     f32x16 s[2];
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
@@ -139,41 +202,40 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_kernel(
       const int r = kb * 32 + (lane & 31);
 #pragma unroll
       for (int st = 0; st < NKS; ++st)
-        s[kb] = mfma32x32x16(as_bf16x8(sK[r * KCH + kswz<HD>(r, 2 * st + G)]), qf[st], s[kb]);
+        s[kb] = mfma32x32x16(as_bf16x8(sK[buf][r * KROW + 2 * st + G]), qf[st], s[kb]);
     }
-
-    const bool diag = (k0 + kBK - 1) > qw;
     float mx = -INFINITY;
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
         const int key = kb * 32 + acc_row(i, lane);
-        float y = fmaf(s[kb][i], qk_scale, sB[key]);
-        if (diag && (k0 + key) > my_q) y = -INFINITY;
+        float y = fmaf(s[kb][i], qk_scale, sB[buf][key]);
+        if (MASK && (k0 + key) > my_q) y = -INFINITY;
         s[kb][i] = y;
         mx = fmaxf(mx, y);
       }
     mx = pair_max(mx);
-    const float m_new = fmaxf(m_run, mx);
-    const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+    if (__any(mx > m_run + kRescale)) {
+      const float m_new = fmaxf(m_run, mx);
+      const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+      l_run *= alpha;
+#pragma unroll
+      for (int db = 0; db < NDB; ++db)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) o[db][i] *= alpha;
+      m_run = m_new;
+    }
     float psum = 0.0f;
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
-        const float p = __builtin_amdgcn_exp2f(s[kb][i] - m_new);
+        const float p = __builtin_amdgcn_exp2f(s[kb][i] - m_run);
         s[kb][i] = p;
         psum += p;
       }
-    l_run = fmaf(l_run, alpha, psum);
-    if (__any(alpha != 1.0f)) {
-#pragma unroll
-      for (int db = 0; db < NDB; ++db)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) o[db][i] *= alpha;
-    }
-    m_run = m_new;
+    l_run += psum;
 
     bf16x8 pb[2][2];
 #pragma unroll
@@ -186,18 +248,46 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_kernel(
 #pragma unroll
     for (int db = 0; db < NDB; ++db) {
       const int d = db * 32 + (lane & 31);
+      const uint32_t* row = &sVt[buf][d * VROW];
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
         for (int hh = 0; hh < 2; ++hh) {
-          const int u0 = kb * 8 + 4 * hh + G;
-          const uint2 a0 = sVt[d * 16 + vswz(d, u0)];
-          const uint2 a1 = sVt[d * 16 + vswz(d, u0 + 2)];
+          const int w0 = 2 * (kb * 8 + 4 * hh + G);  // keys 4G..4G+3 of the step
+          const uint2 a0 = *reinterpret_cast<const uint2*>(row + w0);
+          const uint2 a1 = *reinterpret_cast<const uint2*>(row + w0 + 4);  // keys +8..+11
           const uint4 a = make_uint4(a0.x, a0.y, a1.x, a1.y);
           o[db] = mfma32x32x16(as_bf16x8(a), pb[kb][hh], o[db]);
         }
     }
+  };
+
+  // n_kt >= 1 here (q0 < n).  The unconditional first stage also retires the
+  // Q loads on every path into the loop.
+  prefetch(0);
+  stage(0);
+  __syncthreads();
+
+  // Every wave runs n_kt iterations (one barrier each) but computes only on
+  // the tiles its rows see: unmasked tiles, then the one tile crossing its
+  // diagonal, then staging-only iterations.  Three straight loops keep the
+  // accumulators in place (no merge of differently computed values).
+  auto iteration = [&](int kt, auto mode_tag) {
+    constexpr int MODE = decltype(mode_tag)::value;  // 0 stage only, 1 unmasked, 2 masked
+    const int buf = kt & 1;
+    if (kt + 1 < n_kt) prefetch((kt + 1) * kBK);
+    if constexpr (MODE == 1) tile_step(buf, kt * kBK, std::false_type{});
+    if constexpr (MODE == 2) tile_step(buf, kt * kBK, std::true_type{});
+    if (kt + 1 < n_kt) stage(buf ^ 1);
+    __syncthreads();
+  };
+  int kt = 0;
+  for (; kt + 1 < n_kt_w; ++kt) iteration(kt, std::integral_constant<int, 1>{});
+  if (kt < n_kt_w) {
+    iteration(kt, std::integral_constant<int, 2>{});
+    ++kt;
   }
+  for (; kt < n_kt; ++kt) iteration(kt, std::integral_constant<int, 0>{});
 
   if (!wave_active) return;
   const float l_tot = pair_sum(l_run);
@@ -272,22 +362,28 @@ hipError_t launch_attn_bf16(const void* q, const void* k, const void* v, int64_t
                             int Hkv, int d, void* out, float* lse, hipStream_t s) {
   if (B == 0 || max_len == 0) return hipSuccess;
   const int group = Hq / Hkv;
-  const int n_qtiles = (max_len + kBQ - 1) / kBQ;
+  // head_dim 128: TG_ATTN_WAVES waves (32 query rows each) per workgroup;
+  // head_dim 64: 4 waves (a 64x64 V tile gives 256 transpose items).
+  constexpr int NW = TG_ATTN_WAVES;
   const int swz = (Hq % 8 == 0 && ((Hq / 8) % group) == 0) ? 1 : 0;
   const float qk_scale = tau * kLog2e / sqrtf((float)d);
-  const dim3 grid((unsigned)Hq, (unsigned)B, (unsigned)n_qtiles);
   const auto* qq = static_cast<const uint16_t*>(q);
   const auto* kk = static_cast<const uint16_t*>(k);
   const auto* vv = static_cast<const uint16_t*>(v);
   auto* oo = static_cast<uint16_t*>(out);
-  if (d == 128)
-    hipLaunchKernelGGL(attn_bf16_kernel<128>, grid, dim3(256), 0, s, qq, kk, vv, qs, ks, vs, bias,
-                       gain, qk_scale, cu_kept, Hq, group, swz, n_qtiles, Kt, oo, lse);
-  else if (d == 64)
-    hipLaunchKernelGGL(attn_bf16_kernel<64>, grid, dim3(256), 0, s, qq, kk, vv, qs, ks, vs, bias,
-                       gain, qk_scale, cu_kept, Hq, group, swz, n_qtiles, Kt, oo, lse);
-  else
+  if (d == 128) {
+    const int n_qtiles = (max_len + 32 * NW - 1) / (32 * NW);
+    const dim3 grid((unsigned)Hq, (unsigned)B, (unsigned)n_qtiles);
+    hipLaunchKernelGGL((attn_bf16_kernel<128, NW>), grid, dim3(64 * NW), 0, s, qq, kk, vv, qs, ks,
+                       vs, bias, gain, qk_scale, cu_kept, Hq, group, swz, n_qtiles, Kt, oo, lse);
+  } else if (d == 64) {
+    const int n_qtiles = (max_len + 127) / 128;
+    const dim3 grid((unsigned)Hq, (unsigned)B, (unsigned)n_qtiles);
+    hipLaunchKernelGGL((attn_bf16_kernel<64, 4>), grid, dim3(256), 0, s, qq, kk, vv, qs, ks, vs,
+                       bias, gain, qk_scale, cu_kept, Hq, group, swz, n_qtiles, Kt, oo, lse);
+  } else {
     return hipErrorInvalidValue;
+  }
   return hipGetLastError();
 }
 

@@ -9,8 +9,9 @@
 // run of F rows: the SiLU . w2 epilogue then reduces over F inside the lane,
 // across the two wave halves, and across the F-quarter waves through LDS, in
 // a fixed order (bit-reproducible, no atomics).  The [T, F] activation never
-// reaches memory.  hidden and W1 stream through one LDS stage of 64 columns
-// with register prefetch of the next stage.
+// reaches memory.  hidden and W1 stream through two LDS stages of 64
+// columns: the next stage's global loads are issued before the current
+// stage's MFMAs and written to LDS after them.
 #include "tg_common.h"
 
 namespace tg {
@@ -19,12 +20,9 @@ namespace {
 constexpr int kGateBM = 256;  // tokens per workgroup
 constexpr int kGateBK = 64;   // reduction columns per LDS stage
 constexpr int kRowChunks = kGateBK / 8;  // 16-byte chunks per staged row
-
-// XOR swizzle of the 16-byte chunk inside a 128-byte staged row: rows r and
-// r + 1 share a 256-byte bank window, so (r & 1, chunk ^ ((r >> 1) & 7)) is
-// distinct over any 16 consecutive rows and a fragment read of 32 rows at
-// one logical chunk touches every bank twice at most.
-__device__ __forceinline__ int swz_chunk(int row, int c) { return c ^ ((row >> 1) & 7); }
+constexpr int kRowPad = kRowChunks + 1;  // padded row: 9 x 16 B, so 16
+                                         // consecutive rows hit 16 bank groups
+constexpr int kBufFlags = 0x00020000;    // raw buffer: reads past num_records give 0
 
 template <int NFQ>  // number of 64-wide F quarters (F = 64 * NFQ)
 __global__ __launch_bounds__(128 * NFQ) void gate_bf16_kernel(
@@ -39,53 +37,62 @@ __global__ __launch_bounds__(128 * NFQ) void gate_bf16_kernel(
   constexpr int W_PER_T = W_CHUNKS / NT;
   static_assert(H_CHUNKS % NT == 0 && W_CHUNKS % NT == 0, "tile split");
 
-  __shared__ uint4 sh_h[kGateBM * kRowChunks];
-  __shared__ uint4 sh_w[F * kRowChunks];
+  // Two LDS stages: the next 64 columns are written while these are read.
+  __shared__ uint4 sh_h[2][kGateBM * kRowPad];
+  __shared__ uint4 sh_w[2][F * kRowPad];
   __shared__ float sh_red[NFQ][kGateBM];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wt = wave / NFQ;  // token half: tokens [128 wt, 128 wt + 128)
   const int wf = wave % NFQ;  // F quarter: rows [64 wf, 64 wf + 64)
   const int64_t t0 = (int64_t)blockIdx.x * kGateBM;
+  const int rows = (int)min((int64_t)kGateBM, T - t0);
 
+  // hidden rows past T read as zero through the buffer descriptor; W1 is
+  // always in range.
+  int h_off[H_PER_T];
+#pragma unroll
+  for (int j = 0; j < H_PER_T; ++j) {
+    const int id = tid + j * NT;
+    h_off[j] = ((id / kRowChunks) * (int)ld + (id % kRowChunks) * 8) * 2;
+  }
+  int w_off[W_PER_T];
+#pragma unroll
+  for (int j = 0; j < W_PER_T; ++j) {
+    const int id = tid + j * NT;
+    w_off[j] = ((id / kRowChunks) * D + (id % kRowChunks) * 8) * 2;
+  }
   uint4 pre_h[H_PER_T];
   uint4 pre_w[W_PER_T];
+  const uint16_t* hbase = hidden + t0 * ld;
 
-  auto prefetch = [&](int kc) {
-    const int k0 = kc * kGateBK;
-#pragma unroll
-    for (int j = 0; j < H_PER_T; ++j) {
-      const int id = tid + j * NT;
-      const int r = id / kRowChunks, c = id % kRowChunks;
-      const int64_t t = t0 + r;
-      if (t < T)
-        pre_h[j] = *reinterpret_cast<const uint4*>(hidden + t * ld + k0 + c * 8);
-      else
-        pre_h[j] = make_uint4(0, 0, 0, 0);
-    }
-#pragma unroll
-    for (int j = 0; j < W_PER_T; ++j) {
-      const int id = tid + j * NT;
-      const int r = id / kRowChunks, c = id % kRowChunks;
-      pre_w[j] = *reinterpret_cast<const uint4*>(W1 + (int64_t)r * D + k0 + c * 8);
-    }
-  };
-  auto stage = [&]() {
-#pragma unroll
-    for (int j = 0; j < H_PER_T; ++j) {
-      const int id = tid + j * NT;
-      const int r = id / kRowChunks, c = id % kRowChunks;
-      sh_h[r * kRowChunks + swz_chunk(r, c)] = pre_h[j];
-    }
-#pragma unroll
-    for (int j = 0; j < W_PER_T; ++j) {
-      const int id = tid + j * NT;
-      const int r = id / kRowChunks, c = id % kRowChunks;
-      sh_w[r * kRowChunks + swz_chunk(r, c)] = pre_w[j];
-    }
-  };
+  // Global -> registers for reduction columns [k0, k0 + 64).
+#define TG_GATE_PREFETCH(k0_)                                                                  \
+  do {                                                                                         \
+    const int k0 = (k0_);                                                                      \
+    const __amdgpu_buffer_rsrc_t rh = __builtin_amdgcn_make_buffer_rsrc(                       \
+        (void*)(hbase + k0), (short)0, rows * (int)ld * 2 - k0 * 2, kBufFlags);                \
+    const __amdgpu_buffer_rsrc_t rw = __builtin_amdgcn_make_buffer_rsrc(                       \
+        (void*)(W1 + k0), (short)0, F * D * 2 - k0 * 2, kBufFlags);                            \
+    _Pragma("unroll") for (int j = 0; j < H_PER_T; ++j) pre_h[j] =                             \
+        __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rh, h_off[j], 0, 0));  \
+    _Pragma("unroll") for (int j = 0; j < W_PER_T; ++j) pre_w[j] =                             \
+        __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rw, w_off[j], 0, 0));  \
+  } while (0)
+  // Registers -> LDS stage buf_.
+#define TG_GATE_STAGE(buf_)                                                                    \
+  do {                                                                                         \
+    _Pragma("unroll") for (int j = 0; j < H_PER_T; ++j) {                                      \
+      const int id = tid + j * NT;                                                             \
+      sh_h[buf_][(id / kRowChunks) * kRowPad + (id % kRowChunks)] = pre_h[j];                  \
+    }                                                                                          \
+    _Pragma("unroll") for (int j = 0; j < W_PER_T; ++j) {                                      \
+      const int id = tid + j * NT;                                                             \
+      sh_w[buf_][(id / kRowChunks) * kRowPad + (id % kRowChunks)] = pre_w[j];                  \
+    }                                                                                          \
+  } while (0)
 
   f32x16 acc[2][4];
 #pragma unroll
@@ -96,32 +103,32 @@ __global__ __launch_bounds__(128 * NFQ) void gate_bf16_kernel(
       for (int i = 0; i < 16; ++i) acc[a][b][i] = 0.0f;
 
   const int nk = D / kGateBK;
-  prefetch(0);
+  TG_GATE_PREFETCH(0);
+  TG_GATE_STAGE(0);
+  __syncthreads();
   for (int kc = 0; kc < nk; ++kc) {
-    __syncthreads();
-    stage();
-    __syncthreads();
-    if (kc + 1 < nk) prefetch(kc + 1);
+    const int buf = kc & 1;
+    if (kc + 1 < nk) TG_GATE_PREFETCH((kc + 1) * kGateBK);
 #pragma unroll
     for (int ks = 0; ks < kGateBK / 16; ++ks) {
       const int c = ks * 2 + (lane >> 5);
       bf16x8 fa[2], fb[4];
 #pragma unroll
-      for (int fbk = 0; fbk < 2; ++fbk) {
-        const int r = wf * 64 + fbk * 32 + (lane & 31);
-        fa[fbk] = as_bf16x8(sh_w[r * kRowChunks + swz_chunk(r, c)]);
-      }
+      for (int fbk = 0; fbk < 2; ++fbk)
+        fa[fbk] = as_bf16x8(sh_w[buf][(wf * 64 + fbk * 32 + (lane & 31)) * kRowPad + c]);
 #pragma unroll
-      for (int tb = 0; tb < 4; ++tb) {
-        const int r = wt * 128 + tb * 32 + (lane & 31);
-        fb[tb] = as_bf16x8(sh_h[r * kRowChunks + swz_chunk(r, c)]);
-      }
+      for (int tb = 0; tb < 4; ++tb)
+        fb[tb] = as_bf16x8(sh_h[buf][(wt * 128 + tb * 32 + (lane & 31)) * kRowPad + c]);
 #pragma unroll
       for (int fbk = 0; fbk < 2; ++fbk)
 #pragma unroll
         for (int tb = 0; tb < 4; ++tb) acc[fbk][tb] = mfma32x32x16(fa[fbk], fb[tb], acc[fbk][tb]);
     }
+    if (kc + 1 < nk) TG_GATE_STAGE(buf ^ 1);
+    __syncthreads();
   }
+#undef TG_GATE_PREFETCH
+#undef TG_GATE_STAGE
 
   // Epilogue: lane holds token column (lane & 31) of each token block and F
   // rows acc_row(i, lane) of each F block.
@@ -152,10 +159,10 @@ __global__ __launch_bounds__(128 * NFQ) void gate_bf16_kernel(
   for (int r = tid; r < kGateBM; r += NT) {
     const int64_t t = t0 + r;
     if (t < T) {
-      float s = 0.0f;
+      float sum = 0.0f;
 #pragma unroll
-      for (int q = 0; q < NFQ; ++q) s += sh_red[q][r];
-      scores[t] = s + b2;
+      for (int q = 0; q < NFQ; ++q) sum += sh_red[q][r];
+      scores[t] = sum + b2;
     }
   }
 }

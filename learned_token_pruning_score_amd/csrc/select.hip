@@ -16,8 +16,9 @@
 //   sel_init   per prompt: state from (doc span, budget); clears histogram
 //   sel_hist   per (chunk, prompt): LDS histogram of the current digit over
 //              keys matching the chosen prefix, flushed with integer atomics
-//   sel_pick   per prompt: suffix scan of the histogram picks the digit
-//   sel_ties   per prompt: index bound among keys equal to theta if needed
+//   sel_pick   per prompt: suffix scan of the histogram picks the digit;
+//              after the last digit, the index bound among keys equal to
+//              theta when not all of them are kept
 //   sel_mark   per token: keep flag
 // Integer atomics only: the histogram, and so every result, is independent
 // of execution order.
@@ -121,98 +122,95 @@ __global__ __launch_bounds__(kHistThreads) void sel_hist(const float* __restrict
   }
 }
 
-// One workgroup of 256 threads per prompt; thread i owns bins [8i, 8i + 8).
-__global__ __launch_bounds__(256) void sel_pick(SelState* st, unsigned* hist, int pass) {
+// One workgroup of 1024 threads per prompt; thread i owns bins 2i, 2i + 1.
+// The digit is the bin where the count of keys in higher bins first reaches
+// k_rem; the counts above each thread come from an exclusive scan run from
+// the top bin down (wave shuffles, then the 16 wave totals).  The histogram
+// is cleared for the next pass.  After the last digit, theta is exact; if
+// fewer than all keys equal to theta are kept, the same workgroup walks the
+// document in index order to find the index bound (1024 tokens per round,
+// stopping at the round that holds the k_rem-th equal key).
+__global__ __launch_bounds__(1024) void sel_pick(const float* __restrict__ scores, SelState* st,
+                                                 unsigned* hist, int pass) {
   const int b = blockIdx.x;
-  __shared__ int s_active;
-  __shared__ unsigned part[256];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  __shared__ SelState s;
+  __shared__ unsigned wtot[16];
   __shared__ int s_digit;
-  __shared__ unsigned s_above;
-  __shared__ unsigned s_bin;
-  if (threadIdx.x == 0) {
-    s_active = st[b].active;
+  __shared__ unsigned s_above, s_bin;
+  if (tid == 0) {
+    s = st[b];
     s_digit = 0;
     s_above = 0u;
     s_bin = 0u;
   }
   __syncthreads();
-  if (!s_active) return;
+  if (!s.active) return;
   unsigned* h = hist + (size_t)b * kBins;
-  const int i = threadIdx.x;
-  unsigned c[8];
-  unsigned sum = 0;
+  // thread j (counted from the top) owns bins hi = 2047 - 2j and hi - 1
+  const int hi_bin = kBins - 1 - 2 * tid;
+  const unsigned c_hi = h[hi_bin], c_lo = h[hi_bin - 1];
+  h[hi_bin] = 0u;
+  h[hi_bin - 1] = 0u;
+  const unsigned mine = c_hi + c_lo;
+  unsigned incl = mine;  // inclusive scan over threads, top bins first
 #pragma unroll
-  for (int j = 0; j < 8; ++j) {
-    c[j] = h[8 * i + j];
-    h[8 * i + j] = 0u;  // cleared for the next pass
-    sum += c[j];
+  for (int off = 1; off < 64; off <<= 1) {
+    const unsigned y = __shfl_up(incl, off);
+    if (lane >= off) incl += y;
   }
-  part[i] = sum;
+  if (lane == 63) wtot[wave] = incl;
   __syncthreads();
-  // Count of keys in bins strictly above this thread's range (suffix sum),
-  // by a plain loop: 256 partials, deterministic.
-  unsigned above = 0;
-  for (int j = i + 1; j < 256; ++j) above += part[j];
-  const int k_rem = st[b].k_rem;
-  // The digit lies in this thread's range iff above < k_rem <= above + sum.
-  if ((int)above < k_rem && k_rem <= (int)(above + sum)) {
-    unsigned run = above;
-    for (int j = 7; j >= 0; --j) {
-      if ((int)(run + c[j]) >= k_rem) {
-        s_digit = 8 * i + j;
-        s_above = run;
-        s_bin = c[j];
-        break;
-      }
-      run += c[j];
+  unsigned above = incl - mine;
+  for (int w = 0; w < wave; ++w) above += wtot[w];
+  const unsigned k_rem = (unsigned)s.k_rem;
+  if (above < k_rem && k_rem <= above + mine) {
+    if (above + c_hi >= k_rem) {
+      s_digit = hi_bin;
+      s_above = above;
+      s_bin = c_hi;
+    } else {
+      s_digit = hi_bin - 1;
+      s_above = above + c_hi;
+      s_bin = c_lo;
     }
   }
   __syncthreads();
-  if (threadIdx.x == 0) {
-    SelState s = st[b];
-    const int d = s_digit;
+  if (tid == 0) {
     const int sh = digit_shift(pass);
-    s.prefix |= (unsigned)d << sh;
+    s.prefix |= (unsigned)s_digit << sh;
     s.mask |= digit_mask(pass) << sh;
     s.k_rem -= (int)s_above;
-    if (pass == 2) {  // every bit fixed: theta found, ties resolved next
+    if (pass == 2) {  // every bit fixed: theta found
       s.theta = s.prefix;
       s.active = 0;
       s.n_eq = (int)s_bin;  // keys equal to theta
     }
-    st[b] = s;
   }
-}
-
-// Tie pass: among document keys equal to theta, keep the first k_rem by
-// index.  Runs only when some equal keys must be dropped (k_rem < n_eq);
-// walks the span in index order, 1024 tokens per round, and stops at the
-// round holding the k_rem-th equal key.  One workgroup per prompt.
-__global__ __launch_bounds__(1024) void sel_ties(const float* __restrict__ scores, SelState* st) {
-  const int b = blockIdx.x;
-  const SelState s = st[b];
-  if (s.mode != 2 || s.k_rem >= s.n_eq) return;
-  __shared__ int wsum[16];
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  int seen = 0;  // equal keys before this round (same value in every thread)
-  for (int base = s.lo; base < s.hi; base += 1024) {
-    const int t = base + (int)threadIdx.x;
-    const int eq = (t < s.hi) && (score_key(scores[t]) == s.theta);
-    // inclusive prefix of eq within the wave, then across the 16 waves
-    const unsigned long long bal = __ballot(eq);
-    const int in_wave = __popcll(bal & ((lane == 63) ? ~0ull : ((2ull << lane) - 1)));
-    if (lane == 63) wsum[wave] = in_wave;
-    __syncthreads();
-    int before_wave = 0, round_total = 0;
-    for (int w = 0; w < 16; ++w) {
-      if (w < wave) before_wave += wsum[w];
-      round_total += wsum[w];
+  __syncthreads();
+  if (pass == 2 && s.k_rem < s.n_eq) {
+    // keep only the first k_rem keys equal to theta, by index
+    int seen = 0;
+    for (int base = s.lo; base < s.hi; base += 1024) {
+      const int t = base + tid;
+      const int eq = (t < s.hi) && (score_key(scores[t]) == s.theta);
+      const unsigned long long bal = __ballot(eq);
+      const int in_wave = __popcll(bal & ((lane == 63) ? ~0ull : ((2ull << lane) - 1)));
+      __syncthreads();
+      if (lane == 63) wtot[wave] = (unsigned)in_wave;
+      __syncthreads();
+      int before = 0, round_total = 0;
+      for (int w = 0; w < 16; ++w) {
+        if (w < wave) before += (int)wtot[w];
+        round_total += (int)wtot[w];
+      }
+      if (eq && seen + before + in_wave == s.k_rem) s.idx_bound = t;
+      seen += round_total;
+      if (seen >= s.k_rem) break;
     }
-    if (eq && seen + before_wave + in_wave == s.k_rem) st[b].idx_bound = t;
-    seen += round_total;
-    __syncthreads();
-    if (seen >= s.k_rem) break;
   }
+  __syncthreads();
+  if (tid == 0) st[b] = s;
 }
 
 __device__ __forceinline__ int find_prompt(const int32_t* cu, int B, int64_t t) {
@@ -259,9 +257,8 @@ hipError_t launch_select(const float* scores, const int32_t* cu, const int32_t* 
   const dim3 hgrid((unsigned)((T + kHistChunk - 1) / kHistChunk), (unsigned)B);
   for (int p = 0; p < 3; ++p) {
     hipLaunchKernelGGL(sel_hist, hgrid, dim3(kHistThreads), 0, s, scores, st, hist, p);
-    hipLaunchKernelGGL(sel_pick, dim3(B), dim3(256), 0, s, st, hist, p);
+    hipLaunchKernelGGL(sel_pick, dim3(B), dim3(1024), 0, s, scores, st, hist, p);
   }
-  hipLaunchKernelGGL(sel_ties, dim3(B), dim3(1024), 0, s, scores, st);
   hipLaunchKernelGGL(sel_mark, dim3((unsigned)((T + 255) / 256)), dim3(256), 0, s, scores, st,
                      cu, B, T, keep);
   return hipGetLastError();

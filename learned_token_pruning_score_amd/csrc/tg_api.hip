@@ -86,6 +86,8 @@ int tg_gate_score(const void* hidden, int64_t ld_hidden, int64_t T, int D, const
   if (!hidden || !W1 || !w2 || !scores) return TG_ERR_NULL;
   if (dtype == TG_BF16) {
     if (D % 64 != 0 || !(F == 64 || F == 128 || F == 256)) return TG_ERR_UNSUPPORTED;
+    // a 256-row tile of hidden is addressed with 32-bit byte offsets
+    if (ld_hidden > (1 << 22) || (int64_t)F * D > (1 << 29)) return TG_ERR_UNSUPPORTED;
     if (!aligned16(hidden) || !aligned16(W1) || (ld_hidden * 2) % 16 != 0) return TG_ERR_ALIGN;
     return from_hip(tg::launch_gate_bf16(hidden, ld_hidden, T, D, W1, b1, w2, b2, F, scores,
                                          as_stream(stream)));
@@ -165,6 +167,8 @@ int tg_gated_attn_fwd(const void* q, const void* k, const void* v, int64_t q_tok
     return TG_ERR_SHAPE;
   if (!isfinite(tau)) return TG_ERR_RANGE;
   if (d != 64 && d != 128) return TG_ERR_UNSUPPORTED;
+  // a 64-key tile of k or v is addressed with 32-bit byte offsets
+  if (k_tok_stride > (1 << 23) || v_tok_stride > (1 << 23)) return TG_ERR_UNSUPPORTED;
   if (B == 0 || Kt == 0) return TG_OK;
   if (!q || !k || !v || !cu_kept || !out) return TG_ERR_NULL;
   if (gain && !bias_s) return TG_ERR_NULL;
