@@ -162,6 +162,7 @@ int tg_compact(const void* hidden, int64_t ld_hidden, int D, int dtype,
  *     o_i  = sum_j softmax(x)_j * v_j
  *     lse_i = ln sum_j exp(x_j)
  * gain == NULL drops the bias term (plain causal attention with temperature).
+ * tau must be finite and positive (a temperature), else TG_ERR_RANGE.
  *
  * q [Kt, Hq, d], k and v [Kt, Hkv, d]: heads contiguous inside a token, token
  * strides in elements (>= heads * d).  bias_s [Kt] fp32 (may be NULL only when

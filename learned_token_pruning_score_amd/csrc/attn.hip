@@ -75,7 +75,7 @@ __global__ __launch_bounds__(NW * 64, NW == 4 ? 2 : 1) void attn_bf16_kernel(
   // Two LDS stages: the next tile is written while the current one is read.
   __shared__ uint4 sK[2][kBK * KROW];
   __shared__ uint32_t sVt[2][HD * VROW];
-  __shared__ float sB[2][kBK];
+  __shared__ uint32_t sB[2][kBK];  // per key: bias / scale as a bf16 (hi, lo) pair
 
   const int x = blockIdx.x;
   const int h = head_swizzle ? (x % 8) * (Hq / 8) + x / 8 : x;
@@ -91,7 +91,15 @@ __global__ __launch_bounds__(NW * 64, NW == 4 ? 2 : 1) void attn_bf16_kernel(
   const int G = lane >> 5;
   const int qw = q0 + wave * 32;
   const int my_q = qw + (lane & 31);
-  const float gmul = gain ? gain[h] * kLog2e : 0.0f;
+  // The key bias enters the score MFMA as one more k-step: K gains the
+  // columns (c_hi, c_lo) with c_hi + c_lo = g_h log2e s_j / scale (two bf16
+  // parts, exact to about 2^-16 of c) and Q gains the columns (1, 1), so the
+  // accumulator holds q.k + c and the logit is scale * acc.  The softmax then
+  // needs one FMA per score.  Requires scale > 0 (checked on the host).
+  const bool has_bias = (bias != nullptr) && (gain != nullptr);
+  const float cmul = has_bias ? gain[h] * kLog2e / qk_scale : 0.0f;
+  const bf16x8 q_one = as_bf16x8(make_uint4(G == 0 ? 0x3F803F80u : 0u, 0u, 0u, 0u));
+  const float rs_thr = kRescale / qk_scale;  // rescale threshold in accumulator units
 
   bf16x8 qf[NKS];
   {
@@ -108,7 +116,9 @@ __global__ __launch_bounds__(NW * 64, NW == 4 ? 2 : 1) void attn_bf16_kernel(
   for (int db = 0; db < NDB; ++db)
 #pragma unroll
     for (int i = 0; i < 16; ++i) o[db][i] = 0.0f;
-  float m_run = -INFINITY, l_run = 0.0f;
+  float m_run = -INFINITY;  // running max of the accumulator (q.k + c)
+  float nms = 0.0f;         // -m_run * scale
+  float l_run = 0.0f;
 
   const int kv_end = min(q0 + BQ, n);
   const int n_kt = (kv_end + kBK - 1) / kBK;
@@ -185,7 +195,13 @@ __global__ __launch_bounds__(NW * 64, NW == 4 ? 2 : 1) void attn_bf16_kernel(
       dst[6 * VROW] = __builtin_amdgcn_perm(c2.w, a.w, 0x05040100u);
       dst[7 * VROW] = __builtin_amdgcn_perm(c2.w, a.w, 0x07060302u);
     }
-    if (tid < kBK) sB[buf][tid] = breg * gmul;
+    if (tid < kBK) {
+      const float c = breg * cmul;
+      const __bf16 c_hi = (__bf16)c;
+      const __bf16 c_lo = (__bf16)(c - (float)c_hi);
+      sB[buf][tid] = (uint32_t)__builtin_bit_cast(uint16_t, c_hi) |
+                     ((uint32_t)__builtin_bit_cast(uint16_t, c_lo) << 16);
+    }
   };
 
   // One 64-key tile for this wave's 32 rows.  MASK: the tile crosses the
@@ -194,46 +210,77 @@ __global__ __launch_bounds__(NW * 64, NW == 4 ? 2 : 1) void attn_bf16_kernel(
   // harmless in fp32 and bf16, and the O/l rescale is skipped.
   auto tile_step = [&](int buf, int k0, auto mask_tag) {
     constexpr bool MASK = decltype(mask_tag)::value;
+    // All fragment reads of the tile are issued before its MFMAs, so their
+    // LDS latency overlaps, and the two 32-key MFMA chains are interleaved
+    // so neither waits on its own previous result.
     f32x16 s[2];
+    uint4 cb[2];
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
+    for (int kb = 0; kb < 2; ++kb)
+      cb[kb] = make_uint4((has_bias && G == 0) ? sB[buf][kb * 32 + (lane & 31)] : 0u, 0u, 0u, 0u);
+    uint4 kf[2][NKS];
+#pragma unroll
+    for (int st = 0; st < NKS; ++st)
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) kf[kb][st] = sK[buf][(kb * 32 + (lane & 31)) * KROW + 2 * st + G];
+    __builtin_amdgcn_sched_barrier(0);  // keep every read ahead of the MFMAs
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
       for (int i = 0; i < 16; ++i) s[kb][i] = 0.0f;
-      const int r = kb * 32 + (lane & 31);
 #pragma unroll
-      for (int st = 0; st < NKS; ++st)
-        s[kb] = mfma32x32x16(as_bf16x8(sK[buf][r * KROW + 2 * st + G]), qf[st], s[kb]);
+    for (int st = 0; st < NKS; ++st)
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) s[kb] = mfma32x32x16(as_bf16x8(kf[kb][st]), qf[st], s[kb]);
+    if (has_bias) {
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) s[kb] = mfma32x32x16(as_bf16x8(cb[kb]), q_one, s[kb]);
     }
+    // V^T fragments of the value product, read now so their LDS latency
+    // overlaps the softmax below.
+    uint4 vf[NDB][4];
+#pragma unroll
+    for (int db = 0; db < NDB; ++db) {
+      const uint32_t* row = &sVt[buf][(db * 32 + (lane & 31)) * VROW];
+#pragma unroll
+      for (int kh = 0; kh < 4; ++kh) {  // (kb, hh) = (kh / 2, kh % 2)
+        const int w0 = 2 * ((kh >> 1) * 8 + 4 * (kh & 1) + G);  // keys 4G..4G+3 of the step
+        const uint2 a0 = *reinterpret_cast<const uint2*>(row + w0);
+        const uint2 a1 = *reinterpret_cast<const uint2*>(row + w0 + 4);  // keys +8..+11
+        vf[db][kh] = make_uint4(a0.x, a0.y, a1.x, a1.y);
+      }
+    }
+    __builtin_amdgcn_sched_barrier(0);
     float mx = -INFINITY;
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
-        const int key = kb * 32 + acc_row(i, lane);
-        float y = fmaf(s[kb][i], qk_scale, sB[buf][key]);
-        if (MASK && (k0 + key) > my_q) y = -INFINITY;
-        s[kb][i] = y;
-        mx = fmaxf(mx, y);
+        if (MASK) {
+          const int key = kb * 32 + acc_row(i, lane);
+          if ((k0 + key) > my_q) s[kb][i] = -INFINITY;
+        }
+        mx = fmaxf(mx, s[kb][i]);
       }
     mx = pair_max(mx);
-    if (__any(mx > m_run + kRescale)) {
+    if (__any(mx > m_run + rs_thr)) {
       const float m_new = fmaxf(m_run, mx);
-      const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+      const float alpha = __builtin_amdgcn_exp2f((m_run - m_new) * qk_scale);
       l_run *= alpha;
 #pragma unroll
       for (int db = 0; db < NDB; ++db)
 #pragma unroll
         for (int i = 0; i < 16; ++i) o[db][i] *= alpha;
       m_run = m_new;
+      nms = -m_new * qk_scale;
     }
-    float psum = 0.0f;
+    float psum = 0.0f;  // fp32 row sum (keeps lse exact to fp32 rounding)
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
-        const float p = __builtin_amdgcn_exp2f(s[kb][i] - m_run);
-        s[kb][i] = p;
-        psum += p;
+        s[kb][i] = __builtin_amdgcn_exp2f(fmaf(s[kb][i], qk_scale, nms));
+        psum += s[kb][i];
       }
     l_run += psum;
 
@@ -244,22 +291,11 @@ __global__ __launch_bounds__(NW * 64, NW == 4 ? 2 : 1) void attn_bf16_kernel(
       for (int hh = 0; hh < 2; ++hh)
 #pragma unroll
         for (int j = 0; j < 8; ++j) pb[kb][hh][j] = (__bf16)s[kb][8 * hh + j];
-
 #pragma unroll
-    for (int db = 0; db < NDB; ++db) {
-      const int d = db * 32 + (lane & 31);
-      const uint32_t* row = &sVt[buf][d * VROW];
+    for (int db = 0; db < NDB; ++db)
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int hh = 0; hh < 2; ++hh) {
-          const int w0 = 2 * (kb * 8 + 4 * hh + G);  // keys 4G..4G+3 of the step
-          const uint2 a0 = *reinterpret_cast<const uint2*>(row + w0);
-          const uint2 a1 = *reinterpret_cast<const uint2*>(row + w0 + 4);  // keys +8..+11
-          const uint4 a = make_uint4(a0.x, a0.y, a1.x, a1.y);
-          o[db] = mfma32x32x16(as_bf16x8(a), pb[kb][hh], o[db]);
-        }
-    }
+      for (int kh = 0; kh < 4; ++kh)
+        o[db] = mfma32x32x16(as_bf16x8(vf[db][kh]), pb[kh >> 1][kh & 1], o[db]);
   };
 
   // n_kt >= 1 here (q0 < n).  The unconditional first stage also retires the
@@ -309,7 +345,7 @@ __global__ __launch_bounds__(NW * 64, NW == 4 ? 2 : 1) void attn_bf16_kernel(
         }
         *reinterpret_cast<uint2*>(op + d0) = make_uint2(w[0], w[1]);
       }
-    if (lse != nullptr && G == 0) lse[(int64_t)h * Kt + lo + my_q] = (m_run + __log2f(l_tot)) * kLn2;
+    if (lse != nullptr && G == 0) lse[(int64_t)h * Kt + lo + my_q] = (m_run * qk_scale + __log2f(l_tot)) * kLn2;
   }
 }
 

@@ -165,7 +165,7 @@ int tg_gated_attn_fwd(const void* q, const void* k, const void* v, int64_t q_tok
   if (q_tok_stride < (int64_t)Hq * d || k_tok_stride < (int64_t)Hkv * d ||
       v_tok_stride < (int64_t)Hkv * d)
     return TG_ERR_SHAPE;
-  if (!isfinite(tau)) return TG_ERR_RANGE;
+  if (!isfinite(tau) || !(tau > 0.0f)) return TG_ERR_RANGE;
   if (d != 64 && d != 128) return TG_ERR_UNSUPPORTED;
   // a 64-key tile of k or v is addressed with 32-bit byte offsets
   if (k_tok_stride > (1 << 23) || v_tok_stride > (1 << 23)) return TG_ERR_UNSUPPORTED;

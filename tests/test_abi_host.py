@@ -168,6 +168,7 @@ def test_attention_argument_checks():
     assert call(qs=2000) == TG_ERR_SHAPE
     assert call(maxlen=101) == TG_ERR_SHAPE
     assert call(tau=float("inf")) == TG_ERR_RANGE
+    assert call(tau=0.0) == TG_ERR_RANGE and call(tau=-1.0) == TG_ERR_RANGE
     assert call(d=96, qs=96 * 16, ks=96 * 8, vs=96 * 8) == TG_ERR_UNSUPPORTED
     assert call(q=None) == TG_ERR_NULL
     assert call(bias=None) == TG_ERR_NULL  # gain given without bias
