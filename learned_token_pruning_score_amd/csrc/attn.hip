@@ -14,8 +14,8 @@
 //    y = acc * (tau log2e / sqrt(d)) + (g_h log2e) s_j; p = exp2(y - m).
 //  * P^T stays in registers: the accumulator layout of S^T is exactly the B
 //    operand layout of O^T += V^T P^T once keys are relabelled (within each
-//    16-key MFMA step, lane half G holds keys 4G..4G+3 and 8+4G..8+4G+3), so
-//    V is staged transposed in LDS and read as two 8-byte runs.
+//    16-key MFMA step, lane half G holds keys 4G..4G+3 and 8+4G..8+4G+3); V
+//    stays row-major in LDS and a transposing LDS read delivers those keys.
 //  * K rows and V^T rows are padded in LDS (odd multiples of the read
 //    width) so fragment reads of 32 rows spread over the banks.
 //  * Two LDS stages: the next tile's global loads are issued before the
@@ -68,13 +68,13 @@ __global__ __launch_bounds__(NW * 64, NW == 4 ? 2 : 1) void attn_bf16_kernel(
   constexpr int NDB = HD / 32;      // 32-row blocks of O^T
   constexpr int K_ITEMS = kBK * KCH;
   constexpr int K_PER_T = (K_ITEMS + NT - 1) / NT;
-  constexpr int V_ITEMS = (kBK / 2) * KCH;  // (key pair, 8-wide d chunk)
+  constexpr int V_ITEMS = kBK * KCH;  // 16-byte chunks of a V tile
   constexpr int V_PER_T = (V_ITEMS + NT - 1) / NT;
   constexpr int KROW = KCH + 1;     // 16-byte units per padded K row
-  constexpr int VROW = kBK / 2 + 2; // 32-bit words per padded V^T row (two keys each)
+  constexpr int VROW = KCH + 2;     // 16-byte units per padded V row (HD*2 + 32 bytes)
   // Two LDS stages: the next tile is written while the current one is read.
   __shared__ uint4 sK[2][kBK * KROW];
-  __shared__ uint32_t sVt[2][HD * VROW];
+  __shared__ uint4 sV[2][kBK * VROW];
   __shared__ uint32_t sB[2][kBK];  // per key: bias / scale as a bf16 (hi, lo) pair
 
   const int x = blockIdx.x;
@@ -139,17 +139,16 @@ __global__ __launch_bounds__(NW * 64, NW == 4 ? 2 : 1) void attn_bf16_kernel(
     const int id = tid + j * NT;
     k_off[j] = ((id / KCH) * (int)ks + (id % KCH) * 8) * 2;
   }
-  int v_off[V_PER_T][2];
+  int v_off[V_PER_T];
 #pragma unroll
   for (int j = 0; j < V_PER_T; ++j) {
     const int id = tid + j * NT;
-#pragma unroll
-    for (int e = 0; e < 2; ++e) v_off[j][e] = ((2 * (id / KCH) + e) * (int)vs + (id % KCH) * 8) * 2;
+    v_off[j] = ((id / KCH) * (int)vs + (id % KCH) * 8) * 2;
   }
   const float* bias_p = bias ? bias + lo : nullptr;
 
   uint4 kreg[K_PER_T];
-  uint4 vreg[V_PER_T][2];
+  uint4 vreg[V_PER_T];
   float breg = 0.0f;
   auto prefetch = [&](int k0) {
     const int rows = min(n - k0, kBK);
@@ -162,17 +161,15 @@ __global__ __launch_bounds__(NW * 64, NW == 4 ? 2 : 1) void attn_bf16_kernel(
       kreg[j] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rk, k_off[j], 0, 0));
 #pragma unroll
     for (int j = 0; j < V_PER_T; ++j)
-#pragma unroll
-      for (int e = 0; e < 2; ++e)
-        vreg[j][e] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rv, v_off[j][e], 0, 0));
+      vreg[j] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rv, v_off[j], 0, 0));
     if (bias_p != nullptr) {
       const __amdgpu_buffer_rsrc_t rb = __builtin_amdgcn_make_buffer_rsrc(
           (void*)(bias_p + k0), (short)0, rows * 4, kBufFlags);
       breg = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rb, (tid & (kBK - 1)) * 4, 0, 0));
     }
   };
-  // Registers -> LDS stage `buf`: K rows padded, V transposed to V^T (two
-  // keys per 32-bit word, packed with byte permutes), bias pre-scaled.
+  // Registers -> LDS stage `buf`: K and V rows copied as they are (padded
+  // rows), bias pre-scaled.
   auto stage = [&](int buf) {
 #pragma unroll
     for (int j = 0; j < K_PER_T; ++j) {
@@ -182,18 +179,7 @@ __global__ __launch_bounds__(NW * 64, NW == 4 ? 2 : 1) void attn_bf16_kernel(
 #pragma unroll
     for (int j = 0; j < V_PER_T; ++j) {
       const int id = tid + j * NT;
-      const int dc = id % KCH, p = id / KCH;
-      uint32_t* dst = &sVt[buf][(dc * 8) * VROW + p];
-      const uint4 a = vreg[j][0], c2 = vreg[j][1];
-      // word (d, key pair p) = (V[2p][d], V[2p+1][d]) for d = 8 dc + 0..7
-      dst[0 * VROW] = __builtin_amdgcn_perm(c2.x, a.x, 0x05040100u);
-      dst[1 * VROW] = __builtin_amdgcn_perm(c2.x, a.x, 0x07060302u);
-      dst[2 * VROW] = __builtin_amdgcn_perm(c2.y, a.y, 0x05040100u);
-      dst[3 * VROW] = __builtin_amdgcn_perm(c2.y, a.y, 0x07060302u);
-      dst[4 * VROW] = __builtin_amdgcn_perm(c2.z, a.z, 0x05040100u);
-      dst[5 * VROW] = __builtin_amdgcn_perm(c2.z, a.z, 0x07060302u);
-      dst[6 * VROW] = __builtin_amdgcn_perm(c2.w, a.w, 0x05040100u);
-      dst[7 * VROW] = __builtin_amdgcn_perm(c2.w, a.w, 0x07060302u);
+      sV[buf][(id / KCH) * VROW + (id % KCH)] = vreg[j];
     }
     if (tid < kBK) {
       const float c = breg * cmul;
@@ -237,18 +223,30 @@ __global__ __launch_bounds__(NW * 64, NW == 4 ? 2 : 1) void attn_bf16_kernel(
       for (int kb = 0; kb < 2; ++kb) s[kb] = mfma32x32x16(as_bf16x8(cb[kb]), q_one, s[kb]);
     }
     // V^T fragments of the value product, read now so their LDS latency
-    // overlaps the softmax below.
-    uint4 vf[NDB][4];
+    // overlaps the softmax below.  A transposing LDS read
+    // (ds_read_b64_tr_b16) turns the row-major V tile into the MFMA operand:
+    // within each 16-lane group, lane i receives element i % 4 of the 8-byte
+    // chunks addressed by lanes 4j + i / 4 (j = 0..3).  Lane s of group g
+    // therefore addresses key row 4 (g / 2) + s / 4 and columns
+    // 16 (g % 2) + 4 (s % 4) .. +3 of a 16-key step, and lane l receives keys
+    // 4G..4G+3 (then +8..+11) of head-dim row l % 32 of the block.
+    bf16x8 vf[NDB][4];
+    {
+      const int gi = lane & 15, g = lane >> 4;
+      const char* vb = reinterpret_cast<const char*>(&sV[buf][0]) +
+                       (4 * (g >> 1) + (gi >> 2)) * (VROW * 16) + (16 * (g & 1) + 4 * (gi & 3)) * 2;
 #pragma unroll
-    for (int db = 0; db < NDB; ++db) {
-      const uint32_t* row = &sVt[buf][(db * 32 + (lane & 31)) * VROW];
+      for (int db = 0; db < NDB; ++db)
 #pragma unroll
-      for (int kh = 0; kh < 4; ++kh) {  // (kb, hh) = (kh / 2, kh % 2)
-        const int w0 = 2 * ((kh >> 1) * 8 + 4 * (kh & 1) + G);  // keys 4G..4G+3 of the step
-        const uint2 a0 = *reinterpret_cast<const uint2*>(row + w0);
-        const uint2 a1 = *reinterpret_cast<const uint2*>(row + w0 + 4);  // keys +8..+11
-        vf[db][kh] = make_uint4(a0.x, a0.y, a1.x, a1.y);
-      }
+        for (int kh = 0; kh < 4; ++kh) {  // (kb, hh) = (kh / 2, kh % 2): keys kb*32 + 16hh ..
+          const char* p0 = vb + ((kh >> 1) * 32 + 16 * (kh & 1)) * (VROW * 16) + db * 64;
+          typedef short s4 __attribute__((ext_vector_type(4)));
+          const s4 lo4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+              (__attribute__((address_space(3))) s4*)(p0));
+          const s4 hi4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+              (__attribute__((address_space(3))) s4*)(p0 + 8 * (VROW * 16)));
+          vf[db][kh] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo4, hi4, 0, 1, 2, 3, 4, 5, 6, 7));
+        }
     }
     __builtin_amdgcn_sched_barrier(0);
     float mx = -INFINITY;
@@ -295,7 +293,7 @@ __global__ __launch_bounds__(NW * 64, NW == 4 ? 2 : 1) void attn_bf16_kernel(
     for (int db = 0; db < NDB; ++db)
 #pragma unroll
       for (int kh = 0; kh < 4; ++kh)
-        o[db] = mfma32x32x16(as_bf16x8(vf[db][kh]), pb[kh >> 1][kh & 1], o[db]);
+        o[db] = mfma32x32x16(vf[db][kh], pb[kh >> 1][kh & 1], o[db]);
   };
 
   // n_kt >= 1 here (q0 < n).  The unconditional first stage also retires the
