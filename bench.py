@@ -41,6 +41,11 @@ def parse():
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-phase-events", action="store_true",
                    help="time only whole steps (no per-phase events inside the timed region)")
+    p.add_argument("--copy-probe-mib", type=int, default=0,
+                   help="before the timed region, copy a buffer of this many MiB on the device "
+                        "(a kernel of known traffic for calibrating memory counters)")
+    p.add_argument("--graph", action="store_true",
+                   help="also time the step captured in a HIP graph (reported as graph_ms_per_step)")
     return p.parse_args()
 
 
@@ -132,6 +137,14 @@ def main():
 
     stream = torch.cuda.current_stream()
     phase_events = not args.no_phase_events
+    if args.copy_probe_mib > 0:
+        n = args.copy_probe_mib * (1 << 20)
+        src = torch.ones(n, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        dst.copy_(src)  # one device copy: reads n bytes, writes n bytes
+        torch.cuda.synchronize()
+        del src, dst
+        log(f"[bench] copy probe: {args.copy_probe_mib} MiB")
 
     def step(ev=None):
         if ev is not None:
@@ -173,6 +186,33 @@ def main():
     value = w.T * args.steps / (total_ms / 1e3)
     log(f"[bench] {args.steps} steps: {ms_per_step:.4f} ms/step, {value:.4g} tokens/s")
 
+    graph_ms = None
+    if args.graph:
+        # The same step captured once and replayed: one launch per replay
+        # instead of one per kernel.  Inputs and buffers are the eager ones.
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        cap = torch.cuda.Stream()
+        cap.wait_stream(stream)
+        with torch.cuda.stream(cap):
+            step()  # warm the capture stream
+            torch.cuda.synchronize()
+            with torch.cuda.graph(g, stream=cap):
+                step()
+        torch.cuda.synchronize()
+        for _ in range(args.warmup):
+            g.replay()
+        torch.cuda.synchronize()
+        gs = torch.cuda.Event(enable_timing=True)
+        ge = torch.cuda.Event(enable_timing=True)
+        gs.record(stream)
+        for _ in range(args.steps):
+            g.replay()
+        ge.record(stream)
+        torch.cuda.synchronize()
+        graph_ms = gs.elapsed_time(ge) / args.steps
+        log(f"[bench] graph replay: {graph_ms:.4f} ms/step, {w.T / (graph_ms / 1e3):.4g} tokens/s")
+
     work = algorithmic_work(w, Kt, gp.cu_kept_h)
     phases = None
     roof = None
@@ -200,7 +240,7 @@ def main():
             "attn_layers": s.layers,
         }
         achieved = work["attn_flop_per_layer"] / (attn_avg / 1e3) / 1e12
-        roof = {"bound": "mfma", "kernel": "attn_bf16_kernel<128>",
+        roof = {"bound": "mfma", "kernel": "attn_bf16_kernel<128, 8>",
                 "achieved": achieved, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                 "frac": achieved / PEAK_BF16_TFLOPS, "traffic": None,
                 "per_launch_flop": work["attn_flop_per_layer"],
@@ -232,6 +272,7 @@ def main():
         "roofline": roof,
         "cpu_baseline": cpu,
         "phases": phases,
+        "graph_ms_per_step": graph_ms,
     }
     print(json.dumps(line), flush=True)
 
