@@ -65,6 +65,30 @@ def algorithmic_work(w, Kt, cu_kept):
     }
 
 
+TRAFFIC_SUMMARY = os.path.join(ROOT, "profiles", "gated_prefill_128k_hbm_traffic.md")
+
+
+def measured_traffic(kernel, source):
+    """HBM bytes per launch of `kernel` from the committed FETCH_SIZE /
+    WRITE_SIZE summary, or None when the summary is missing or was taken on
+    a different version of the kernel's source."""
+    import hashlib
+    try:
+        with open(source, "rb") as f:
+            sha = hashlib.sha256(f.read()).hexdigest()
+        with open(TRAFFIC_SUMMARY) as f:
+            lines = f.read().splitlines()
+    except OSError:
+        return None
+    for line in lines:
+        if not line.startswith(kernel + " "):
+            continue
+        fields = dict(kv.split("=", 1) for kv in line[len(kernel) + 1:].split() if "=" in kv)
+        if fields.get("source_sha256") == sha:
+            return float(fields["traffic_bytes_per_launch"])
+    return None
+
+
 def cpu_baseline(w, q_layers, cu_kept, Kt):
     """The fp64 oracle on a bounded sample of the same workload, scaled to the
     whole step: gate, top-K and compaction on all tokens; attention for one
@@ -141,7 +165,7 @@ def main():
         n = args.copy_probe_mib * (1 << 20)
         src = torch.ones(n, dtype=torch.uint8, device=dev)
         dst = torch.empty_like(src)
-        dst.copy_(src)  # one device copy: reads n bytes, writes n bytes
+        torch.bitwise_not(src, out=dst)  # one elementwise kernel: reads n bytes, writes n bytes
         torch.cuda.synchronize()
         del src, dst
         log(f"[bench] copy probe: {args.copy_probe_mib} MiB")
@@ -240,9 +264,16 @@ def main():
             "attn_layers": s.layers,
         }
         achieved = work["attn_flop_per_layer"] / (attn_avg / 1e3) / 1e12
+        traffic = None
+        if s.name == "qwen3_1p7b_128k":
+            traffic = measured_traffic(
+                "attn_bf16_kernel<128, 8>",
+                os.path.join(ROOT, "learned_token_pruning_score_amd", "csrc", "attn.hip"))
         roof = {"bound": "mfma", "kernel": "attn_bf16_kernel<128, 8>",
                 "achieved": achieved, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                "frac": achieved / PEAK_BF16_TFLOPS, "traffic": None,
+                "frac": achieved / PEAK_BF16_TFLOPS, "traffic": traffic,
+                "traffic_unit": "HBM bytes per launch (FETCH_SIZE + WRITE_SIZE, copy-calibrated)",
+                "algorithmic_bytes_per_launch": work["attn_bytes_per_layer"],
                 "per_launch_flop": work["attn_flop_per_layer"],
                 "avg_launch_us": attn_avg * 1e3}
         log(f"[bench] phases: {json.dumps(phases)}")
