@@ -5,23 +5,27 @@
 //     x_ij = tau * q_i . k_j / sqrt(d) + g_h * s_j,   j <= i within a prompt
 //     o_i  = softmax_j(x_ij) v_j,  lse_i = ln sum_j exp(x_ij)
 //
-// bf16 path (gfx950 MFMA, fp32 accumulation), one workgroup of 4 waves per
-// (query head, prompt, 128-row query tile); wave w owns rows 32w..32w+31.
+// bf16 path (gfx950 MFMA, fp32 accumulation): one workgroup of 8 waves per
+// (query head, prompt, 256-row query tile); each wave owns 32 query rows.
 //  * Scores are formed transposed, S^T = K Q^T, with the 32x32x16 MFMA: lane
 //    l then holds 32 keys of query row (l & 31) per 64-key tile, so the
 //    softmax max and sum are lane-local plus one exchange with lane l ^ 32.
-//  * The bias and temperature fold into one FMA in the log2 domain:
-//    y = acc * (tau log2e / sqrt(d)) + (g_h log2e) s_j; p = exp2(y - m).
+//  * The bias and temperature fold into the score: the bias enters the MFMA
+//    as one more k-step and the logit is scale * acc, so p = exp2(scale *
+//    acc - scale * m) is one FMA and one exp2 per score.
 //  * P^T stays in registers: the accumulator layout of S^T is exactly the B
 //    operand layout of O^T += V^T P^T once keys are relabelled (within each
 //    16-key MFMA step, lane half G holds keys 4G..4G+3 and 8+4G..8+4G+3); V
 //    stays row-major in LDS and a transposing LDS read delivers those keys.
-//  * K rows and V^T rows are padded in LDS (odd multiples of the read
-//    width) so fragment reads of 32 rows spread over the banks.
-//  * Two LDS stages: the next tile's global loads are issued before the
-//    current tile's MFMAs and written to the other stage after them.
-//  * Causal masking only on tiles that cross the wave's diagonal; tiles are
-//    launched longest-first (tile index is the slowest grid dimension,
+//  * MFMA and vector ALU work overlap only across the waves of a SIMD, so
+//    the two waves sharing a SIMD alternate: while one issues only MFMAs
+//    (value product of its previous tile, scores of its next tile) the
+//    other runs only the softmax of its current tile (see the schedule).
+//  * Three LDS stages with padded rows (conflict-free fragment reads); the
+//    K and V halves of each tile are loaded by the two wave groups in their
+//    vector-ALU phases, one tile ahead.
+//  * Causal masking only on the tile that crosses a wave's diagonal; tiles
+//    are launched longest-first (tile index is the slowest grid dimension,
 //    reversed); the heads of one GQA group land on the same XCD.
 // fp32 path: one thread per (row, head), online softmax on vector ALUs.
 #include <math.h>
@@ -36,26 +40,15 @@ namespace {
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 constexpr int kBK = 64;   // keys per tile
-constexpr float kRescale = 8.0f;
+constexpr float kRescale = 8.0f;  // lazy-rescale threshold on the running max (log2 units)
 // Fourth word of a raw buffer descriptor (32-bit data format, no swizzle):
 // accesses at or past num_records read as zero.
-constexpr int kBufFlags = 0x00020000;  // lazy-rescale threshold on the running max (log2 units)
-#ifndef TG_ATTN_WAVES
-#define TG_ATTN_WAVES 8   // waves per workgroup; 32 query rows each
-#endif
-
-// LDS rows are padded so that a fragment read of 32 consecutive rows at one
-// column spreads over the banks, and every per-step offset is a constant:
-// a K row is HD*2 + 16 bytes (an odd number of 16-byte units), a V^T row is
-// 64 keys * 2 + 8 = 136 bytes (an odd number of 8-byte units).
-
-__device__ __forceinline__ unsigned elem16(const uint4& v, int e) {
-  const unsigned w = (e < 2) ? v.x : (e < 4) ? v.y : (e < 6) ? v.z : v.w;
-  return (e & 1) ? (w >> 16) : (w & 0xffffu);
-}
+constexpr int kBufFlags = 0x00020000;
+constexpr int KAHEAD = 2;  // k-steps of K fragments read ahead of their MFMAs
+constexpr int VAHEAD = 3;  // V fragments read ahead of their MFMAs
 
 template <int HD, int NW>
-__global__ __launch_bounds__(NW * 64, NW == 4 ? 2 : 1) void attn_bf16_kernel(
+__global__ __launch_bounds__(NW * 64, 1) void attn_bf16_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
     const uint16_t* __restrict__ v, int64_t qs, int64_t ks, int64_t vs,
     const float* __restrict__ bias, const float* __restrict__ gain, float qk_scale,
@@ -66,16 +59,17 @@ __global__ __launch_bounds__(NW * 64, NW == 4 ? 2 : 1) void attn_bf16_kernel(
   constexpr int KCH = HD / 8;       // 16-byte chunks per K row
   constexpr int NKS = HD / 16;      // MFMA k-steps over the head dim
   constexpr int NDB = HD / 32;      // 32-row blocks of O^T
-  constexpr int K_ITEMS = kBK * KCH;
-  constexpr int K_PER_T = (K_ITEMS + NT - 1) / NT;
-  constexpr int V_ITEMS = kBK * KCH;  // 16-byte chunks of a V tile
-  constexpr int V_PER_T = (V_ITEMS + NT - 1) / NT;
+  constexpr int K_ITEMS = kBK * KCH;  // 16-byte chunks of a K (or V) tile
+  // LDS rows are padded so that fragment reads spread over the banks: a K
+  // row is HD*2 + 16 bytes (an odd number of 16-byte units), a V row HD*2 +
+  // 64 bytes, so the eight rows one transposing read touches cover every
+  // bank exactly twice.
   constexpr int KROW = KCH + 1;     // 16-byte units per padded K row
-  constexpr int VROW = KCH + 2;     // 16-byte units per padded V row (HD*2 + 32 bytes)
-  // Two LDS stages: the next tile is written while the current one is read.
-  __shared__ uint4 sK[2][kBK * KROW];
-  __shared__ uint4 sV[2][kBK * VROW];
-  __shared__ uint32_t sB[2][kBK];  // per key: bias / scale as a bf16 (hi, lo) pair
+  constexpr int VROW = KCH + 4;     // 16-byte units per padded V row
+  // Three LDS stages (see the schedule below).
+  __shared__ uint4 sK[3][kBK * KROW];
+  __shared__ uint4 sV[3][kBK * VROW];
+  __shared__ uint32_t sB[3][kBK];  // per key: bias / scale as a bf16 (hi, lo) pair
 
   const int x = blockIdx.x;
   const int h = head_swizzle ? (x % 8) * (Hq / 8) + x / 8 : x;
@@ -89,7 +83,12 @@ __global__ __launch_bounds__(NW * 64, NW == 4 ? 2 : 1) void attn_bf16_kernel(
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
   const int G = lane >> 5;
-  const int qw = q0 + wave * 32;
+  // Waves w and w + 4 share a SIMD (the dispatcher places the waves of a
+  // workgroup round-robin over the four SIMDs; another placement would only
+  // cost speed).  They own the two 32-row halves of one 64-row block, so
+  // both cross the causal diagonal in the same key tile.
+  const int grp = wave >> 2;  // 0: first half of the block, 1: second
+  const int qw = q0 + 64 * (wave & 3) + 32 * grp;
   const int my_q = qw + (lane & 31);
   // The key bias enters the score MFMA as one more k-step: K gains the
   // columns (c_hi, c_lo) with c_hi + c_lo = g_h log2e s_j / scale (two bf16
@@ -127,128 +126,107 @@ __global__ __launch_bounds__(NW * 64, NW == 4 ? 2 : 1) void attn_bf16_kernel(
   const uint16_t* kbase = k + (int64_t)lo * ks + (int64_t)kvh * HD;
   const uint16_t* vbase = v + (int64_t)lo * vs + (int64_t)kvh * HD;
 
-  static_assert(K_ITEMS % NT == 0 && V_ITEMS % NT == 0, "tile split");
-  // Buffer-resource loads: the descriptor of each tile starts at its first
-  // key and ends at the prompt's last key (or 64 keys on), so rows past the
-  // prompt read as zero without a branch.  Such keys only occur in a tile
-  // that crosses the causal diagonal of every wave reading it, where they
-  // are masked.  Per-thread byte offsets are loop-invariant.
-  int k_off[K_PER_T];
-#pragma unroll
-  for (int j = 0; j < K_PER_T; ++j) {
-    const int id = tid + j * NT;
-    k_off[j] = ((id / KCH) * (int)ks + (id % KCH) * 8) * 2;
-  }
-  int v_off[V_PER_T];
-#pragma unroll
-  for (int j = 0; j < V_PER_T; ++j) {
-    const int id = tid + j * NT;
-    v_off[j] = ((id / KCH) * (int)vs + (id % KCH) * 8) * 2;
-  }
   const float* bias_p = bias ? bias + lo : nullptr;
 
-  uint4 kreg[K_PER_T];
-  uint4 vreg[V_PER_T];
+  // Staging split between the two wave groups, each in its vector ALU
+  // phase: group 0 writes the K rows and the bias of a tile, group 1 its V
+  // rows, 4 * 64 threads with HALF_T 16-byte chunks each.  Buffer-resource
+  // loads: the descriptor of each tile starts at its first key and ends at
+  // the prompt's last key (or 64 keys on), so rows past the prompt read as
+  // zero without a branch, and a tile wholly past the prompt reads nothing.
+  // Rows past the prompt only occur in a tile that crosses the causal
+  // diagonal of every wave reading it, where they are masked.
+  constexpr int HALF_T = K_ITEMS / (NT / 2);
+  static_assert(K_ITEMS % (NT / 2) == 0, "half split");
+  const int gtid = tid & (NT / 2 - 1);
+  int h_off[HALF_T];
+#pragma unroll
+  for (int j = 0; j < HALF_T; ++j) {
+    const int id = gtid + j * (NT / 2);
+    h_off[j] = ((id / KCH) * (int)(grp == 0 ? ks : vs) + (id % KCH) * 8) * 2;
+  }
+  uint4 hreg[HALF_T];
   float breg = 0.0f;
-  auto prefetch = [&](int k0) {
-    const int rows = min(n - k0, kBK);
-    const __amdgpu_buffer_rsrc_t rk = __builtin_amdgcn_make_buffer_rsrc(
-        (void*)(kbase + (int64_t)k0 * ks), (short)0, rows * (int)ks * 2, kBufFlags);
-    const __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc(
-        (void*)(vbase + (int64_t)k0 * vs), (short)0, rows * (int)vs * 2, kBufFlags);
+  auto prefetch_half = [&](int k0) __attribute__((always_inline)) {
+    // wave-uniform (kept in scalar registers, so the descriptors are too)
+    const int rows = __builtin_amdgcn_readfirstlane(max(min(n - k0, kBK), 0));
+    const uint16_t* base = grp == 0 ? kbase + (int64_t)k0 * ks : vbase + (int64_t)k0 * vs;
+    const int stride = grp == 0 ? (int)ks : (int)vs;
+    const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)base, (short)0, rows * stride * 2, kBufFlags);
 #pragma unroll
-    for (int j = 0; j < K_PER_T; ++j)
-      kreg[j] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rk, k_off[j], 0, 0));
-#pragma unroll
-    for (int j = 0; j < V_PER_T; ++j)
-      vreg[j] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rv, v_off[j], 0, 0));
-    if (bias_p != nullptr) {
+    for (int j = 0; j < HALF_T; ++j)
+      hreg[j] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, h_off[j], 0, 0));
+    if (grp == 0 && bias_p != nullptr) {
       const __amdgpu_buffer_rsrc_t rb = __builtin_amdgcn_make_buffer_rsrc(
           (void*)(bias_p + k0), (short)0, rows * 4, kBufFlags);
-      breg = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rb, (tid & (kBK - 1)) * 4, 0, 0));
+      breg = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rb, (gtid & (kBK - 1)) * 4, 0, 0));
     }
   };
-  // Registers -> LDS stage `buf`: K and V rows copied as they are (padded
-  // rows), bias pre-scaled.
-  auto stage = [&](int buf) {
+  auto stage_half = [&](int buf) __attribute__((always_inline)) {
 #pragma unroll
-    for (int j = 0; j < K_PER_T; ++j) {
-      const int id = tid + j * NT;
-      sK[buf][(id / KCH) * KROW + (id % KCH)] = kreg[j];
+    for (int j = 0; j < HALF_T; ++j) {
+      const int id = gtid + j * (NT / 2);
+      if (grp == 0) sK[buf][(id / KCH) * KROW + (id % KCH)] = hreg[j];
+      else sV[buf][(id / KCH) * VROW + (id % KCH)] = hreg[j];
     }
-#pragma unroll
-    for (int j = 0; j < V_PER_T; ++j) {
-      const int id = tid + j * NT;
-      sV[buf][(id / KCH) * VROW + (id % KCH)] = vreg[j];
-    }
-    if (tid < kBK) {
+    if (grp == 0 && gtid < kBK) {
       const float c = breg * cmul;
       const __bf16 c_hi = (__bf16)c;
       const __bf16 c_lo = (__bf16)(c - (float)c_hi);
-      sB[buf][tid] = (uint32_t)__builtin_bit_cast(uint16_t, c_hi) |
-                     ((uint32_t)__builtin_bit_cast(uint16_t, c_lo) << 16);
+      sB[buf][gtid] = (uint32_t)__builtin_bit_cast(uint16_t, c_hi) |
+                      ((uint32_t)__builtin_bit_cast(uint16_t, c_lo) << 16);
     }
   };
 
-  // One 64-key tile for this wave's 32 rows.  MASK: the tile crosses the
-  // wave's causal diagonal.  The running max is only moved when a row's max
-  // grows by more than kRescale (log2 units): until then p <= 2^kRescale,
-  // harmless in fp32 and bf16, and the O/l rescale is skipped.
-  auto tile_step = [&](int buf, int k0, auto mask_tag) {
-    constexpr bool MASK = decltype(mask_tag)::value;
-    // All fragment reads of the tile are issued before its MFMAs, so their
-    // LDS latency overlaps, and the two 32-key MFMA chains are interleaved
-    // so neither waits on its own previous result.
-    f32x16 s[2];
-    uint4 cb[2];
+  // Scores S^T = K Q^T (+ bias column) of one tile into s, two interleaved
+  // MFMA chains; the K fragments are read KAHEAD k-steps ahead.
+  f32x16 s[2];
+  auto qk = [&](int buf) __attribute__((always_inline)) {
+    // The lane's address in the stage is made opaque once, so each
+    // fragment read is that address plus an immediate offset.  kfrag: the
+    // fragments of k-step st for both key halves; st == NKS: the bias
+    // columns.
+    typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+    typedef __attribute__((address_space(3))) const u32x4 lds_u4;
+    uint32_t ka = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) const char*)
+        reinterpret_cast<const char*>(&sK[buf][(lane & 31) * KROW + G]);
+    asm volatile("" : "+v"(ka));
+    auto kfrag = [&](int st, uint4 (&f)[2]) __attribute__((always_inline)) {
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-      cb[kb] = make_uint4((has_bias && G == 0) ? sB[buf][kb * 32 + (lane & 31)] : 0u, 0u, 0u, 0u);
-    uint4 kf[2][NKS];
-#pragma unroll
-    for (int st = 0; st < NKS; ++st)
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb) kf[kb][st] = sK[buf][(kb * 32 + (lane & 31)) * KROW + 2 * st + G];
-    __builtin_amdgcn_sched_barrier(0);  // keep every read ahead of the MFMAs
+      for (int kb = 0; kb < 2; ++kb)
+        f[kb] = st < NKS ? __builtin_bit_cast(uint4, *(lds_u4*)(uintptr_t)(ka + ((kb * 32) * KROW + 2 * st) * 16))
+                         : make_uint4((has_bias && G == 0) ? sB[buf][kb * 32 + (lane & 31)] : 0u, 0u, 0u, 0u);
+    };
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
       for (int i = 0; i < 16; ++i) s[kb][i] = 0.0f;
+    // each fragment has its own registers: no copies between steps
+    uint4 f[NKS + 1][2];
 #pragma unroll
-    for (int st = 0; st < NKS; ++st)
+    for (int j = 0; j < KAHEAD; ++j) kfrag(j, f[j]);
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb) s[kb] = mfma32x32x16(as_bf16x8(kf[kb][st]), qf[st], s[kb]);
-    if (has_bias) {
+    for (int st = 0; st <= NKS; ++st) {
+      if (st + KAHEAD <= NKS) kfrag(st + KAHEAD, f[st + KAHEAD]);
+      __builtin_amdgcn_sched_barrier(0);
+      const bf16x8 bq = st < NKS ? qf[st < NKS ? st : 0] : q_one;
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb) s[kb] = mfma32x32x16(as_bf16x8(cb[kb]), q_one, s[kb]);
+      for (int kb = 0; kb < 2; ++kb) s[kb] = mfma32x32x16(as_bf16x8(f[st][kb]), bq, s[kb]);
+      __builtin_amdgcn_sched_barrier(0);
     }
-    // V^T fragments of the value product, read now so their LDS latency
-    // overlaps the softmax below.  A transposing LDS read
-    // (ds_read_b64_tr_b16) turns the row-major V tile into the MFMA operand:
-    // within each 16-lane group, lane i receives element i % 4 of the 8-byte
-    // chunks addressed by lanes 4j + i / 4 (j = 0..3).  Lane s of group g
-    // therefore addresses key row 4 (g / 2) + s / 4 and columns
-    // 16 (g % 2) + 4 (s % 4) .. +3 of a 16-key step, and lane l receives keys
-    // 4G..4G+3 (then +8..+11) of head-dim row l % 32 of the block.
-    bf16x8 vf[NDB][4];
-    {
-      const int gi = lane & 15, g = lane >> 4;
-      const char* vb = reinterpret_cast<const char*>(&sV[buf][0]) +
-                       (4 * (g >> 1) + (gi >> 2)) * (VROW * 16) + (16 * (g & 1) + 4 * (gi & 3)) * 2;
-#pragma unroll
-      for (int db = 0; db < NDB; ++db)
-#pragma unroll
-        for (int kh = 0; kh < 4; ++kh) {  // (kb, hh) = (kh / 2, kh % 2): keys kb*32 + 16hh ..
-          const char* p0 = vb + ((kh >> 1) * 32 + 16 * (kh & 1)) * (VROW * 16) + db * 64;
-          typedef short s4 __attribute__((ext_vector_type(4)));
-          const s4 lo4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-              (__attribute__((address_space(3))) s4*)(p0));
-          const s4 hi4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-              (__attribute__((address_space(3))) s4*)(p0 + 8 * (VROW * 16)));
-          vf[db][kh] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo4, hi4, 0, 1, 2, 3, 4, 5, 6, 7));
-        }
-    }
-    __builtin_amdgcn_sched_barrier(0);
+  };
+  // Softmax of the tile in s: masked max (MASK: the tile crosses the
+  // wave's diagonal), lazy rescale of O (the running max only moves when a
+  // row's max grows by more than kRescale, log2 units: until then
+  // p <= 2^kRescale, harmless in fp32 and bf16), p = exp2(scale * acc -
+  // scale * m), fp32 row sum, bf16 P^T.  P^T needs no shuffle: the S^T
+  // accumulator layout equals the B-operand layout once keys are relabelled
+  // (within each 16-key step, lane half G holds keys 4G..4G+3 and
+  // 8+4G..8+4G+3), which is the order pv reads V^T in.
+  bf16x8 pb[2][2];
+  auto softmax = [&](int k0, auto mask_tag) __attribute__((always_inline)) {
+    constexpr bool MASK = decltype(mask_tag)::value;
     float mx = -INFINITY;
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
@@ -281,47 +259,146 @@ __global__ __launch_bounds__(NW * 64, NW == 4 ? 2 : 1) void attn_bf16_kernel(
         psum += s[kb][i];
       }
     l_run += psum;
-
-    bf16x8 pb[2][2];
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
       for (int hh = 0; hh < 2; ++hh)
 #pragma unroll
         for (int j = 0; j < 8; ++j) pb[kb][hh][j] = (__bf16)s[kb][8 * hh + j];
+  };
+  // O^T += V^T P^T for the tile whose probabilities are in pb, V^T
+  // fragments read VAHEAD MFMAs ahead.  A transposing LDS read
+  // (ds_read_b64_tr_b16) turns the row-major V tile into the MFMA operand:
+  // within each 16-lane group, lane i receives element i % 4 of the 8-byte
+  // chunks addressed by lanes 4j + i / 4 (j = 0..3).  Lane s of group g
+  // therefore addresses key row 4 (g / 2) + s / 4 and columns
+  // 16 (g % 2) + 4 (s % 4) .. +3 of a 16-key step, and lane l receives keys
+  // 4G..4G+3 (then +8..+11) of head-dim row l % 32 of the block.
+  auto pv = [&](int buf) __attribute__((always_inline)) {
+    const int gi = lane & 15, g = lane >> 4;
+    typedef short s4 __attribute__((ext_vector_type(4)));
+    typedef __attribute__((address_space(3))) s4 lds_s4;
+    uint32_t va = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) const char*)(
+        reinterpret_cast<const char*>(&sV[buf][0]) + (4 * (g >> 1) + (gi >> 2)) * (VROW * 16) +
+        (16 * (g & 1) + 4 * (gi & 3)) * 2);
+    asm volatile("" : "+v"(va));  // opaque lane address: reads use immediate offsets
+    constexpr int NM = 4 * NDB;
+    // fragment m = (kh, db): keys 32 (kh / 2) + 16 (kh % 2) .., head-dim block db
+    auto vfrag = [&](int mi) __attribute__((always_inline)) {
+      const int kh = mi / NDB, db = mi % NDB;
+      const uint32_t a0 = va + ((kh >> 1) * 32 + 16 * (kh & 1)) * (VROW * 16) + db * 64;
+      const s4 lo4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s4*)(uintptr_t)a0);
+      const s4 hi4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s4*)(uintptr_t)(a0 + 8 * (VROW * 16)));
+      return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo4, hi4, 0, 1, 2, 3, 4, 5, 6, 7));
+    };
+    // each fragment has its own registers: no copies between steps
+    bf16x8 vf[NM];
 #pragma unroll
-    for (int db = 0; db < NDB; ++db)
+    for (int j = 0; j < VAHEAD; ++j) vf[j] = vfrag(j);
 #pragma unroll
-      for (int kh = 0; kh < 4; ++kh)
-        o[db] = mfma32x32x16(vf[db][kh], pb[kh >> 1][kh & 1], o[db]);
+    for (int mi = 0; mi < NM; ++mi) {
+      if (mi + VAHEAD < NM) vf[mi + VAHEAD] = vfrag(mi + VAHEAD);
+      __builtin_amdgcn_sched_barrier(0);
+      const int kh = mi / NDB, db = mi % NDB;
+      o[db] = mfma32x32x16(vf[mi], pb[kh >> 1][kh & 1], o[db]);
+      __builtin_amdgcn_sched_barrier(0);
+    }
   };
 
-  // n_kt >= 1 here (q0 < n).  The unconditional first stage also retires the
-  // Q loads on every path into the loop.
-  prefetch(0);
-  stage(0);
+  // Schedule.  Each key tile takes two barrier intervals.  In every
+  // interval one wave of each SIMD pair runs only MFMAs (the value product
+  // of its previous tile, then the scores of its next tile) while the other
+  // runs only vector ALU work (the softmax of its current tile, and its
+  // group's share of the staging), so the matrix core and the vector ALU of
+  // the SIMD are busy at the same time:
+  //   interval 2t:     group 0: PV(t - 1), QK(t)    group 1: softmax(t - 1), V rows of t + 1
+  //   interval 2t + 1: group 0: softmax(t), K rows of t + 1    group 1: PV(t - 1), QK(t)
+  // Tile t sits in LDS stage t % 3: the K rows of tile t + 1 replace those
+  // of tile t - 2 (last read in interval 2t - 3), its V rows those of tile
+  // t - 2 (last read in interval 2t - 1).  Every wave takes part in every
+  // barrier; the tile crossing its diagonal is its last and the only
+  // masked one.
+  const int t_diag = n_kt_w - 1;  // -1: no rows
+  const int n_loop = n_kt + 1;    // the last value products come one tile late
+  // unsigned, so the compiler knows LDS addresses are non-negative and folds
+  // the per-fragment offsets into the instructions
+  auto buf_of = [&](int t) __attribute__((always_inline)) { return (int)((unsigned)t % 3u); };
+  // this group's half of tile t from the registers into its stage, then
+  // the global loads of its half of tile t + 1 (landing two intervals on)
+  auto stage_next = [&](int t) __attribute__((always_inline)) {
+    stage_half(buf_of(t));
+    prefetch_half((t + 1) * kBK);
+  };
+  prefetch_half(0);
+  stage_half(0);
+  prefetch_half(kBK);
   __syncthreads();
-
-  // Every wave runs n_kt iterations (one barrier each) but computes only on
-  // the tiles its rows see: unmasked tiles, then the one tile crossing its
-  // diagonal, then staging-only iterations.  Three straight loops keep the
-  // accumulators in place (no merge of differently computed values).
-  auto iteration = [&](int kt, auto mode_tag) {
-    constexpr int MODE = decltype(mode_tag)::value;  // 0 stage only, 1 unmasked, 2 masked
-    const int buf = kt & 1;
-    if (kt + 1 < n_kt) prefetch((kt + 1) * kBK);
-    if constexpr (MODE == 1) tile_step(buf, kt * kBK, std::false_type{});
-    if constexpr (MODE == 2) tile_step(buf, kt * kBK, std::true_type{});
-    if (kt + 1 < n_kt) stage(buf ^ 1);
-    __syncthreads();
-  };
-  int kt = 0;
-  for (; kt + 1 < n_kt_w; ++kt) iteration(kt, std::integral_constant<int, 1>{});
-  if (kt < n_kt_w) {
-    iteration(kt, std::integral_constant<int, 2>{});
-    ++kt;
+  int t = 0;
+  if (grp == 0) {
+    if (t_diag >= 0) {
+      qk(0);
+      __syncthreads();
+      stage_next(1);
+      if (t_diag == 0) softmax(0, std::true_type{});
+      else softmax(0, std::false_type{});
+      __syncthreads();
+      t = 1;
+      for (; t < t_diag; ++t) {
+        pv(buf_of(t - 1));
+        qk(buf_of(t));
+        __syncthreads();
+        stage_next(t + 1);
+        softmax(t * kBK, std::false_type{});
+        __syncthreads();
+      }
+      if (t == t_diag) {
+        pv(buf_of(t - 1));
+        qk(buf_of(t));
+        __syncthreads();
+        stage_next(t + 1);
+        softmax(t * kBK, std::true_type{});
+        __syncthreads();
+        ++t;
+      }
+      pv(buf_of(t - 1));  // t == t_diag + 1: the last value product
+      __syncthreads();
+      stage_next(t + 1);
+      __syncthreads();
+      ++t;
+    }
+    for (; t < n_loop; ++t) {
+      __syncthreads();
+      stage_next(t + 1);
+      __syncthreads();
+    }
+  } else {
+    if (t_diag >= 0) {
+      stage_next(1);
+      __syncthreads();
+      qk(0);
+      __syncthreads();
+      t = 1;
+      for (; t <= t_diag; ++t) {
+        stage_next(t + 1);
+        softmax((t - 1) * kBK, std::false_type{});
+        __syncthreads();
+        pv(buf_of(t - 1));
+        qk(buf_of(t));
+        __syncthreads();
+      }
+      stage_next(t + 1);  // t == t_diag + 1
+      softmax(t_diag * kBK, std::true_type{});
+      __syncthreads();
+      pv(buf_of(t - 1));
+      __syncthreads();
+      ++t;
+    }
+    for (; t < n_loop; ++t) {
+      stage_next(t + 1);
+      __syncthreads();
+      __syncthreads();
+    }
   }
-  for (; kt < n_kt; ++kt) iteration(kt, std::integral_constant<int, 0>{});
 
   if (!wave_active) return;
   const float l_tot = pair_sum(l_run);
@@ -396,25 +473,22 @@ hipError_t launch_attn_bf16(const void* q, const void* k, const void* v, int64_t
                             int Hkv, int d, void* out, float* lse, hipStream_t s) {
   if (B == 0 || max_len == 0) return hipSuccess;
   const int group = Hq / Hkv;
-  // head_dim 128: TG_ATTN_WAVES waves (32 query rows each) per workgroup;
-  // head_dim 64: 4 waves (a 64x64 V tile gives 256 transpose items).
-  constexpr int NW = TG_ATTN_WAVES;
+  // 8 waves (4 SIMD pairs), 32 query rows each
+  constexpr int NW = 8;
   const int swz = (Hq % 8 == 0 && ((Hq / 8) % group) == 0) ? 1 : 0;
   const float qk_scale = tau * kLog2e / sqrtf((float)d);
   const auto* qq = static_cast<const uint16_t*>(q);
   const auto* kk = static_cast<const uint16_t*>(k);
   const auto* vv = static_cast<const uint16_t*>(v);
   auto* oo = static_cast<uint16_t*>(out);
+  const int n_qtiles = (max_len + 32 * NW - 1) / (32 * NW);
+  const dim3 grid((unsigned)Hq, (unsigned)B, (unsigned)n_qtiles);
   if (d == 128) {
-    const int n_qtiles = (max_len + 32 * NW - 1) / (32 * NW);
-    const dim3 grid((unsigned)Hq, (unsigned)B, (unsigned)n_qtiles);
     hipLaunchKernelGGL((attn_bf16_kernel<128, NW>), grid, dim3(64 * NW), 0, s, qq, kk, vv, qs, ks,
                        vs, bias, gain, qk_scale, cu_kept, Hq, group, swz, n_qtiles, Kt, oo, lse);
   } else if (d == 64) {
-    const int n_qtiles = (max_len + 127) / 128;
-    const dim3 grid((unsigned)Hq, (unsigned)B, (unsigned)n_qtiles);
-    hipLaunchKernelGGL((attn_bf16_kernel<64, 4>), grid, dim3(256), 0, s, qq, kk, vv, qs, ks, vs,
-                       bias, gain, qk_scale, cu_kept, Hq, group, swz, n_qtiles, Kt, oo, lse);
+    hipLaunchKernelGGL((attn_bf16_kernel<64, NW>), grid, dim3(64 * NW), 0, s, qq, kk, vv, qs, ks,
+                       vs, bias, gain, qk_scale, cu_kept, Hq, group, swz, n_qtiles, Kt, oo, lse);
   } else {
     return hipErrorInvalidValue;
   }
