@@ -3,202 +3,210 @@
 // post-attention residual at the gate layer):
 //     s_t = b2 + sum_f w2[f] * SiLU(b1[f] + W1[f, :] . hidden[t, :])
 //
-// bf16 path: one workgroup of 2 * F/64 waves scores 256 tokens.  The product
-// is computed transposed, C^T[f][t] = W1[f] . h[t], with the 32x32x16 bf16
-// MFMA, so that each lane of the accumulator holds one token's column and a
-// run of F rows: the SiLU . w2 epilogue then reduces over F inside the lane,
-// across the two wave halves, and across the F-quarter waves through LDS, in
-// a fixed order (bit-reproducible, no atomics).  The [T, F] activation never
-// reaches memory.  hidden and W1 stream through four LDS stages of 32
-// columns, filled by buffer-to-LDS loads (no registers in between) issued
-// three stages ahead of the MFMAs that read them.
+// bf16 path: the product is computed transposed, C^T[f][t] = W1[f] . h[t],
+// with the 32x32x16 bf16 MFMA.  A workgroup of 8 waves owns tiles of 256
+// tokens, each wave 32 tokens and all F rows, so that every lane of the
+// accumulators holds one token's column: the SiLU . w2 epilogue reduces over
+// F inside the lane and across the two wave halves, in a fixed order
+// (bit-reproducible, no atomics), and the [T, F] activation never reaches
+// memory.  hidden is read once, from HBM straight into the registers that
+// serve as the MFMA's B operand, three stages of 64 columns ahead of their
+// use (the register file holds far more bytes in flight than LDS could);
+// W1, which every tile reads in full, streams through four LDS stages filled
+// by buffer-to-LDS loads.  One workgroup per CU loops over tiles, and the
+// loads run ahead across tile boundaries.
 #include "tg_common.h"
 
 namespace tg {
 namespace {
 
-constexpr int kGateBM = 256;  // tokens per workgroup
-constexpr int kGateBK = 32;   // reduction columns per LDS stage
-constexpr int kGateStages = 4;
+constexpr int kGateBM = 256;   // tokens per tile: 8 waves x 32
+constexpr int kGateBK = 64;    // reduction columns per stage (128-byte row segments)
+constexpr int kGateAhead = 3;  // stages loaded ahead of the one computed
 constexpr int kBufFlags = 0x00020000;  // raw buffer: reads past num_records give 0
 
-// Stage layout: a row of 32 bf16 columns is four 16-byte chunks, rows are
-// packed (64 bytes), and chunk c of row r sits at position c ^ ((r >> 2) & 3)
-// so that a fragment read of 16 consecutive rows at one column touches 16
-// different bank groups.
-__device__ __forceinline__ int gate_swz(int r, int c) { return c ^ ((r >> 2) & 3); }
+// A staged row of W1 is 64 columns = eight 16-byte chunks; logical chunk c
+// of row r sits at position c ^ ((r >> 1) & 7), so that the fragment reads
+// of 16 consecutive rows at one chunk touch 16 different 16-byte bank groups.
+__device__ __forceinline__ int gate_swz(int r, int c) { return c ^ ((r >> 1) & 7); }
 
-template <int NFQ>  // number of 64-wide F quarters (F = 64 * NFQ)
-__global__ __launch_bounds__(128 * NFQ) void gate_bf16_kernel(
-    const uint16_t* __restrict__ hidden, int64_t ld, int64_t T, int D,
+// One 16-byte buffer-to-LDS load per lane: lane l writes bytes
+// [16 l, 16 l + 16) of lds.  Out-of-range reads write zeros.
+__device__ __forceinline__ void lds_load16(__amdgpu_buffer_rsrc_t r, char* lds, int voff) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)lds, 16, voff, 0, 0, 0);
+}
+
+// Reduction order inside a stage.  A lane of half h = lane / 32 supplies,
+// for k-step j, the 8 columns [32 h + 8 j, 32 h + 8 j + 8) of its stage: for
+// hidden that is the j-th 16 bytes of the 64 contiguous bytes it loads, and
+// the W1 fragments follow the same column map, so the products sum over the
+// same columns as the definition, in another order.
+template <int NFB>  // F = 32 * NFB
+__global__ __launch_bounds__(512, 1) void gate_bf16_kernel(
+    const uint16_t* __restrict__ hidden, int64_t ld, int64_t T, int D, int n_tiles,
     const uint16_t* __restrict__ W1, const float* __restrict__ b1,
     const float* __restrict__ w2, float b2, float* __restrict__ scores) {
-  constexpr int F = 64 * NFQ;
-  constexpr int NT = 128 * NFQ;              // threads
-  constexpr int NW = NT / 64;                // waves
-  constexpr int ROW_B = kGateBK * 2;         // bytes per staged row
-  constexpr int H_BYTES = kGateBM * ROW_B;   // hidden stage
-  constexpr int W_BYTES = F * ROW_B;         // W1 stage
-  constexpr int H_DMA = H_BYTES / 1024 / NW; // 1 KB wave copies per wave per stage
-  constexpr int W_DMA = W_BYTES / 1024 / NW;
-  constexpr int ND = H_DMA + W_DMA;          // global loads per thread per stage
-  static_assert(H_BYTES % (1024 * NW) == 0 && W_BYTES % (1024 * NW) == 0, "stage split");
+  constexpr int F = 32 * NFB;
+  constexpr int NW = 8;
+  constexpr int W_BYTES = F * kGateBK * 2;    // one stage of W1
+  constexpr int W_DMA = W_BYTES / 1024 / NW;  // 1 KB buffer-to-LDS copies per wave per stage
+  constexpr int PER = W_DMA + 4;              // vector-memory instructions per wave per stage
+  static_assert(W_BYTES % (1024 * NW) == 0, "stage split");
 
-  // Four stages, each its own array so that the compiler can tell the stage
-  // being loaded from the ones being read.
-  __shared__ __attribute__((aligned(16))) char sh_h0[H_BYTES], sh_h1[H_BYTES], sh_h2[H_BYTES], sh_h3[H_BYTES];
-  __shared__ __attribute__((aligned(16))) char sh_w0[W_BYTES], sh_w1[W_BYTES], sh_w2[W_BYTES], sh_w3[W_BYTES];
-  __shared__ float sh_red[NFQ][kGateBM];
+  __shared__ __attribute__((aligned(16))) char sw0[W_BYTES], sw1[W_BYTES], sw2[W_BYTES], sw3[W_BYTES];
+  __shared__ __attribute__((aligned(16))) float sb1[F], sw2v[F];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int wt = wave / NFQ;  // token half: tokens [128 wt, 128 wt + 128)
-  const int wf = wave % NFQ;  // F quarter: rows [64 wf, 64 wf + 64)
-  const int64_t t0 = (int64_t)blockIdx.x * kGateBM;
-  const int rows = (int)min((int64_t)kGateBM, T - t0);
-  const uint16_t* hbase = hidden + t0 * ld;
-
-  // Per-thread source offsets of its 16 bytes in each wave copy: copy j of
-  // this wave covers rows 16 (wave * COPIES + j) .. +15; lane l writes
-  // position l % 4 of row l / 4, which holds the row's chunk
-  // (l % 4) ^ ((row >> 2) & 3).
-  int h_src[H_DMA], w_src[W_DMA];
-#pragma unroll
-  for (int j = 0; j < H_DMA; ++j) {
-    const int r = (wave * H_DMA + j) * 16 + (lane >> 2);
-    h_src[j] = (r * (int)ld + gate_swz(r, lane & 3) * 8) * 2;
+  for (int f = tid; f < F; f += NW * 64) {
+    sb1[f] = b1 ? b1[f] : 0.0f;
+    sw2v[f] = w2[f];
   }
+
+  // Stages per tile, rounded up to a multiple of four (the unroll below);
+  // stages past D load zeros and add nothing.
+  const int nk = (D / kGateBK + 3) & ~3;
+  const int my_tiles = ((int)blockIdx.x < n_tiles) ? (n_tiles - 1 - (int)blockIdx.x) / (int)gridDim.x + 1 : 0;
+  const int n_steps = my_tiles * nk;
+
+  // hidden: lane loads 64 contiguous bytes of token wave * 32 + lane % 32
+  const int h_voff = ((wave * 32 + (lane & 31)) * (int)ld + (lane >> 5) * 32) * 2;
+  // W1 copies: copy j of this wave fills rows 8 (wave * W_DMA + j) .. +7;
+  // lane l writes position l % 8 of row l / 8, which holds that row's
+  // logical chunk gate_swz(row, l % 8).
+  int w_src[W_DMA];
 #pragma unroll
   for (int j = 0; j < W_DMA; ++j) {
-    const int r = (wave * W_DMA + j) * 16 + (lane >> 2);
-    w_src[j] = (r * D + gate_swz(r, lane & 3) * 8) * 2;
+    const int r = (wave * W_DMA + j) * 8 + (lane >> 3);
+    w_src[j] = (r * D + gate_swz(r, lane & 7) * 8) * 2;
   }
-  // Buffer-to-LDS loads of reduction columns [k0, k0 + 32) into one stage;
-  // hidden rows past T, and columns past D, read as zero (the descriptor's
-  // range check also keeps every access inside the two arrays).  The loads
-  // are written as instructions of their own so that the compiler does not
-  // wait for them at the next LDS read: their completion is waited for
-  // explicitly, two stages later, before the barrier that precedes the
-  // first read of their stage.
-  auto dma = [&](const uint16_t* base, int bytes, char* lds, int voff) __attribute__((always_inline)) {
-    const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc((void*)base, (short)0, bytes, kBufFlags);
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)lds, 16, voff, 0, 0, 0);
-  };
-  auto load_stage = [&](int k0, char* sh, char* sw) __attribute__((always_inline)) {
-    const int kk = __builtin_amdgcn_readfirstlane(min(k0, D));
-    const int hb = __builtin_amdgcn_readfirstlane(k0 < D ? rows * (int)ld * 2 - kk * 2 : 0);
-    const int wb = __builtin_amdgcn_readfirstlane(k0 < D ? F * D * 2 - kk * 2 : 0);
+  // W1 fragment of F block fb, k-step ks: row 32 fb + lane % 32, logical
+  // chunk 4 (lane / 32) + ks; the swizzle term depends on the lane only.
+  int a_off[4];
 #pragma unroll
-    for (int j = 0; j < H_DMA; ++j) dma(hbase + kk, hb, sh + (wave * H_DMA + j) * 1024, h_src[j]);
-#pragma unroll
-    for (int j = 0; j < W_DMA; ++j) dma(W1 + kk, wb, sw + (wave * W_DMA + j) * 1024, w_src[j]);
-  };
+  for (int ks = 0; ks < 4; ++ks)
+    a_off[ks] = (lane & 31) * (kGateBK * 2) + gate_swz(lane & 31, 4 * (lane >> 5) + ks) * 16;
 
-  f32x16 acc[2][4];
+  // Load position: tile ld_tile (a multiple of gridDim.x past blockIdx.x),
+  // stage ld_k of it.  Loads past the last tile read nothing (zero range).
+  int ld_tile = blockIdx.x, ld_k = 0;
+  auto issue = [&](char* sw, uint4 (&h)[4]) __attribute__((always_inline)) {
+    const int64_t tt0 = (int64_t)ld_tile * kGateBM;
+    const int rows = ld_tile < n_tiles ? (int)min((int64_t)kGateBM, T - tt0) : 0;
+    const int k0 = ld_k * kGateBK;
+    const bool kin = k0 < D;
+    const int kk = kin ? k0 : 0;
+    const int hb = __builtin_amdgcn_readfirstlane((rows > 0 && kin) ? rows * (int)ld * 2 - kk * 2 : 0);
+    const int wb = __builtin_amdgcn_readfirstlane(kin ? F * D * 2 - kk * 2 : 0);
+    const uint16_t* hb_ptr = rows > 0 ? hidden + tt0 * ld + kk : hidden;
+    const __amdgpu_buffer_rsrc_t rh = __builtin_amdgcn_make_buffer_rsrc((void*)hb_ptr, (short)0, hb, kBufFlags);
+    const __amdgpu_buffer_rsrc_t rw = __builtin_amdgcn_make_buffer_rsrc((void*)(W1 + kk), (short)0, wb, kBufFlags);
 #pragma unroll
-  for (int a = 0; a < 2; ++a)
+    for (int j = 0; j < W_DMA; ++j)
+      lds_load16(rw, sw + (wave * W_DMA + j) * 1024, w_src[j]);
 #pragma unroll
-    for (int b = 0; b < 4; ++b)
-#pragma unroll
-      for (int i = 0; i < 16; ++i) acc[a][b][i] = 0.0f;
-
-  // MFMAs over one stage: two k-steps of 16 columns.  Every fragment row
-  // is a multiple of 32 plus lane % 32, so its swizzle term is
-  // (lane >> 2) & 3 and the per-lane part of the address depends on the
-  // k-step only; rows of different fragments differ by constants.
-  int a_off[kGateBK / 16], b_off[kGateBK / 16];
-#pragma unroll
-  for (int ks = 0; ks < kGateBK / 16; ++ks) {
-    const int lane_part = (lane & 31) * ROW_B + (((ks * 2 + (lane >> 5)) ^ ((lane >> 2) & 3)) * 16);
-    a_off[ks] = wf * 64 * ROW_B + lane_part;
-    b_off[ks] = wt * 128 * ROW_B + lane_part;
-  }
-  auto compute_stage = [&](const char* sh, const char* sw) __attribute__((always_inline)) {
-#pragma unroll
-    for (int ks = 0; ks < kGateBK / 16; ++ks) {
-      bf16x8 fa[2], fb[4];
-#pragma unroll
-      for (int fbk = 0; fbk < 2; ++fbk)
-        fa[fbk] = *reinterpret_cast<const bf16x8*>(sw + a_off[ks] + fbk * 32 * ROW_B);
-#pragma unroll
-      for (int tb = 0; tb < 4; ++tb)
-        fb[tb] = *reinterpret_cast<const bf16x8*>(sh + b_off[ks] + tb * 32 * ROW_B);
-#pragma unroll
-      for (int fbk = 0; fbk < 2; ++fbk)
-#pragma unroll
-        for (int tb = 0; tb < 4; ++tb) acc[fbk][tb] = mfma32x32x16(fa[fbk], fb[tb], acc[fbk][tb]);
+    for (int j = 0; j < 4; ++j)
+      h[j] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rh, h_voff + 16 * j, 0, 0));
+    if (++ld_k == nk) {
+      ld_k = 0;
+      ld_tile += gridDim.x;
     }
   };
-  // End of a stage: this wave's loads of the stage two steps back are
-  // complete (ND loads are issued per stage and complete in order) and its
-  // LDS reads are done; then all waves meet.  An LDS-only barrier: the
-  // loads of the newer stages stay in flight across it.
-#define TG_GATE_SYNC() asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(2 * ND) : "memory")
 
-  // Stage s holds reduction columns [32 k, 32 k + 32) for k = s mod 4; the
-  // loads of k + 3 are issued while k is computed.  The step count is
-  // rounded up to a multiple of four: steps past D load zeros (an
-  // out-of-range buffer-to-LDS load writes zeros) and add nothing.
-  const int nk = (D / kGateBK + 3) & ~3;
-  load_stage(0, sh_h0, sh_w0);
-  load_stage(kGateBK, sh_h1, sh_w1);
-  load_stage(2 * kGateBK, sh_h2, sh_w2);
-  TG_GATE_SYNC();
-  for (int k = 0; k < nk; k += 4) {
-    load_stage((k + 3) * kGateBK, sh_h3, sh_w3);
-    compute_stage(sh_h0, sh_w0);
+  f32x16 acc[NFB];
+#pragma unroll
+  for (int fb = 0; fb < NFB; ++fb)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) acc[fb][i] = 0.0f;
+
+  // One stage: 4 k-steps x NFB F blocks; each W1 fragment is read three
+  // MFMAs ahead of its use.
+  constexpr int NM = 4 * NFB;
+  constexpr int AHEAD = 3;
+  auto compute = [&](const char* sw, const uint4 (&h)[4]) __attribute__((always_inline)) {
+    bf16x8 fa[NM];
+    auto frag = [&](int m) __attribute__((always_inline)) {
+      const int ks = m / NFB, fb = m % NFB;
+      return *reinterpret_cast<const bf16x8*>(sw + a_off[ks] + fb * 32 * (kGateBK * 2));
+    };
+#pragma unroll
+    for (int m = 0; m < AHEAD; ++m) fa[m] = frag(m);
+#pragma unroll
+    for (int m = 0; m < NM; ++m) {
+      if (m + AHEAD < NM) fa[m + AHEAD] = frag(m + AHEAD);
+      __builtin_amdgcn_sched_barrier(0);
+      const int ks = m / NFB, fb = m % NFB;
+      acc[fb] = mfma32x32x16(fa[m], as_bf16x8(h[ks]), acc[fb]);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  };
+
+  // Epilogue of one tile: lane holds token column lane % 32 and F rows
+  // 32 fb + acc_row(i, lane).
+  int ep_tile = blockIdx.x;
+  auto epilogue = [&]() __attribute__((always_inline)) {
+    float p[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+    for (int fb = 0; fb < NFB; ++fb)
+#pragma unroll
+      for (int i4 = 0; i4 < 4; ++i4) {
+        const int f = fb * 32 + 8 * i4 + 4 * (lane >> 5);
+        const float4 bb = *reinterpret_cast<const float4*>(&sb1[f]);
+        const float4 ww = *reinterpret_cast<const float4*>(&sw2v[f]);
+        const float bv[4] = {bb.x, bb.y, bb.z, bb.w}, wv[4] = {ww.x, ww.y, ww.z, ww.w};
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+          const float a = acc[fb][4 * i4 + c] + bv[c];
+          const float z = a * __builtin_amdgcn_rcpf(1.0f + __expf(-a));
+          p[c] = fmaf(wv[c], z, p[c]);
+        }
+      }
+    const float part = pair_sum((p[0] + p[1]) + (p[2] + p[3]));
+    const int64_t t = (int64_t)ep_tile * kGateBM + wave * 32 + lane;
+    if (lane < 32 && t < T) scores[t] = part + b2;
+    ep_tile += gridDim.x;
+  };
+
+  // End of a stage's wait: this wave's loads of the stage about to be
+  // computed are complete (PER loads per stage, completing in order; the
+  // two newer stages stay in flight) and its LDS reads of the previous
+  // stage are done; then all waves meet, so the stage's W1 copy is whole and
+  // the buffer the next loads fill is no longer read.
+#define TG_GATE_SYNC() asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"((kGateAhead - 1) * PER) : "memory")
+
+  uint4 h0[4], h1[4], h2[4], h3[4];
+  issue(sw0, h0);
+  issue(sw1, h1);
+  issue(sw2, h2);
+  int kc = 0;
+  for (int s = 0; s < n_steps; s += 4) {
     TG_GATE_SYNC();
-    load_stage((k + 4) * kGateBK, sh_h0, sh_w0);
-    compute_stage(sh_h1, sh_w1);
+    issue(sw3, h3);
+    compute(sw0, h0);
     TG_GATE_SYNC();
-    load_stage((k + 5) * kGateBK, sh_h1, sh_w1);
-    compute_stage(sh_h2, sh_w2);
+    issue(sw0, h0);
+    compute(sw1, h1);
     TG_GATE_SYNC();
-    load_stage((k + 6) * kGateBK, sh_h2, sh_w2);
-    compute_stage(sh_h3, sh_w3);
+    issue(sw1, h1);
+    compute(sw2, h2);
     TG_GATE_SYNC();
+    issue(sw2, h2);
+    compute(sw3, h3);
+    kc += 4;
+    if (kc == nk) {
+      kc = 0;
+      epilogue();
+#pragma unroll
+      for (int fb = 0; fb < NFB; ++fb)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) acc[fb][i] = 0.0f;
+    }
   }
 #undef TG_GATE_SYNC
-  // the trailing loads (past D) must land before the workgroup's LDS is released
+  // the loads issued past the last stage must land before the workgroup's
+  // LDS is released
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-  __syncthreads();
-
-  // Epilogue: lane holds token column (lane & 31) of each token block and F
-  // rows acc_row(i, lane) of each F block.
-  float bb[2][16], ww[2][16];
-#pragma unroll
-  for (int fbk = 0; fbk < 2; ++fbk)
-#pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const int f = wf * 64 + fbk * 32 + acc_row(i, lane);
-      bb[fbk][i] = b1 ? b1[f] : 0.0f;
-      ww[fbk][i] = w2[f];
-    }
-#pragma unroll
-  for (int tb = 0; tb < 4; ++tb) {
-    float part = 0.0f;
-#pragma unroll
-    for (int fbk = 0; fbk < 2; ++fbk)
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const float a = acc[fbk][tb][i] + bb[fbk][i];
-        const float z = a / (1.0f + __expf(-a));
-        part = fmaf(ww[fbk][i], z, part);
-      }
-    part = pair_sum(part);
-    if (lane < 32) sh_red[wf][wt * 128 + tb * 32 + lane] = part;
-  }
-  __syncthreads();
-  for (int r = tid; r < kGateBM; r += NT) {
-    const int64_t t = t0 + r;
-    if (t < T) {
-      float sum = 0.0f;
-#pragma unroll
-      for (int q = 0; q < NFQ; ++q) sum += sh_red[q][r];
-      scores[t] = sum + b2;
-    }
-  }
 }
 
 // fp32 path: one wave per token, lanes split F; the dot products over D run
@@ -230,13 +238,26 @@ hipError_t launch_gate_bf16(const void* hidden, int64_t ld, int64_t T, int D, co
                             const float* b1, const float* w2, float b2, int F, float* scores,
                             hipStream_t s) {
   if (T == 0) return hipSuccess;
-  const dim3 grid((unsigned)((T + kGateBM - 1) / kGateBM));
+  // one workgroup per CU, each looping over tiles
+  static int n_cu[64] = {0};
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= 64) return hipErrorInvalidDevice;
+  if (n_cu[dev] == 0) {
+    int c = 0;
+    e = hipDeviceGetAttribute(&c, hipDeviceAttributeMultiprocessorCount, dev);
+    if (e != hipSuccess) return e;
+    n_cu[dev] = c > 0 ? c : 1;
+  }
+  const int n_tiles = (int)((T + kGateBM - 1) / kGateBM);
+  const dim3 grid((unsigned)min(n_tiles, n_cu[dev]));
   const auto* h = static_cast<const uint16_t*>(hidden);
   const auto* w = static_cast<const uint16_t*>(W1);
   switch (F) {
-    case 64: hipLaunchKernelGGL(gate_bf16_kernel<1>, grid, dim3(128), 0, s, h, ld, T, D, w, b1, w2, b2, scores); break;
-    case 128: hipLaunchKernelGGL(gate_bf16_kernel<2>, grid, dim3(256), 0, s, h, ld, T, D, w, b1, w2, b2, scores); break;
-    case 256: hipLaunchKernelGGL(gate_bf16_kernel<4>, grid, dim3(512), 0, s, h, ld, T, D, w, b1, w2, b2, scores); break;
+    case 64: hipLaunchKernelGGL(gate_bf16_kernel<2>, grid, dim3(512), 0, s, h, ld, T, D, n_tiles, w, b1, w2, b2, scores); break;
+    case 128: hipLaunchKernelGGL(gate_bf16_kernel<4>, grid, dim3(512), 0, s, h, ld, T, D, n_tiles, w, b1, w2, b2, scores); break;
+    case 256: hipLaunchKernelGGL(gate_bf16_kernel<8>, grid, dim3(512), 0, s, h, ld, T, D, n_tiles, w, b1, w2, b2, scores); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();

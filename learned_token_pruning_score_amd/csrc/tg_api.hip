@@ -87,7 +87,7 @@ int tg_gate_score(const void* hidden, int64_t ld_hidden, int64_t T, int D, const
   if (dtype == TG_BF16) {
     if (D % 64 != 0 || !(F == 64 || F == 128 || F == 256)) return TG_ERR_UNSUPPORTED;
     // a 256-row tile of hidden is addressed with 32-bit byte offsets
-    if (ld_hidden > (1 << 22) || (int64_t)F * D > (1 << 29)) return TG_ERR_UNSUPPORTED;
+    if (ld_hidden >= (1 << 22) || (int64_t)F * D > (1 << 29)) return TG_ERR_UNSUPPORTED;
     if (!aligned16(hidden) || !aligned16(W1) || (ld_hidden * 2) % 16 != 0) return TG_ERR_ALIGN;
     return from_hip(tg::launch_gate_bf16(hidden, ld_hidden, T, D, W1, b1, w2, b2, F, scores,
                                          as_stream(stream)));

@@ -254,7 +254,10 @@ def test_select_distinct_random_scores_large():
 @pytest.mark.parametrize("T,D,F,ld_pad,dtype", [
     (1000, 2048, 256, 0, torch.bfloat16), (257, 1024, 128, 64, torch.bfloat16),
     (1, 128, 64, 0, torch.bfloat16), (300, 192, 256, 0, torch.bfloat16),
-    (130, 320, 128, 16, torch.bfloat16), (513, 256, 64, 8, torch.float32),
+    (130, 320, 128, 16, torch.bfloat16),
+    # more tiles than CUs: workgroups loop over tiles, loads run across tile ends
+    (70001, 320, 256, 8, torch.bfloat16), (66000, 128, 64, 0, torch.bfloat16),
+    (513, 256, 64, 8, torch.float32),
     (77, 100, 30, 3, torch.float32)])
 def test_gate_shapes(T, D, F, ld_pad, dtype):
     rng = np.random.default_rng(T)
