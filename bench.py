@@ -46,6 +46,8 @@ def parse():
                         "(a kernel of known traffic for calibrating memory counters)")
     p.add_argument("--graph", action="store_true",
                    help="also time the step captured in a HIP graph (reported as graph_ms_per_step)")
+    p.add_argument("--no-reference-points", action="store_true",
+                   help="skip the reference timings taken after the timed region")
     return p.parse_args()
 
 
@@ -87,6 +89,100 @@ def measured_traffic(kernel, source):
         if fields.get("source_sha256") == sha:
             return float(fields["traffic_bytes_per_launch"])
     return None
+
+
+def time_launches(fn, stream, reps=5, n=5, before=None):
+    """Median over `reps` of the mean time of `n` back-to-back calls of fn,
+    from HIP events on `stream`; `before` runs untimed ahead of each rep."""
+    import torch
+    ts = []
+    for _ in range(reps):
+        if before is not None:
+            before()
+        a = torch.cuda.Event(enable_timing=True)
+        b = torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        for _ in range(n):
+            fn()
+        b.record(stream)
+        torch.cuda.synchronize()
+        ts.append(a.elapsed_time(b) / n)
+    return float(np.median(ts))
+
+
+def reference_points(tg, w, gp, layers, outs, hidden, W1, b1, w2, stream, dev):
+    """Reference timings outside the timed region (each a median of event-timed
+    repetitions on the launch stream):
+      * the key-bias cost: the same attention launch with the bias and the
+        temperature switched off (gain = NULL, tau = 1), as a ratio;
+      * the dense comparator: full-length causal GQA attention (no pruning, no
+        bias) at 32768 tokens with the same head shapes;
+      * gate and attention launches after a 1 GiB write that evicts L2 and
+        the last-level cache (the timed step runs them back to back);
+      * what the chip reaches here on plain library work: a bf16 GEMM of
+        8192^3 and a 1 GiB device copy."""
+    import torch
+    s = w.spec
+    q, k, v, gain = layers[0]
+    out = outs[0]
+    gated = lambda: tg.tg_gated_attn_fwd(q, k, v, gp.bias_s, gain, s.tau, gp.cu_kept,  # noqa: E731
+                                         gp.max_kept_len, out=out)
+    plain = lambda: tg.tg_gated_attn_fwd(q, k, v, None, None, 1.0, gp.cu_kept,  # noqa: E731
+                                         gp.max_kept_len, out=out)
+    for _ in range(3):
+        gated()
+        plain()
+    # alternate the two so that both see the same clock and temperature
+    tp, tgt = [], []
+    for _ in range(7):
+        tp.append(time_launches(plain, stream, reps=1, n=5))
+        tgt.append(time_launches(gated, stream, reps=1, n=5))
+    t_plain, t_gated = float(np.median(tp)), float(np.median(tgt))
+    work = algorithmic_work(w, gp.Kt, gp.cu_kept_h)
+    r = {"attn_gated_us": t_gated * 1e3, "attn_no_bias_us": t_plain * 1e3,
+         "key_bias_cost_ratio": t_gated / t_plain}
+
+    flush_buf = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+    flush = lambda: flush_buf.fill_(1)  # noqa: E731
+    gate = lambda: tg.tg_gate_score(hidden, W1, b1, w2, w.b2, scores=gp.scores)  # noqa: E731
+    r["gate_us_after_cache_flush"] = time_launches(gate, stream, reps=7, n=1, before=flush) * 1e3
+    r["attn_us_after_cache_flush"] = time_launches(gated, stream, reps=7, n=1, before=flush) * 1e3
+    del flush_buf
+
+    if s.dtype == "bf16":
+        N = 32768
+        g = torch.Generator(device="cpu").manual_seed(1)
+        dq = torch.randn((N, s.Hq, s.d), generator=g).to(torch.bfloat16).to(dev)
+        dk = torch.randn((N, s.Hkv, s.d), generator=g).to(torch.bfloat16).to(dev)
+        dv = torch.randn((N, s.Hkv, s.d), generator=g).to(torch.bfloat16).to(dev)
+        do = torch.empty_like(dq)
+        cu = torch.tensor([0, N], dtype=torch.int32, device=dev)
+        dense = lambda: tg.tg_gated_attn_fwd(dq, dk, dv, None, None, 1.0, cu, N, out=do)  # noqa: E731
+        dense()
+        t = time_launches(dense, stream, reps=3, n=3)
+        flop = 2.0 * s.d * s.Hq * N * (N + 1)
+        r["dense_causal_32k_us"] = t * 1e3
+        r["dense_causal_32k_TFLOPs"] = flop / (t / 1e3) / 1e12
+        del dq, dk, dv, do
+
+        M = 8192
+        A = torch.randn((M, M), device=dev, dtype=torch.bfloat16)
+        B = torch.randn((M, M), device=dev, dtype=torch.bfloat16)
+        C = torch.empty((M, M), device=dev, dtype=torch.bfloat16)
+        mm = lambda: torch.matmul(A, B, out=C)  # noqa: E731
+        mm()
+        t = time_launches(mm, stream, reps=3, n=5)
+        r["library_bf16_gemm_8192_TFLOPs"] = 2.0 * M ** 3 / (t / 1e3) / 1e12
+        del A, B, C
+    src = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+    dst = torch.empty_like(src)
+    cp = lambda: dst.copy_(src)  # noqa: E731
+    cp()
+    t = time_launches(cp, stream, reps=3, n=5)
+    r["library_copy_1GiB_GBps"] = 2.0 * src.numel() / (t / 1e3) / 1e9
+    del src, dst
+    torch.cuda.synchronize()
+    return r
 
 
 def cpu_baseline(w, q_layers, cu_kept, Kt):
@@ -278,6 +374,11 @@ def main():
                 "avg_launch_us": attn_avg * 1e3}
         log(f"[bench] phases: {json.dumps(phases)}")
 
+    refs = None
+    if not args.no_reference_points:
+        refs = reference_points(tg, w, gp, layers, outs, hidden, W1, b1, w2, stream, dev)
+        log(f"[bench] reference points: {json.dumps(refs)}")
+
     cpu = None
     if not args.no_cpu_baseline:
         log("[bench] timing the CPU oracle on a bounded sample ...")
@@ -304,6 +405,7 @@ def main():
         "cpu_baseline": cpu,
         "phases": phases,
         "graph_ms_per_step": graph_ms,
+        "reference_points": refs,
     }
     print(json.dumps(line), flush=True)
 

@@ -7,21 +7,28 @@
 // keys whose unsigned order is that score order (-0.0 folded onto +0.0, every
 // NaN onto key 0, below -inf).  Per prompt, an MSB-first radix select over
 // three digits (11, 11, 10 bits) finds theta, the key of the k-th best
-// document token, and how many tokens of key theta must be kept; a tie pass
-// turns that count into an index bound only when some equal keys must be
-// dropped.  A token is kept when it lies outside the document, or its key is
-// above theta, or its key equals theta and its index is at most the bound.
+// document token, and how many tokens of key theta must be kept.  A token is
+// kept when it lies outside the document, or its key is above theta, or its
+// key equals theta and fewer than that many equal keys precede it.
 //
-// Kernels (all on the caller's stream, no host sync):
-//   sel_init   per prompt: state from (doc span, budget); clears histogram
-//   sel_hist   per (chunk, prompt): LDS histogram of the current digit over
-//              keys matching the chosen prefix, flushed with integer atomics
-//   sel_pick   per prompt: suffix scan of the histogram picks the digit;
-//              after the last digit, the index bound among keys equal to
-//              theta when not all of them are kept
-//   sel_mark   per token: keep flag
-// Integer atomics only: the histogram, and so every result, is independent
-// of execution order.
+// Each prompt is cut into chunks of C tokens from its first token.  Four
+// kernels, all on the caller's stream, no host sync, no atomics to global
+// memory and no buffer that must start cleared:
+//   sel_pass<0>  per (chunk, prompt): LDS histogram of digit 0 over the
+//                chunk's document keys, written whole to the chunk's slot
+//   sel_pass<1>, sel_pass<2>: every workgroup first sums the previous pass's
+//                chunk histograms of its prompt and picks that digit (the same
+//                result in every workgroup; the first one over the document
+//                stores it for the next pass), then histograms the next digit
+//                over the keys that match the digits picked so far
+//   sel_mark     per (chunk, prompt): picks the last digit the same way, so
+//                theta is exact; the last pass's chunk histograms also count
+//                the keys equal to theta in each chunk, which ranks the equal
+//                keys of a chunk among those of the whole document; writes
+//                every keep flag of the chunk, question and template tokens
+//                included
+// Every count is an integer sum in a fixed order: the results do not depend
+// on execution order.
 #include <limits.h>
 
 #include "tg_common.h"
@@ -30,20 +37,16 @@ namespace tg {
 namespace {
 
 constexpr int kBins = 2048;
-constexpr int kHistChunk = 4096;  // keys per sel_hist workgroup
-constexpr int kHistThreads = 256;
+constexpr int kThreads = 1024;
+constexpr int kMinChunk = 16384;  // tokens per workgroup
+constexpr int kMaxChunks = 64;    // chunks per prompt at most (chunk size grows past that)
+constexpr int kPer = kMinChunk / kThreads;  // keys per thread and round
 
+// State of a prompt after the digits of passes < p are picked.
 struct SelState {
-  int lo, hi;          // global doc span [lo, hi)
-  int k_rem;           // keys still to place at/below the current prefix
-  int active;          // 1 while the radix passes must run
-  int mode;            // 0: keep no document token, 1: keep all, 2: radix
-  unsigned prefix;     // chosen high bits of theta
-  unsigned mask;       // which bits of prefix are fixed
-  unsigned theta;      // final threshold key
-  int idx_bound;       // keep key == theta iff index <= idx_bound
-  int n_eq;            // number of keys equal to theta
-  int pad[6];
+  unsigned prefix;  // picked high bits of theta
+  int k_rem;        // keys still to place at/below the prefix
+  int pad[14];
 };
 static_assert(sizeof(SelState) == 64, "state size");
 
@@ -55,103 +58,90 @@ __device__ __forceinline__ unsigned score_key(float f) {
 }
 
 // Digit p: bits [shift, shift + width).
-__device__ __forceinline__ int digit_shift(int p) { return p == 0 ? 21 : (p == 1 ? 10 : 0); }
-__device__ __forceinline__ unsigned digit_mask(int p) { return p == 2 ? 0x3ffu : 0x7ffu; }
-
-__global__ __launch_bounds__(256) void sel_init(SelState* st, unsigned* hist,
-                                                const int32_t* cu, const int32_t* db,
-                                                const int32_t* de, const int32_t* budget) {
-  const int b = blockIdx.x;
-  unsigned* h = hist + (size_t)b * kBins;
-  for (int i = threadIdx.x; i < kBins; i += blockDim.x) h[i] = 0u;
-  if (threadIdx.x == 0) {
-    SelState s;
-    s.lo = cu[b] + db[b];
-    s.hi = cu[b] + de[b];
-    const int n = s.hi - s.lo;
-    const int k = min(budget[b], n);
-    s.k_rem = k;
-    s.prefix = 0u;
-    s.mask = 0u;
-    s.n_eq = 0;
-    if (k <= 0) {            // keep no document token
-      s.active = 0;
-      s.mode = 0;
-      s.theta = 0xffffffffu;  // above every key
-      s.idx_bound = -1;
-    } else if (k >= n) {     // keep the whole document
-      s.active = 0;
-      s.mode = 1;
-      s.theta = 0u;
-      s.idx_bound = INT_MAX;
-    } else {
-      s.active = 1;
-      s.mode = 2;
-      s.theta = 0u;
-      s.idx_bound = INT_MAX;
-    }
-    for (int i = 0; i < 6; ++i) s.pad[i] = 0;
-    st[b] = s;
-  }
+__host__ __device__ constexpr int digit_shift(int p) { return p == 0 ? 21 : (p == 1 ? 10 : 0); }
+__host__ __device__ constexpr unsigned digit_mask(int p) { return p == 2 ? 0x3ffu : 0x7ffu; }
+// Bits fixed once the digits of passes < p are picked.
+__host__ __device__ constexpr unsigned fixed_mask(int p) {
+  return p == 0 ? 0u : (p == 1 ? 0xffe00000u : 0xfffffc00u);
 }
 
-__global__ __launch_bounds__(kHistThreads) void sel_hist(const float* __restrict__ scores,
-                                                         const SelState* st, unsigned* hist,
-                                                         int pass) {
+// Per-workgroup view of its prompt and chunk.
+struct Chunk {
+  int pb, pe;    // prompt [pb, pe)
+  int lo, hi;    // document [lo, hi)
+  int k;         // document tokens to keep
+  int mode;      // 0: keep no document token, 1: keep all, 2: radix select
+  int c0, c1;    // this chunk [c0, c1)
+  int x_first, x_last;  // chunks holding document tokens
+  int slot0;     // slot of this prompt's chunk 0
+};
+
+// Sum over thread-held values of the workgroup (fixed order: wave sums,
+// then the 16 wave totals in order).
+__device__ int block_sum(int v, int* red) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off);
+  __syncthreads();
+  if (lane == 0) red[wave] = v;
+  __syncthreads();
+  int s = 0;
+#pragma unroll
+  for (int w = 0; w < kThreads / 64; ++w) s += red[w];
+  return s;
+}
+
+// Returns false when the chunk lies past the prompt (workgroup has nothing
+// to do).  Uniform across the workgroup.
+__device__ bool chunk_of(Chunk& c, const int32_t* cu, const int32_t* db, const int32_t* de,
+                         const int32_t* budget, int C, int* red) {
   const int b = blockIdx.y;
-  const SelState s = st[b];
-  if (!s.active) return;
-  const int64_t c0 = (int64_t)s.lo + (int64_t)blockIdx.x * kHistChunk;
-  if (c0 >= s.hi) return;
-  const int64_t c1 = min((int64_t)s.hi, c0 + kHistChunk);
-
-  __shared__ unsigned lh[kBins];
-  for (int i = threadIdx.x; i < kBins; i += kHistThreads) lh[i] = 0u;
-  __syncthreads();
-  const int sh = digit_shift(pass);
-  const unsigned dm = digit_mask(pass);
-  for (int64_t t = c0 + threadIdx.x; t < c1; t += kHistThreads) {
-    const unsigned key = score_key(scores[t]);
-    if ((key & s.mask) == s.prefix) atomicAdd(&lh[(key >> sh) & dm], 1u);
+  c.pb = cu[b];
+  c.pe = cu[b + 1];
+  const int64_t c0 = (int64_t)c.pb + (int64_t)blockIdx.x * C;
+  if (c0 >= c.pe) return false;
+  c.c0 = (int)c0;
+  c.c1 = (int)min((int64_t)c.pe, c0 + C);
+  c.lo = c.pb + db[b];
+  c.hi = c.pb + de[b];
+  const int n = c.hi - c.lo;
+  c.k = min(budget[b], n);
+  c.mode = c.k <= 0 ? 0 : (c.k >= n ? 1 : 2);
+  c.x_first = (c.lo - c.pb) / C;
+  c.x_last = n > 0 ? (c.hi - 1 - c.pb) / C : c.x_first - 1;
+  // slots of earlier prompts: one per chunk of each
+  int s = 0;
+  for (int bb = threadIdx.x; bb < b; bb += kThreads) {
+    const int len = cu[bb + 1] - cu[bb];
+    s += (len + C - 1) / C;
   }
-  __syncthreads();
-  unsigned* gh = hist + (size_t)b * kBins;
-  for (int i = threadIdx.x; i < kBins; i += kHistThreads) {
-    const unsigned c = lh[i];
-    if (c) atomicAdd(&gh[i], c);
-  }
+  c.slot0 = block_sum(s, red);
+  return true;
 }
 
-// One workgroup of 1024 threads per prompt; thread i owns bins 2i, 2i + 1.
-// The digit is the bin where the count of keys in higher bins first reaches
-// k_rem; the counts above each thread come from an exclusive scan run from
-// the top bin down (wave shuffles, then the 16 wave totals).  The histogram
-// is cleared for the next pass.  After the last digit, theta is exact; if
-// fewer than all keys equal to theta are kept, the same workgroup walks the
-// document in index order to find the index bound (1024 tokens per round,
-// stopping at the round that holds the k_rem-th equal key).
-__global__ __launch_bounds__(1024) void sel_pick(const float* __restrict__ scores, SelState* st,
-                                                 unsigned* hist, int pass) {
-  const int b = blockIdx.x;
+// The digit of pass p from the chunk histograms of that pass: the bin where
+// the count of keys in higher bins first reaches k_rem.  Thread j (counted
+// from the top) owns bins 2047 - 2j and 2046 - 2j.  Returns the state after
+// the pick; *n_bin is the count of the picked bin.
+__device__ SelState pick_digit(int p, const SelState in, const unsigned* part, const Chunk& c,
+                               unsigned* n_bin, unsigned* wtot, unsigned* s_res) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  __shared__ SelState s;
-  __shared__ unsigned wtot[16];
-  __shared__ int s_digit;
-  __shared__ unsigned s_above, s_bin;
-  if (tid == 0) {
-    s = st[b];
-    s_digit = 0;
-    s_above = 0u;
-    s_bin = 0u;
-  }
-  __syncthreads();
-  if (!s.active) return;
-  unsigned* h = hist + (size_t)b * kBins;
-  // thread j (counted from the top) owns bins hi = 2047 - 2j and hi - 1
   const int hi_bin = kBins - 1 - 2 * tid;
-  const unsigned c_hi = h[hi_bin], c_lo = h[hi_bin - 1];
-  h[hi_bin] = 0u;
-  h[hi_bin - 1] = 0u;
+  unsigned c_hi = 0u, c_lo = 0u;
+  // both bins in one 8-byte load; eight chunks' loads in flight at once
+  for (int x0 = c.x_first; x0 <= c.x_last; x0 += 8) {
+    uint2 v[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+      v[j] = x0 + j <= c.x_last
+                 ? *reinterpret_cast<const uint2*>(part + (size_t)(c.slot0 + x0 + j) * kBins + hi_bin - 1)
+                 : make_uint2(0u, 0u);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      c_lo += v[j].x;
+      c_hi += v[j].y;
+    }
+  }
   const unsigned mine = c_hi + c_lo;
   unsigned incl = mine;  // inclusive scan over threads, top bins first
 #pragma unroll
@@ -159,91 +149,186 @@ __global__ __launch_bounds__(1024) void sel_pick(const float* __restrict__ score
     const unsigned y = __shfl_up(incl, off);
     if (lane >= off) incl += y;
   }
+  __syncthreads();
   if (lane == 63) wtot[wave] = incl;
   __syncthreads();
   unsigned above = incl - mine;
   for (int w = 0; w < wave; ++w) above += wtot[w];
-  const unsigned k_rem = (unsigned)s.k_rem;
+  const unsigned k_rem = (unsigned)in.k_rem;
   if (above < k_rem && k_rem <= above + mine) {
+    // exactly one thread: the counts above its bins are < k_rem <= those
+    // including them
     if (above + c_hi >= k_rem) {
-      s_digit = hi_bin;
-      s_above = above;
-      s_bin = c_hi;
+      s_res[0] = (unsigned)hi_bin;
+      s_res[1] = above;
+      s_res[2] = c_hi;
     } else {
-      s_digit = hi_bin - 1;
-      s_above = above + c_hi;
-      s_bin = c_lo;
+      s_res[0] = (unsigned)(hi_bin - 1);
+      s_res[1] = above + c_hi;
+      s_res[2] = c_lo;
     }
   }
   __syncthreads();
-  if (tid == 0) {
-    const int sh = digit_shift(pass);
-    s.prefix |= (unsigned)s_digit << sh;
-    s.mask |= digit_mask(pass) << sh;
-    s.k_rem -= (int)s_above;
-    if (pass == 2) {  // every bit fixed: theta found
-      s.theta = s.prefix;
-      s.active = 0;
-      s.n_eq = (int)s_bin;  // keys equal to theta
+  SelState out = in;
+  out.prefix = in.prefix | (s_res[0] << digit_shift(p));
+  out.k_rem = in.k_rem - (int)s_res[1];
+  *n_bin = s_res[2];
+  return out;
+}
+
+// Pass P: pick digit P - 1 (P > 0), then histogram digit P over this chunk's
+// document keys that match the digits picked so far.  Chunk histograms of
+// pass P go to part[P & 1]; the state after pick P - 1 goes to st[P - 1].
+template <int P>
+__global__ __launch_bounds__(kThreads) void sel_pass(const float* __restrict__ scores,
+                                                     const int32_t* cu, const int32_t* db,
+                                                     const int32_t* de, const int32_t* budget,
+                                                     int B, int C, SelState* st,
+                                                     unsigned* part0, unsigned* part1) {
+  __shared__ unsigned lh[kBins];
+  __shared__ int red[kThreads / 64];
+  __shared__ unsigned wtot[kThreads / 64];
+  __shared__ unsigned s_res[3];
+  Chunk c;
+  if (!chunk_of(c, cu, db, de, budget, C, red)) return;
+  if (c.mode != 2) return;
+  const int b = blockIdx.y;
+  const int x = blockIdx.x;
+  SelState s;
+  if (P == 0) {
+    s.prefix = 0u;
+    s.k_rem = c.k;
+  } else {
+    const SelState in = P == 1 ? SelState{0u, c.k, {0}} : st[(size_t)(P - 2) * B + b];
+    unsigned n_bin;
+    s = pick_digit(P - 1, in, (P - 1) & 1 ? part1 : part0, c, &n_bin, wtot, s_res);
+    if (x == c.x_first && threadIdx.x == 0) st[(size_t)(P - 1) * B + b] = s;
+  }
+  if (x < c.x_first || x > c.x_last) return;  // no document token here
+  for (int i = threadIdx.x; i < kBins; i += kThreads) lh[i] = 0u;
+  __syncthreads();
+  const int d0 = max(c.c0, c.lo), d1 = min(c.c1, c.hi);
+  constexpr unsigned fm = fixed_mask(P);
+  constexpr int sh = digit_shift(P);
+  constexpr unsigned dm = digit_mask(P);
+  // kPer keys per thread and round, all loads issued before the first use
+  for (int r0 = d0; r0 < d1; r0 += kPer * kThreads) {
+    float v[kPer];
+#pragma unroll
+    for (int j = 0; j < kPer; ++j) {
+      const int t = r0 + (int)threadIdx.x + j * kThreads;
+      v[j] = t < d1 ? scores[t] : 0.0f;
+    }
+#pragma unroll
+    for (int j = 0; j < kPer; ++j) {
+      const int t = r0 + (int)threadIdx.x + j * kThreads;
+      const unsigned key = score_key(v[j]);
+      if (t < d1 && (key & fm) == s.prefix) atomicAdd(&lh[(key >> sh) & dm], 1u);
     }
   }
   __syncthreads();
-  if (pass == 2 && s.k_rem < s.n_eq) {
-    // keep only the first k_rem keys equal to theta, by index
-    int seen = 0;
-    for (int base = s.lo; base < s.hi; base += 1024) {
-      const int t = base + tid;
-      const int eq = (t < s.hi) && (score_key(scores[t]) == s.theta);
-      const unsigned long long bal = __ballot(eq);
-      const int in_wave = __popcll(bal & ((lane == 63) ? ~0ull : ((2ull << lane) - 1)));
-      __syncthreads();
-      if (lane == 63) wtot[wave] = (unsigned)in_wave;
-      __syncthreads();
-      int before = 0, round_total = 0;
-      for (int w = 0; w < 16; ++w) {
-        if (w < wave) before += (int)wtot[w];
-        round_total += (int)wtot[w];
+  unsigned* h = (P & 1 ? part1 : part0) + (size_t)(c.slot0 + x) * kBins;
+  for (int i = threadIdx.x; i < kBins; i += kThreads) h[i] = lh[i];
+}
+
+// Keep flags of one chunk.  With the last digit picked, theta is exact and
+// k_rem is the number of keys equal to theta that are kept, the first ones
+// by index.  The equal keys before this chunk are counted from the last
+// pass's chunk histograms (bin of theta's last digit); inside the chunk they
+// are ranked in index order, 1024 tokens per step.
+__global__ __launch_bounds__(kThreads) void sel_mark(const float* __restrict__ scores,
+                                                     const int32_t* cu, const int32_t* db,
+                                                     const int32_t* de, const int32_t* budget,
+                                                     int B, int C, const SelState* st,
+                                                     const unsigned* part0,
+                                                     uint8_t* __restrict__ keep) {
+  __shared__ int red[kThreads / 64];
+  __shared__ unsigned wtot[kThreads / 64];
+  __shared__ unsigned s_res[3];
+  Chunk c;
+  if (!chunk_of(c, cu, db, de, budget, C, red)) return;
+  const int b = blockIdx.y;
+  const int x = blockIdx.x;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  unsigned theta = 0u;
+  int eq_keep = 0;   // equal keys kept (over the whole document)
+  int eq_before = 0; // equal keys in the document's earlier chunks
+  bool all_eq = true;
+  if (c.mode == 2) {
+    unsigned n_eq;
+    const SelState s = pick_digit(2, st[(size_t)B + b], part0, c, &n_eq, wtot, s_res);
+    theta = s.prefix;
+    eq_keep = s.k_rem;
+    all_eq = (unsigned)eq_keep >= n_eq;
+    if (!all_eq) {
+      const unsigned bin = theta & digit_mask(2);
+      int e = 0;  // at most kMaxChunks terms: one load per thread
+      for (int xx = c.x_first + tid; xx < x; xx += kThreads)
+        e += (int)part0[(size_t)(c.slot0 + xx) * kBins + bin];
+      eq_before = block_sum(e, red);
+    }
+  }
+  // kPer tokens per thread and round (token r0 + tid + j * kThreads), the
+  // score loads all issued before the first use; index order within a round
+  // is (j, tid)
+  for (int r0 = c.c0; r0 < c.c1; r0 += kPer * kThreads) {
+    float v[kPer];
+    if (c.mode == 2) {
+#pragma unroll
+      for (int j = 0; j < kPer; ++j) {
+        const int t = r0 + tid + j * kThreads;
+        v[j] = (t < c.c1 && t >= c.lo && t < c.hi) ? scores[t] : 0.0f;
       }
-      if (eq && seen + before + in_wave == s.k_rem) s.idx_bound = t;
-      seen += round_total;
-      if (seen >= s.k_rem) break;
+    }
+#pragma unroll
+    for (int j = 0; j < kPer; ++j) {
+      const int t = r0 + tid + j * kThreads;
+      const bool in = t < c.c1;
+      const bool doc = in && t >= c.lo && t < c.hi;
+      uint8_t k = 1;
+      bool eq = false;
+      if (doc) {
+        if (c.mode == 0) {
+          k = 0;
+        } else if (c.mode == 2) {
+          const unsigned key = score_key(v[j]);
+          k = key > theta ? 1 : 0;
+          eq = key == theta;
+          if (eq && all_eq) k = 1;
+        }
+      }
+      if (!all_eq) {  // uniform: rank the equal keys of this step
+        const unsigned long long bal = __ballot(eq);
+        const int in_wave = __popcll(bal & ((lane == 63) ? ~0ull : ((2ull << lane) - 1)));
+        __syncthreads();
+        if (lane == 63) wtot[wave] = (unsigned)in_wave;
+        __syncthreads();
+        int before = 0, round_total = 0;
+        for (int w = 0; w < kThreads / 64; ++w) {
+          if (w < wave) before += (int)wtot[w];
+          round_total += (int)wtot[w];
+        }
+        if (eq) k = (eq_before + before + in_wave <= eq_keep) ? 1 : 0;
+        eq_before += round_total;
+      }
+      if (in) keep[t] = k;
     }
   }
-  __syncthreads();
-  if (tid == 0) st[b] = s;
 }
 
-__device__ __forceinline__ int find_prompt(const int32_t* cu, int B, int64_t t) {
-  int lo = 0, hi = B - 1;  // largest b with cu[b] <= t
-  while (lo < hi) {
-    const int mid = (lo + hi + 1) >> 1;
-    if ((int64_t)cu[mid] <= t) lo = mid; else hi = mid - 1;
-  }
-  return lo;
+int chunk_size(int64_t T) {
+  int64_t C = kMinChunk;
+  while ((T + C - 1) / C > kMaxChunks) C *= 2;
+  return (int)C;
 }
 
-__global__ __launch_bounds__(256) void sel_mark(const float* __restrict__ scores,
-                                                const SelState* __restrict__ st,
-                                                const int32_t* __restrict__ cu, int B, int64_t T,
-                                                uint8_t* __restrict__ keep) {
-  const int64_t t = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  if (t >= T) return;
-  const int b = find_prompt(cu, B, t);
-  const SelState& s = st[b];
-  uint8_t k = 1;
-  if (t >= s.lo && t < s.hi) {
-    const unsigned key = score_key(scores[t]);
-    k = (key > s.theta || (key == s.theta && t <= (int64_t)s.idx_bound)) ? 1 : 0;
-    if (s.theta == 0xffffffffu) k = 0;
-  }
-  keep[t] = k;
-}
+size_t n_slots(int B, int64_t T) { return (size_t)((T + chunk_size(T) - 1) / chunk_size(T)) + (size_t)B; }
 
 }  // namespace
 
-size_t select_workspace_bytes(int B, int64_t /*T*/) {
-  const size_t st = ((size_t)B * sizeof(SelState) + 255) & ~(size_t)255;
-  return st + (size_t)B * kBins * sizeof(unsigned);
+size_t select_workspace_bytes(int B, int64_t T) {
+  const size_t st = ((size_t)2 * B * sizeof(SelState) + 255) & ~(size_t)255;
+  return st + 2 * n_slots(B, T) * kBins * sizeof(unsigned);
 }
 
 hipError_t launch_select(const float* scores, const int32_t* cu, const int32_t* db,
@@ -251,16 +336,19 @@ hipError_t launch_select(const float* scores, const int32_t* cu, const int32_t* 
                          uint8_t* keep, void* ws, hipStream_t s) {
   if (B == 0 || T == 0) return hipSuccess;
   auto* st = static_cast<SelState*>(ws);
-  const size_t st_bytes = ((size_t)B * sizeof(SelState) + 255) & ~(size_t)255;
-  auto* hist = reinterpret_cast<unsigned*>(static_cast<char*>(ws) + st_bytes);
-  hipLaunchKernelGGL(sel_init, dim3(B), dim3(256), 0, s, st, hist, cu, db, de, budget);
-  const dim3 hgrid((unsigned)((T + kHistChunk - 1) / kHistChunk), (unsigned)B);
-  for (int p = 0; p < 3; ++p) {
-    hipLaunchKernelGGL(sel_hist, hgrid, dim3(kHistThreads), 0, s, scores, st, hist, p);
-    hipLaunchKernelGGL(sel_pick, dim3(B), dim3(1024), 0, s, scores, st, hist, p);
-  }
-  hipLaunchKernelGGL(sel_mark, dim3((unsigned)((T + 255) / 256)), dim3(256), 0, s, scores, st,
-                     cu, B, T, keep);
+  const size_t st_bytes = ((size_t)2 * B * sizeof(SelState) + 255) & ~(size_t)255;
+  auto* part0 = reinterpret_cast<unsigned*>(static_cast<char*>(ws) + st_bytes);
+  auto* part1 = part0 + n_slots(B, T) * kBins;
+  const int C = chunk_size(T);
+  const dim3 grid((unsigned)((T + C - 1) / C), (unsigned)B);
+  hipLaunchKernelGGL(sel_pass<0>, grid, dim3(kThreads), 0, s, scores, cu, db, de, budget, B, C, st,
+                     part0, part1);
+  hipLaunchKernelGGL(sel_pass<1>, grid, dim3(kThreads), 0, s, scores, cu, db, de, budget, B, C, st,
+                     part0, part1);
+  hipLaunchKernelGGL(sel_pass<2>, grid, dim3(kThreads), 0, s, scores, cu, db, de, budget, B, C, st,
+                     part0, part1);
+  hipLaunchKernelGGL(sel_mark, grid, dim3(kThreads), 0, s, scores, cu, db, de, budget, B, C, st,
+                     part0, keep);
   return hipGetLastError();
 }
 

@@ -300,6 +300,39 @@ def test_compact_explicit_positions_and_copy_modes(dtype, D):
     assert np.array_equal(ik.cpu().numpy(), ir)
 
 
+@pytest.mark.parametrize("lens,unaligned_keep", [
+    ([600000, 3, 500000], False),   # more than 2^20 tokens
+    ([5000, 7, 20000], True),       # keep flags not 16-byte aligned
+    ([4095, 1, 70000, 4097], False)])  # chunks straddling prompts
+def test_compact_sizes_and_alignment(lens, unaligned_keep):
+    rng = np.random.default_rng(len(lens) + sum(lens))
+    lens = np.array(lens)
+    cu = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
+    db = np.minimum(lens, 2); de = np.maximum(db, lens - 1); bud = lens // 7
+    T, D = int(cu[-1]), 16
+    h = torch.from_numpy(rng.standard_normal((T, D)).astype(np.float32)).to(torch.bfloat16)
+    s = rng.standard_normal(T).astype(np.float32)
+    keep = oracle.select_topk(s, cu, db, de, bud)
+    cu_kept, _ = oracle.plan(cu, db, de, bud)
+    Kt = int(cu_kept[-1])
+    d = lambda a: torch.from_numpy(np.ascontiguousarray(a, np.int32)).to(DEV)  # noqa: E731
+    kd = torch.from_numpy(keep).to(DEV)
+    if unaligned_keep:
+        buf = torch.zeros(T + 1, dtype=torch.uint8, device=DEV)
+        buf[1:] = kd
+        kd = buf[1:]
+        assert kd.data_ptr() % 16 != 0
+    hk, pk, bk, ik = tg.tg_compact(h.to(DEV), None, torch.from_numpy(s).to(DEV), kd, d(cu), d(db),
+                                   d(de), Kt)
+    torch.cuda.synchronize()
+    pos = np.concatenate([np.arange(n) for n in lens]).astype(np.int32)
+    hr, pr, br, ir = oracle.compact(h.view(torch.int16).numpy(), pos, s, keep, cu, db, de)
+    assert np.array_equal(hk.cpu().view(torch.int16).numpy(), hr)
+    assert np.array_equal(pk.cpu().numpy(), pr)
+    assert np.array_equal(bk.cpu().numpy().view(np.uint32), br.view(np.uint32))
+    assert np.array_equal(ik.cpu().numpy(), ir)
+
+
 def _attn_inputs(rng, lens, Hq, Hkv, d, dtype):
     Kt = int(sum(lens))
     mk = lambda *shape: torch.from_numpy(rng.standard_normal(shape).astype(np.float32)).to(dtype)  # noqa: E731
