@@ -4,12 +4,14 @@
 //     s_t = b2 + sum_f w2[f] * SiLU(b1[f] + W1[f, :] . hidden[t, :])
 //
 // bf16 path: the product is computed transposed, C^T[f][t] = W1[f] . h[t],
-// with the 32x32x16 bf16 MFMA.  A workgroup of 8 waves owns tiles of 256
-// tokens, each wave 32 tokens and all F rows, so that every lane of the
-// accumulators holds one token's column: the SiLU . w2 epilogue reduces over
-// F inside the lane and across the two wave halves, in a fixed order
-// (bit-reproducible, no atomics), and the [T, F] activation never reaches
-// memory.  hidden is read once, from HBM straight into the registers that
+// with the 32x32x16 bf16 MFMA.  A workgroup of 8 waves owns tiles of
+// 256 / FS tokens: each wave owns 32 tokens and F / FS rows of W1 (FS = 1
+// when the tokens fill every CU with 256-token tiles, 2 or 4 for shorter
+// inputs), so that every lane of the accumulators holds one token's column.
+// The SiLU . w2 epilogue reduces over F inside the lane, across the two wave
+// halves and, for FS > 1, across the FS waves of a token group through LDS,
+// in a fixed order (bit-reproducible, no atomics); the [T, F] activation
+// never reaches memory.  hidden is read once, from HBM straight into the registers that
 // serve as the MFMA's B operand, three stages of 64 columns ahead of their
 // use (the register file holds far more bytes in flight than LDS could);
 // W1, which every tile reads in full, streams through four LDS stages filled
@@ -20,7 +22,6 @@
 namespace tg {
 namespace {
 
-constexpr int kGateBM = 256;   // tokens per tile: 8 waves x 32
 constexpr int kGateBK = 64;    // reduction columns per stage (128-byte row segments)
 constexpr int kGateAhead = 3;  // stages loaded ahead of the one computed
 constexpr int kBufFlags = 0x00020000;  // raw buffer: reads past num_records give 0
@@ -41,13 +42,16 @@ __device__ __forceinline__ void lds_load16(__amdgpu_buffer_rsrc_t r, char* lds, 
 // hidden that is the j-th 16 bytes of the 64 contiguous bytes it loads, and
 // the W1 fragments follow the same column map, so the products sum over the
 // same columns as the definition, in another order.
-template <int NFB>  // F = 32 * NFB
+template <int NFB, int FS>  // F = 32 * NFB, split over FS waves per token group
 __global__ __launch_bounds__(512, 1) void gate_bf16_kernel(
     const uint16_t* __restrict__ hidden, int64_t ld, int64_t T, int D, int n_tiles,
     const uint16_t* __restrict__ W1, const float* __restrict__ b1,
     const float* __restrict__ w2, float b2, float* __restrict__ scores) {
   constexpr int F = 32 * NFB;
   constexpr int NW = 8;
+  constexpr int BM = 32 * NW / FS;    // tokens per tile
+  constexpr int NFW = NFB / FS;       // F blocks per wave
+  static_assert(NFB % FS == 0, "F split");
   constexpr int W_BYTES = F * kGateBK * 2;    // one stage of W1
   constexpr int W_DMA = W_BYTES / 1024 / NW;  // 1 KB buffer-to-LDS copies per wave per stage
   constexpr int PER = W_DMA + 4;              // vector-memory instructions per wave per stage
@@ -55,10 +59,13 @@ __global__ __launch_bounds__(512, 1) void gate_bf16_kernel(
 
   __shared__ __attribute__((aligned(16))) char sw0[W_BYTES], sw1[W_BYTES], sw2[W_BYTES], sw3[W_BYTES];
   __shared__ __attribute__((aligned(16))) float sb1[F], sw2v[F];
+  __shared__ float sred[FS][BM];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int tgrp = wave / FS;  // token group: tokens [32 tgrp, 32 tgrp + 32) of the tile
+  const int fpart = wave % FS; // F blocks [NFW fpart, NFW fpart + NFW)
   for (int f = tid; f < F; f += NW * 64) {
     sb1[f] = b1 ? b1[f] : 0.0f;
     sw2v[f] = w2[f];
@@ -70,8 +77,8 @@ __global__ __launch_bounds__(512, 1) void gate_bf16_kernel(
   const int my_tiles = ((int)blockIdx.x < n_tiles) ? (n_tiles - 1 - (int)blockIdx.x) / (int)gridDim.x + 1 : 0;
   const int n_steps = my_tiles * nk;
 
-  // hidden: lane loads 64 contiguous bytes of token wave * 32 + lane % 32
-  const int h_voff = ((wave * 32 + (lane & 31)) * (int)ld + (lane >> 5) * 32) * 2;
+  // hidden: lane loads 64 contiguous bytes of token tgrp * 32 + lane % 32
+  const int h_voff = ((tgrp * 32 + (lane & 31)) * (int)ld + (lane >> 5) * 32) * 2;
   // W1 copies: copy j of this wave fills rows 8 (wave * W_DMA + j) .. +7;
   // lane l writes position l % 8 of row l / 8, which holds that row's
   // logical chunk gate_swz(row, l % 8).
@@ -86,14 +93,14 @@ __global__ __launch_bounds__(512, 1) void gate_bf16_kernel(
   int a_off[4];
 #pragma unroll
   for (int ks = 0; ks < 4; ++ks)
-    a_off[ks] = (lane & 31) * (kGateBK * 2) + gate_swz(lane & 31, 4 * (lane >> 5) + ks) * 16;
+    a_off[ks] = (fpart * NFW * 32 + (lane & 31)) * (kGateBK * 2) + gate_swz(lane & 31, 4 * (lane >> 5) + ks) * 16;
 
   // Load position: tile ld_tile (a multiple of gridDim.x past blockIdx.x),
   // stage ld_k of it.  Loads past the last tile read nothing (zero range).
   int ld_tile = blockIdx.x, ld_k = 0;
   auto issue = [&](char* sw, uint4 (&h)[4]) __attribute__((always_inline)) {
-    const int64_t tt0 = (int64_t)ld_tile * kGateBM;
-    const int rows = ld_tile < n_tiles ? (int)min((int64_t)kGateBM, T - tt0) : 0;
+    const int64_t tt0 = (int64_t)ld_tile * BM;
+    const int rows = ld_tile < n_tiles ? (int)min((int64_t)BM, T - tt0) : 0;
     const int k0 = ld_k * kGateBK;
     const bool kin = k0 < D;
     const int kk = kin ? k0 : 0;
@@ -114,20 +121,20 @@ __global__ __launch_bounds__(512, 1) void gate_bf16_kernel(
     }
   };
 
-  f32x16 acc[NFB];
+  f32x16 acc[NFW];
 #pragma unroll
-  for (int fb = 0; fb < NFB; ++fb)
+  for (int fb = 0; fb < NFW; ++fb)
 #pragma unroll
     for (int i = 0; i < 16; ++i) acc[fb][i] = 0.0f;
 
-  // One stage: 4 k-steps x NFB F blocks; each W1 fragment is read three
+  // One stage: 4 k-steps x NFW F blocks; each W1 fragment is read three
   // MFMAs ahead of its use.
-  constexpr int NM = 4 * NFB;
+  constexpr int NM = 4 * NFW;
   constexpr int AHEAD = 3;
   auto compute = [&](const char* sw, const uint4 (&h)[4]) __attribute__((always_inline)) {
     bf16x8 fa[NM];
     auto frag = [&](int m) __attribute__((always_inline)) {
-      const int ks = m / NFB, fb = m % NFB;
+      const int ks = m / NFW, fb = m % NFW;
       return *reinterpret_cast<const bf16x8*>(sw + a_off[ks] + fb * 32 * (kGateBK * 2));
     };
 #pragma unroll
@@ -136,22 +143,23 @@ __global__ __launch_bounds__(512, 1) void gate_bf16_kernel(
     for (int m = 0; m < NM; ++m) {
       if (m + AHEAD < NM) fa[m + AHEAD] = frag(m + AHEAD);
       __builtin_amdgcn_sched_barrier(0);
-      const int ks = m / NFB, fb = m % NFB;
+      const int ks = m / NFW, fb = m % NFW;
       acc[fb] = mfma32x32x16(fa[m], as_bf16x8(h[ks]), acc[fb]);
       __builtin_amdgcn_sched_barrier(0);
     }
   };
 
   // Epilogue of one tile: lane holds token column lane % 32 and F rows
-  // 32 fb + acc_row(i, lane).
+  // 32 (NFW fpart + fb) + acc_row(i, lane).  With FS > 1 the partial sums of
+  // a token group's waves meet in LDS and its first wave adds them in order.
   int ep_tile = blockIdx.x;
   auto epilogue = [&]() __attribute__((always_inline)) {
     float p[4] = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
-    for (int fb = 0; fb < NFB; ++fb)
+    for (int fb = 0; fb < NFW; ++fb)
 #pragma unroll
       for (int i4 = 0; i4 < 4; ++i4) {
-        const int f = fb * 32 + 8 * i4 + 4 * (lane >> 5);
+        const int f = (fpart * NFW + fb) * 32 + 8 * i4 + 4 * (lane >> 5);
         const float4 bb = *reinterpret_cast<const float4*>(&sb1[f]);
         const float4 ww = *reinterpret_cast<const float4*>(&sw2v[f]);
         const float bv[4] = {bb.x, bb.y, bb.z, bb.w}, wv[4] = {ww.x, ww.y, ww.z, ww.w};
@@ -163,8 +171,21 @@ __global__ __launch_bounds__(512, 1) void gate_bf16_kernel(
         }
       }
     const float part = pair_sum((p[0] + p[1]) + (p[2] + p[3]));
-    const int64_t t = (int64_t)ep_tile * kGateBM + wave * 32 + lane;
-    if (lane < 32 && t < T) scores[t] = part + b2;
+    const int64_t t = (int64_t)ep_tile * BM + tgrp * 32 + lane;
+    if (FS == 1) {
+      if (lane < 32 && t < T) scores[t] = part + b2;
+    } else {
+      if (lane < 32) sred[fpart][tgrp * 32 + lane] = part;
+      // LDS-only barrier: the loads in flight stay in flight.  sred is
+      // written again only a tile later, many barriers on.
+      asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+      if (fpart == 0 && lane < 32 && t < T) {
+        float sum = 0.0f;
+#pragma unroll
+        for (int q = 0; q < FS; ++q) sum += sred[q][tgrp * 32 + lane];
+        scores[t] = sum + b2;
+      }
+    }
     ep_tile += gridDim.x;
   };
 
@@ -198,7 +219,7 @@ __global__ __launch_bounds__(512, 1) void gate_bf16_kernel(
       kc = 0;
       epilogue();
 #pragma unroll
-      for (int fb = 0; fb < NFB; ++fb)
+      for (int fb = 0; fb < NFW; ++fb)
 #pragma unroll
         for (int i = 0; i < 16; ++i) acc[fb][i] = 0.0f;
     }
@@ -250,16 +271,27 @@ hipError_t launch_gate_bf16(const void* hidden, int64_t ld, int64_t T, int D, co
     if (e != hipSuccess) return e;
     n_cu[dev] = c > 0 ? c : 1;
   }
-  const int n_tiles = (int)((T + kGateBM - 1) / kGateBM);
+  // F split: the smallest that gives every CU a tile (256 / FS tokens each)
+  const int nfb = F / 32;
+  int fs = 1;
+  while (fs < 4 && fs * 2 <= nfb && (T + 256 / fs - 1) / (256 / fs) < n_cu[dev]) fs *= 2;
+  const int bm = 256 / fs;
+  const int n_tiles = (int)((T + bm - 1) / bm);
   const dim3 grid((unsigned)min(n_tiles, n_cu[dev]));
   const auto* h = static_cast<const uint16_t*>(hidden);
   const auto* w = static_cast<const uint16_t*>(W1);
-  switch (F) {
-    case 64: hipLaunchKernelGGL(gate_bf16_kernel<2>, grid, dim3(512), 0, s, h, ld, T, D, n_tiles, w, b1, w2, b2, scores); break;
-    case 128: hipLaunchKernelGGL(gate_bf16_kernel<4>, grid, dim3(512), 0, s, h, ld, T, D, n_tiles, w, b1, w2, b2, scores); break;
-    case 256: hipLaunchKernelGGL(gate_bf16_kernel<8>, grid, dim3(512), 0, s, h, ld, T, D, n_tiles, w, b1, w2, b2, scores); break;
-    default: return hipErrorInvalidValue;
+#define TG_GATE_LAUNCH(NFB_, FS_) \
+  hipLaunchKernelGGL((gate_bf16_kernel<NFB_, FS_>), grid, dim3(512), 0, s, h, ld, T, D, n_tiles, w, b1, w2, b2, scores)
+  if (F == 64) {
+    if (fs == 1) TG_GATE_LAUNCH(2, 1); else TG_GATE_LAUNCH(2, 2);
+  } else if (F == 128) {
+    if (fs == 1) TG_GATE_LAUNCH(4, 1); else if (fs == 2) TG_GATE_LAUNCH(4, 2); else TG_GATE_LAUNCH(4, 4);
+  } else if (F == 256) {
+    if (fs == 1) TG_GATE_LAUNCH(8, 1); else if (fs == 2) TG_GATE_LAUNCH(8, 2); else TG_GATE_LAUNCH(8, 4);
+  } else {
+    return hipErrorInvalidValue;
   }
+#undef TG_GATE_LAUNCH
   return hipGetLastError();
 }
 

@@ -257,6 +257,10 @@ def test_select_distinct_random_scores_large():
     (130, 320, 128, 16, torch.bfloat16),
     # more tiles than CUs: workgroups loop over tiles, loads run across tile ends
     (70001, 320, 256, 8, torch.bfloat16), (66000, 128, 64, 0, torch.bfloat16),
+    # shorter inputs: F split over 2 or 4 waves per token group (128- and
+    # 64-token tiles), the last one with more tiles than CUs
+    (40000, 256, 256, 8, torch.bfloat16), (40000, 192, 128, 0, torch.bfloat16),
+    (20000, 128, 256, 0, torch.bfloat16), (9000, 64, 64, 0, torch.bfloat16),
     (513, 256, 64, 8, torch.float32),
     (77, 100, 30, 3, torch.float32)])
 def test_gate_shapes(T, D, F, ld_pad, dtype):
