@@ -116,7 +116,7 @@ int tg_select_topk_workspace(int B, int64_t T, size_t* bytes);
  * device, same values as given to tg_plan); keep [T] uint8 out (1 = kept).
  * workspace: device memory of at least tg_select_topk_workspace() bytes, any
  * contents on entry, clobbered.  Device arguments are trusted to satisfy the
- * rules tg_plan checks; T must equal cu_seqlens[B].
+ * rules tg_plan checks; T must equal cu_seqlens[B].  Supported: B <= 65535.
  */
 int tg_select_topk(const float* scores, const int32_t* cu_seqlens,
                    const int32_t* doc_begin, const int32_t* doc_end,
@@ -170,7 +170,8 @@ int tg_compact(const void* hidden, int64_t ld_hidden, int D, int dtype,
  * tg_plan's output), max_kept_len its longest prompt.  out [Kt, Hq, d]
  * packed, same dtype as q.  lse [Hq, Kt] fp32, or NULL.
  * Supported: d in {64, 128}, Hq % Hkv == 0, k and v token strides up to
- * 2^23 elements.  bf16 runs on MFMA with fp32
+ * 2^23 elements, B <= 65535, max_kept_len <= 65535 * 256 (bf16) and
+ * Hq <= 65535 (fp32).  bf16 runs on MFMA with fp32
  * accumulation and rounds the softmax weights to bf16 before the value
  * product; fp32 runs on vector ALUs throughout.  bf16 needs q, k, v, out and
  * the token strides aligned to 16 bytes.

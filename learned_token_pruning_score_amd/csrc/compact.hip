@@ -8,12 +8,12 @@
 //   cmp_count  per chunk of kCmpChunk tokens: number of kept flags
 //   cmp_index  per chunk: its base row is the sum of the counts before it;
 //              a block scan of the flags gives each kept token its row, and
-//              the owning thread writes the row's source index, position
-//              and bias
+//              the owning thread writes the row's source token
 //   cmp_copy   one wave per kept row: the hidden row is copied byte-exactly
 //              in 16-byte units (or element by element when rows or
-//              pointers are not 16-byte aligned); every lane issues all its
-//              loads before its stores
+//              pointers are not 16-byte aligned), every lane issuing all its
+//              loads before its stores; lane 0 writes the row's position,
+//              bias and source index
 // Integer arithmetic only; deterministic.
 #include "tg_common.h"
 
@@ -53,12 +53,8 @@ __device__ __forceinline__ int find_prompt_c(const int32_t* cu, int B, int64_t t
 }
 
 __global__ __launch_bounds__(kCmpThreads) void cmp_index(
-    const int32_t* __restrict__ pos, const float* __restrict__ scores,
-    const uint8_t* __restrict__ keep, const int32_t* __restrict__ cu,
-    const int32_t* __restrict__ db, const int32_t* __restrict__ de, int B, int64_t T,
-    const int* __restrict__ counts, int64_t Kt, int32_t* __restrict__ src_out,
-    int32_t* __restrict__ pos_out, float* __restrict__ bias_out,
-    int32_t* __restrict__ kept_idx_out) {
+    const uint8_t* __restrict__ keep, int64_t T, const int* __restrict__ counts, int64_t Kt,
+    int32_t* __restrict__ src_out) {
   __shared__ int wsum[kCmpThreads / 64];
   __shared__ int s_row0;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -100,16 +96,7 @@ __global__ __launch_bounds__(kCmpThreads) void cmp_index(
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
     if (!f[j]) continue;
-    const int64_t t = base + j;
-    if (r < Kt) {  // flags beyond the stated Kt write nothing
-      const int b = find_prompt_c(cu, B, t);
-      const int64_t rel = t - cu[b];
-      const bool in_doc = rel >= db[b] && rel < de[b];
-      src_out[r] = (int32_t)t;
-      pos_out[r] = pos ? pos[t] : (int32_t)rel;
-      bias_out[r] = in_doc ? scores[t] : 0.0f;
-      if (kept_idx_out) kept_idx_out[r] = (int32_t)t;
-    }
+    if (r < Kt) src_out[r] = (int32_t)(base + j);  // flags beyond the stated Kt write nothing
     ++r;
   }
 }
@@ -118,13 +105,28 @@ __global__ __launch_bounds__(kCmpThreads) void cmp_index(
 template <int MODE>
 __global__ __launch_bounds__(64 * kRowsPerCopyWG) void cmp_copy(
     const char* __restrict__ hidden, int64_t ld_bytes, int row_bytes,
-    const int32_t* __restrict__ src, int64_t T, int64_t Kt, char* __restrict__ hidden_out) {
+    const int32_t* __restrict__ src, int64_t T, int64_t Kt, char* __restrict__ hidden_out,
+    const int32_t* __restrict__ pos, const float* __restrict__ scores,
+    const int32_t* __restrict__ cu, const int32_t* __restrict__ db,
+    const int32_t* __restrict__ de, int B, int32_t* __restrict__ pos_out,
+    float* __restrict__ bias_out, int32_t* __restrict__ kept_idx_out) {
   const int lane = threadIdx.x & 63;
   const int64_t r = (int64_t)blockIdx.x * kRowsPerCopyWG + (threadIdx.x >> 6);
   if (r >= Kt) return;
   // clamped: with fewer kept flags than Kt (a caller error) the unwritten
   // rows copy some valid row instead of reading outside `hidden`
   const int64_t t = min(max((int64_t)src[r], (int64_t)0), T - 1);
+  // the row's position, bias and source index, written after the copy so
+  // that their loads do not hold the copy's back
+  auto meta = [&]() __attribute__((always_inline)) {
+    if (lane != 0) return;
+    const int b = find_prompt_c(cu, B, t);
+    const int64_t rel = t - cu[b];
+    const bool in_doc = rel >= db[b] && rel < de[b];
+    pos_out[r] = pos ? pos[t] : (int32_t)rel;
+    bias_out[r] = in_doc ? scores[t] : 0.0f;
+    if (kept_idx_out) kept_idx_out[r] = (int32_t)t;
+  };
   const char* s = hidden + t * ld_bytes;
   char* d = hidden_out + r * row_bytes;
   if (MODE == 1) {
@@ -147,6 +149,7 @@ __global__ __launch_bounds__(64 * kRowsPerCopyWG) void cmp_copy(
     for (int u = lane; u < (row_bytes >> 1); u += 64)
       reinterpret_cast<uint16_t*>(d)[u] = reinterpret_cast<const uint16_t*>(s)[u];
   }
+  meta();
 }
 
 }  // namespace
@@ -170,8 +173,7 @@ hipError_t launch_compact(const void* hidden, int64_t ld, int D, int elem_bytes,
   const int row_bytes = D * elem_bytes;
   const int64_t ld_bytes = ld * elem_bytes;
   hipLaunchKernelGGL(cmp_count, dim3(nchunks), dim3(kCmpThreads), 0, s, keep, T, counts);
-  hipLaunchKernelGGL(cmp_index, dim3(nchunks), dim3(kCmpThreads), 0, s, pos, scores, keep, cu, db,
-                     de, B, T, counts, Kt, src, pos_out, bias_out, kept_idx_out);
+  hipLaunchKernelGGL(cmp_index, dim3(nchunks), dim3(kCmpThreads), 0, s, keep, T, counts, Kt, src);
   if (Kt > 0) {
     const dim3 grid((unsigned)((Kt + kRowsPerCopyWG - 1) / kRowsPerCopyWG));
     const dim3 block(64 * kRowsPerCopyWG);
@@ -179,11 +181,14 @@ hipError_t launch_compact(const void* hidden, int64_t ld, int D, int elem_bytes,
     auto* o = static_cast<char*>(hidden_out);
     if ((row_bytes % 16) == 0 && (ld_bytes % 16) == 0 && ((uintptr_t)hidden % 16) == 0 &&
         ((uintptr_t)hidden_out % 16) == 0)
-      hipLaunchKernelGGL(cmp_copy<1>, grid, block, 0, s, h, ld_bytes, row_bytes, src, T, Kt, o);
+      hipLaunchKernelGGL(cmp_copy<1>, grid, block, 0, s, h, ld_bytes, row_bytes, src, T, Kt, o, pos,
+                         scores, cu, db, de, B, pos_out, bias_out, kept_idx_out);
     else if (elem_bytes == 4)
-      hipLaunchKernelGGL(cmp_copy<0>, grid, block, 0, s, h, ld_bytes, row_bytes, src, T, Kt, o);
+      hipLaunchKernelGGL(cmp_copy<0>, grid, block, 0, s, h, ld_bytes, row_bytes, src, T, Kt, o, pos,
+                         scores, cu, db, de, B, pos_out, bias_out, kept_idx_out);
     else
-      hipLaunchKernelGGL(cmp_copy<2>, grid, block, 0, s, h, ld_bytes, row_bytes, src, T, Kt, o);
+      hipLaunchKernelGGL(cmp_copy<2>, grid, block, 0, s, h, ld_bytes, row_bytes, src, T, Kt, o, pos,
+                         scores, cu, db, de, B, pos_out, bias_out, kept_idx_out);
   }
   return hipGetLastError();
 }

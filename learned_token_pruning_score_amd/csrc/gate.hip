@@ -17,6 +17,8 @@
 // W1, which every tile reads in full, streams through four LDS stages filled
 // by buffer-to-LDS loads.  One workgroup per CU loops over tiles, and the
 // loads run ahead across tile boundaries.
+#include <atomic>
+
 #include "tg_common.h"
 
 namespace tg {
@@ -259,25 +261,27 @@ hipError_t launch_gate_bf16(const void* hidden, int64_t ld, int64_t T, int D, co
                             const float* b1, const float* w2, float b2, int F, float* scores,
                             hipStream_t s) {
   if (T == 0) return hipSuccess;
-  // one workgroup per CU, each looping over tiles
-  static int n_cu[64] = {0};
+  // one workgroup per CU, each looping over tiles; the CU count of each
+  // device is queried once (concurrent first calls store the same value)
+  static std::atomic<int> cu_count[64];
   int dev = 0;
   hipError_t e = hipGetDevice(&dev);
   if (e != hipSuccess) return e;
   if (dev < 0 || dev >= 64) return hipErrorInvalidDevice;
-  if (n_cu[dev] == 0) {
-    int c = 0;
-    e = hipDeviceGetAttribute(&c, hipDeviceAttributeMultiprocessorCount, dev);
+  int n_cu = cu_count[dev].load(std::memory_order_relaxed);
+  if (n_cu == 0) {
+    e = hipDeviceGetAttribute(&n_cu, hipDeviceAttributeMultiprocessorCount, dev);
     if (e != hipSuccess) return e;
-    n_cu[dev] = c > 0 ? c : 1;
+    n_cu = n_cu > 0 ? n_cu : 1;
+    cu_count[dev].store(n_cu, std::memory_order_relaxed);
   }
   // F split: the smallest that gives every CU a tile (256 / FS tokens each)
   const int nfb = F / 32;
   int fs = 1;
-  while (fs < 4 && fs * 2 <= nfb && (T + 256 / fs - 1) / (256 / fs) < n_cu[dev]) fs *= 2;
+  while (fs < 4 && fs * 2 <= nfb && (T + 256 / fs - 1) / (256 / fs) < n_cu) fs *= 2;
   const int bm = 256 / fs;
   const int n_tiles = (int)((T + bm - 1) / bm);
-  const dim3 grid((unsigned)min(n_tiles, n_cu[dev]));
+  const dim3 grid((unsigned)min(n_tiles, n_cu));
   const auto* h = static_cast<const uint16_t*>(hidden);
   const auto* w = static_cast<const uint16_t*>(W1);
 #define TG_GATE_LAUNCH(NFB_, FS_) \

@@ -11,9 +11,12 @@
 // kept when it lies outside the document, or its key is above theta, or its
 // key equals theta and fewer than that many equal keys precede it.
 //
-// Each prompt is cut into chunks of C tokens from its first token.  Four
-// kernels, all on the caller's stream, no host sync, no atomics to global
-// memory and no buffer that must start cleared:
+// Up to 2^18 tokens, one workgroup per prompt runs the whole selection
+// (sel_single): every pass re-reads the prompt's scores from L2, so there is
+// one launch.  Longer inputs are cut into chunks of C tokens per prompt,
+// from its first token, and take four kernels, all on the caller's stream,
+// with no host sync, no atomics to global memory and no buffer that must
+// start cleared:
 //   sel_pass<0>  per (chunk, prompt): LDS histogram of digit 0 over the
 //                chunk's document keys, written whole to the chunk's slot
 //   sel_pass<1>, sel_pass<2>: every workgroup first sums the previous pass's
@@ -316,6 +319,155 @@ __global__ __launch_bounds__(kThreads) void sel_mark(const float* __restrict__ s
   }
 }
 
+// Whole selection of one prompt in one workgroup (inputs up to
+// kSingleMaxT tokens): the same three digits and the same keep rule, with
+// the histograms in LDS and the scores re-read from L2 on every pass, so
+// there is one launch and no workspace.  Each digit value has four
+// sub-bins (chosen by lane % 4), which spreads the atomics of equal digits
+// in one wave over four addresses; the pick adds them back.
+constexpr int kSub = 4;
+#ifndef TG_SEL_SINGLE_MAX
+#define TG_SEL_SINGLE_MAX (1 << 15)
+#endif
+constexpr int64_t kSingleMaxT = TG_SEL_SINGLE_MAX;
+#ifndef TG_SEL_SINGLE_PER
+#define TG_SEL_SINGLE_PER 16
+#endif
+constexpr int kSPer = TG_SEL_SINGLE_PER;  // keys per thread and round, all loads in flight
+
+__global__ __launch_bounds__(kThreads) void sel_single(const float* __restrict__ scores,
+                                                       const int32_t* cu, const int32_t* db,
+                                                       const int32_t* de, const int32_t* budget,
+                                                       uint8_t* __restrict__ keep) {
+  __shared__ unsigned lh[kBins * kSub];
+  __shared__ unsigned wtot[kThreads / 64];
+  __shared__ unsigned s_res[3];
+  const int b = blockIdx.x;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int pb = cu[b], pe = cu[b + 1];
+  const int lo = pb + db[b], hi = pb + de[b];
+  const int n = hi - lo;
+  const int k = min(budget[b], n);
+  const int mode = k <= 0 ? 0 : (k >= n ? 1 : 2);
+
+  unsigned theta = 0u;
+  int eq_keep = 0;
+  bool all_eq = true;
+  if (mode == 2) {
+    unsigned prefix = 0u;
+    int k_rem = k;
+    unsigned n_bin = 0u;
+    for (int p = 0; p < 3; ++p) {
+      const unsigned fm = fixed_mask(p);
+      const int sh = digit_shift(p);
+      const unsigned dm = digit_mask(p);
+      for (int i = tid; i < kBins * kSub; i += kThreads) lh[i] = 0u;
+      __syncthreads();
+      for (int r0 = lo; r0 < hi; r0 += kSPer * kThreads) {
+        float v[kSPer];
+#pragma unroll
+        for (int j = 0; j < kSPer; ++j) {
+          const int t = r0 + tid + j * kThreads;
+          v[j] = t < hi ? scores[t] : 0.0f;
+        }
+#pragma unroll
+        for (int j = 0; j < kSPer; ++j) {
+          const int t = r0 + tid + j * kThreads;
+          const unsigned key = score_key(v[j]);
+          if (t < hi && (key & fm) == prefix)
+            atomicAdd(&lh[((key >> sh) & dm) * kSub + (lane & (kSub - 1))], 1u);
+        }
+      }
+      __syncthreads();
+      // pick: thread j (counted from the top) owns bins 2047 - 2j and 2046 - 2j
+      const int hi_bin = kBins - 1 - 2 * tid;
+      unsigned c_hi = 0u, c_lo = 0u;
+#pragma unroll
+      for (int q = 0; q < kSub; ++q) {
+        c_hi += lh[hi_bin * kSub + q];
+        c_lo += lh[(hi_bin - 1) * kSub + q];
+      }
+      const unsigned mine = c_hi + c_lo;
+      unsigned incl = mine;
+#pragma unroll
+      for (int off = 1; off < 64; off <<= 1) {
+        const unsigned y = __shfl_up(incl, off);
+        if (lane >= off) incl += y;
+      }
+      if (lane == 63) wtot[wave] = incl;
+      __syncthreads();
+      unsigned above = incl - mine;
+      for (int w = 0; w < wave; ++w) above += wtot[w];
+      const unsigned kr = (unsigned)k_rem;
+      if (above < kr && kr <= above + mine) {  // exactly one thread
+        if (above + c_hi >= kr) {
+          s_res[0] = (unsigned)hi_bin;
+          s_res[1] = above;
+          s_res[2] = c_hi;
+        } else {
+          s_res[0] = (unsigned)(hi_bin - 1);
+          s_res[1] = above + c_hi;
+          s_res[2] = c_lo;
+        }
+      }
+      __syncthreads();
+      prefix |= s_res[0] << sh;
+      k_rem -= (int)s_res[1];
+      n_bin = s_res[2];
+      __syncthreads();  // s_res and wtot are written again in the next pass
+    }
+    theta = prefix;
+    eq_keep = k_rem;
+    all_eq = (unsigned)eq_keep >= n_bin;
+  }
+
+  // keep flags of the whole prompt; equal keys ranked in index order
+  int eq_before = 0;
+  for (int r0 = pb; r0 < pe; r0 += kSPer * kThreads) {
+    float v[kSPer];
+    if (mode == 2) {
+#pragma unroll
+      for (int j = 0; j < kSPer; ++j) {
+        const int t = r0 + tid + j * kThreads;
+        v[j] = (t < pe && t >= lo && t < hi) ? scores[t] : 0.0f;
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < kSPer; ++j) {
+      const int t = r0 + tid + j * kThreads;
+      const bool in = t < pe;
+      const bool doc = in && t >= lo && t < hi;
+      uint8_t kf = 1;
+      bool eq = false;
+      if (doc) {
+        if (mode == 0) {
+          kf = 0;
+        } else if (mode == 2) {
+          const unsigned key = score_key(v[j]);
+          kf = key > theta ? 1 : 0;
+          eq = key == theta;
+          if (eq && all_eq) kf = 1;
+        }
+      }
+      if (!all_eq) {  // uniform: rank the equal keys of this step
+        const unsigned long long bal = __ballot(eq);
+        const int in_wave = __popcll(bal & ((lane == 63) ? ~0ull : ((2ull << lane) - 1)));
+        __syncthreads();
+        if (lane == 63) wtot[wave] = (unsigned)in_wave;
+        __syncthreads();
+        int before = 0, step_total = 0;
+        for (int w = 0; w < kThreads / 64; ++w) {
+          if (w < wave) before += (int)wtot[w];
+          step_total += (int)wtot[w];
+        }
+        if (eq) kf = (eq_before + before + in_wave <= eq_keep) ? 1 : 0;
+        eq_before += step_total;
+      }
+      if (in) keep[t] = kf;
+    }
+  }
+}
+
 int chunk_size(int64_t T) {
   int64_t C = kMinChunk;
   while ((T + C - 1) / C > kMaxChunks) C *= 2;
@@ -335,6 +487,11 @@ hipError_t launch_select(const float* scores, const int32_t* cu, const int32_t* 
                          const int32_t* de, const int32_t* budget, int B, int64_t T,
                          uint8_t* keep, void* ws, hipStream_t s) {
   if (B == 0 || T == 0) return hipSuccess;
+  if (T <= kSingleMaxT) {
+    hipLaunchKernelGGL(sel_single, dim3((unsigned)B), dim3(kThreads), 0, s, scores, cu, db, de,
+                       budget, keep);
+    return hipGetLastError();
+  }
   auto* st = static_cast<SelState*>(ws);
   const size_t st_bytes = ((size_t)2 * B * sizeof(SelState) + 255) & ~(size_t)255;
   auto* part0 = reinterpret_cast<unsigned*>(static_cast<char*>(ws) + st_bytes);

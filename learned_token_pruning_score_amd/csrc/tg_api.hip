@@ -19,6 +19,9 @@ int from_hip(hipError_t e) { return e == hipSuccess ? TG_OK : TG_ERR_HIP; }
 
 hipStream_t as_stream(void* s) { return reinterpret_cast<hipStream_t>(s); }
 
+// Largest second and third launch-grid dimension.
+constexpr int kMaxGridYZ = 65535;
+
 }  // namespace
 
 extern "C" {
@@ -113,6 +116,7 @@ int tg_select_topk(const float* scores, const int32_t* cu_seqlens, const int32_t
   if (T == 0 && B == 0) return TG_OK;
   if (!cu_seqlens || !doc_begin || !doc_end || !budget) return TG_ERR_NULL;
   if (T > 0 && (!scores || !keep)) return TG_ERR_NULL;
+  if (B > kMaxGridYZ) return TG_ERR_UNSUPPORTED;  // one launch row per prompt
   if (!workspace || workspace_bytes < tg::select_workspace_bytes(B, T)) return TG_ERR_WORKSPACE;
   if (!aligned16(workspace)) return TG_ERR_ALIGN;
   if (T == 0) return TG_OK;
@@ -169,6 +173,11 @@ int tg_gated_attn_fwd(const void* q, const void* k, const void* v, int64_t q_tok
   if (d != 64 && d != 128) return TG_ERR_UNSUPPORTED;
   // a 64-key tile of k or v is addressed with 32-bit byte offsets
   if (k_tok_stride > (1 << 23) || v_tok_stride > (1 << 23)) return TG_ERR_UNSUPPORTED;
+  // launch grids: one row per prompt; 256-row query tiles (bf16) or one
+  // plane per head (fp32) in the third dimension
+  if (B > kMaxGridYZ) return TG_ERR_UNSUPPORTED;
+  if (dtype == TG_BF16 && (max_kept_len + 255) / 256 > kMaxGridYZ) return TG_ERR_UNSUPPORTED;
+  if (dtype == TG_F32 && Hq > kMaxGridYZ) return TG_ERR_UNSUPPORTED;
   if (B == 0 || Kt == 0) return TG_OK;
   if (!q || !k || !v || !cu_kept || !out) return TG_ERR_NULL;
   if (gain && !bias_s) return TG_ERR_NULL;

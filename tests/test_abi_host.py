@@ -124,6 +124,8 @@ def test_select_and_compact_argument_checks():
     assert s(FAKE, FAKE, FAKE, FAKE, FAKE, 3, 1000, FAKE, None, need, None) == TG_ERR_WORKSPACE
     assert s(FAKE, FAKE, FAKE, FAKE, FAKE, 3, 1000, FAKE, FAKE + 4, need, None) == TG_ERR_ALIGN
     assert s(None, None, None, None, None, 0, 0, None, None, 0, None) == TG_OK
+    big = tg.tg_select_topk_workspace(65536, 70000)
+    assert s(FAKE, FAKE, FAKE, FAKE, FAKE, 65536, 70000, FAKE, FAKE, big, None) == TG_ERR_UNSUPPORTED
     cneed = tg.tg_compact_workspace(3, 1000)
     c = lib.tg_compact
     # (hidden, ld, D, dtype, pos, scores, keep, cu, db, de, B, T, Kt, hk, pk, bk, ik, ws, wsb, stream)
@@ -175,3 +177,7 @@ def test_attention_argument_checks():
     assert call(k=FAKE + 2) == TG_ERR_ALIGN
     assert call(vs=1028) == TG_ERR_ALIGN
     assert call(B=0) == TG_OK and call(Kt=0, maxlen=0) == TG_OK  # valid no-ops
+    # launch-grid limits: prompts, 256-row query tiles (bf16), heads (fp32)
+    assert call(B=65536, Kt=70000, maxlen=100) == TG_ERR_UNSUPPORTED
+    assert call(Kt=65536 * 256 + 1, maxlen=65536 * 256 + 1) == TG_ERR_UNSUPPORTED
+    assert call(dtype=0, Hq=65536, Hkv=1, qs=65536 * 128) == TG_ERR_UNSUPPORTED

@@ -218,14 +218,16 @@ def test_select_hand_worked_and_specials_on_gpu():
         assert np.nonzero(keep)[0].tolist() == cs["kept"], cs
 
 
-@pytest.mark.parametrize("seed", [0, 1, 2])
-def test_select_heavy_ties_and_ragged(seed):
+# the first two inputs (115005 tokens) take the one-workgroup-per-prompt
+# path, the last (315005 tokens) the chunked four-kernel path
+@pytest.mark.parametrize("seed,long_len", [(0, 70001), (1, 70001), (2, 270001)])
+def test_select_heavy_ties_and_ragged(seed, long_len):
     rng = np.random.default_rng(100 + seed)
     B = 6
-    lens = np.array([0, 1, 5000, 70001, 3, 40000])
+    lens = np.array([0, 1, 5000, long_len, 3, 40000])
     cu = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
     db = np.array([0, 0, 100, 7, 0, 39990])
-    de = np.array([0, 1, 4900, 70001, 3, 40000])
+    de = np.array([0, 1, 4900, long_len, 3, 40000])
     bud = np.array([5, 0, 1234, 9000, 7, 4])
     T = int(cu[-1])
     # few distinct values -> long runs of equal keys, plus specials
