@@ -7,6 +7,8 @@
 //
 // bf16 path (gfx950 MFMA, fp32 accumulation): one workgroup of 8 waves per
 // (query head, prompt, 256-row query tile); each wave owns 32 query rows.
+// Short inputs (fewer 256-row tiles than twice the CUs) take the key-split
+// schedule described at attn_bf16_ks_kernel instead.
 //  * Scores are formed transposed, S^T = K Q^T, with the 32x32x16 MFMA: lane
 //    l then holds 32 keys of query row (l & 31) per 64-key tile, so the
 //    softmax max and sum are lane-local plus one exchange with lane l ^ 32.
@@ -424,6 +426,385 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_bf16_kernel(
   }
 }
 
+// Key-split schedule (short inputs, where the query tile that sees every
+// key sets the kernel's time): one workgroup of 8 waves per (query head,
+// prompt, 128-row query tile).  Waves w and w + 4 share a SIMD and own the
+// same 32 query rows; wave w takes the even key tiles and wave w + 4 the odd
+// ones, each keeping its own running max, row sum and O.  In interval i the
+// group that owns tile i issues only MFMAs (the value product of its tile
+// i - 2, then the scores of tile i) while the other group runs the softmax
+// of tile i - 1, so one key tile is consumed per interval and the longest
+// row takes half the intervals of the 256-row schedule.  Each group stages
+// its own tiles: the K rows (and bias) of tile t + 2 are loaded in its
+// MFMA interval t and written to LDS in its next (softmax) interval, the V
+// rows of tile t + 2 loaded then and written in its MFMA interval t + 2,
+// so one set of staging registers serves both.  K of tile t lives in LDS
+// stage t % 2 (read in interval t), V of tile t in stage t % 3 (read in
+// interval t + 2).  At the end the odd-tile waves hand (max, sum, O) to
+// their partners through LDS, which merge them in a fixed order.
+template <int HD>
+__global__ __launch_bounds__(512, 1) void attn_bf16_ks_kernel(
+    const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
+    const uint16_t* __restrict__ v, int64_t qs, int64_t ks, int64_t vs,
+    const float* __restrict__ bias, const float* __restrict__ gain, float qk_scale,
+    const int32_t* __restrict__ cu, int Hq, int group, int head_swizzle, int n_qtiles,
+    int64_t Kt, uint16_t* __restrict__ out, float* __restrict__ lse) {
+  constexpr int NT = 512;
+  constexpr int BQ = 128;           // query rows per workgroup
+  constexpr int KCH = HD / 8;
+  constexpr int NKS = HD / 16;
+  constexpr int NDB = HD / 32;
+  constexpr int K_ITEMS = kBK * KCH;
+  constexpr int KROW = KCH + 1;
+  constexpr int VROW = KCH + 4;
+  constexpr int K_STAGE = kBK * KROW;  // uint4 units
+  constexpr int V_STAGE = kBK * VROW;
+  constexpr int B_OFF = 2 * K_STAGE + 3 * V_STAGE;
+  constexpr int LDS_U4 = B_OFF + (2 * kBK * 4) / 16;
+  // the end-of-kernel merge reuses the same memory
+  static_assert(4 * NDB * 16 * 64 + 2 * 4 * 64 <= 4 * B_OFF, "merge area");
+  __shared__ uint4 smem[LDS_U4];
+  uint32_t* const sB = reinterpret_cast<uint32_t*>(smem + B_OFF);  // [2][kBK]
+
+  const int x = blockIdx.x;
+  const int h = head_swizzle ? (x % 8) * (Hq / 8) + x / 8 : x;
+  const int b = blockIdx.y;
+  const int tile = n_qtiles - 1 - (int)blockIdx.z;
+  const int lo = cu[b];
+  const int n = cu[b + 1] - lo;
+  const int q0 = tile * BQ;
+  if (q0 >= n) return;
+  const int kvh = h / group;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int G = lane >> 5;
+  const int grp = wave >> 2;   // 0: even key tiles, 1: odd key tiles
+  const int pair = wave & 3;
+  const int qw = q0 + 32 * pair;
+  const int my_q = qw + (lane & 31);
+  const bool has_bias = (bias != nullptr) && (gain != nullptr);
+  const float cmul = has_bias ? gain[h] * kLog2e / qk_scale : 0.0f;
+  const bf16x8 q_one = as_bf16x8(make_uint4(G == 0 ? 0x3F803F80u : 0u, 0u, 0u, 0u));
+  const float rs_thr = kRescale / qk_scale;
+
+  bf16x8 qf[NKS];
+  {
+    const uint16_t* qp = q + (int64_t)(lo + my_q) * qs + (int64_t)h * HD + 8 * G;
+#pragma unroll
+    for (int st = 0; st < NKS; ++st) {
+      uint4 u = make_uint4(0, 0, 0, 0);
+      if (my_q < n) u = *reinterpret_cast<const uint4*>(qp + 16 * st);
+      qf[st] = as_bf16x8(u);
+    }
+  }
+  f32x16 o[NDB];
+#pragma unroll
+  for (int db = 0; db < NDB; ++db)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) o[db][i] = 0.0f;
+  float m_run = -INFINITY;
+  float nms = 0.0f;
+  float l_run = 0.0f;
+
+  const int kv_end = min(q0 + BQ, n);
+  const int n_kt = (kv_end + kBK - 1) / kBK;
+  const bool wave_active = qw < n;
+  const int t_diag = wave_active ? min(qw + 31, n - 1) / kBK : -1;  // the wave's masked tile
+  const uint16_t* kbase = k + (int64_t)lo * ks + (int64_t)kvh * HD;
+  const uint16_t* vbase = v + (int64_t)lo * vs + (int64_t)kvh * HD;
+  const float* bias_p = bias ? bias + lo : nullptr;
+
+  // Staging by the group's 256 threads, HALF_T 16-byte chunks each; buffer
+  // loads read rows past the prompt as zero (see the 256-row kernel).
+  constexpr int HALF_T = K_ITEMS / (NT / 2);
+  static_assert(K_ITEMS % (NT / 2) == 0, "half split");
+  const int gtid = tid & (NT / 2 - 1);
+  int k_off[HALF_T], v_off[HALF_T];
+#pragma unroll
+  for (int j = 0; j < HALF_T; ++j) {
+    const int id = gtid + j * (NT / 2);
+    k_off[j] = ((id / KCH) * (int)ks + (id % KCH) * 8) * 2;
+    v_off[j] = ((id / KCH) * (int)vs + (id % KCH) * 8) * 2;
+  }
+  uint4 hreg[HALF_T];
+  float breg = 0.0f;
+  auto rows_of = [&](int t) __attribute__((always_inline)) {
+    return __builtin_amdgcn_readfirstlane(max(min(n - t * kBK, kBK), 0));
+  };
+  auto load_k = [&](int t) __attribute__((always_inline)) {
+    const int rows = rows_of(t);
+    const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)(kbase + (int64_t)t * kBK * ks), (short)0, rows * (int)ks * 2, kBufFlags);
+#pragma unroll
+    for (int j = 0; j < HALF_T; ++j)
+      hreg[j] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, k_off[j], 0, 0));
+    if (bias_p != nullptr) {
+      const __amdgpu_buffer_rsrc_t rb = __builtin_amdgcn_make_buffer_rsrc(
+          (void*)(bias_p + t * kBK), (short)0, rows * 4, kBufFlags);
+      breg = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rb, (gtid & (kBK - 1)) * 4, 0, 0));
+    }
+  };
+  auto load_v = [&](int t) __attribute__((always_inline)) {
+    const int rows = rows_of(t);
+    const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)(vbase + (int64_t)t * kBK * vs), (short)0, rows * (int)vs * 2, kBufFlags);
+#pragma unroll
+    for (int j = 0; j < HALF_T; ++j)
+      hreg[j] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, v_off[j], 0, 0));
+  };
+  auto kbuf = [&](int t) __attribute__((always_inline)) { return (int)((unsigned)t & 1u); };
+  auto vbuf = [&](int t) __attribute__((always_inline)) { return (int)((unsigned)t % 3u); };
+  auto store_k = [&](int t) __attribute__((always_inline)) {
+    uint4* sk = smem + kbuf(t) * K_STAGE;
+#pragma unroll
+    for (int j = 0; j < HALF_T; ++j) {
+      const int id = gtid + j * (NT / 2);
+      sk[(id / KCH) * KROW + (id % KCH)] = hreg[j];
+    }
+    if (gtid < kBK) {
+      const float c = breg * cmul;
+      const __bf16 c_hi = (__bf16)c;
+      const __bf16 c_lo = (__bf16)(c - (float)c_hi);
+      sB[kbuf(t) * kBK + gtid] = (uint32_t)__builtin_bit_cast(uint16_t, c_hi) |
+                                  ((uint32_t)__builtin_bit_cast(uint16_t, c_lo) << 16);
+    }
+  };
+  auto store_v = [&](int t) __attribute__((always_inline)) {
+    uint4* sv = smem + 2 * K_STAGE + vbuf(t) * V_STAGE;
+#pragma unroll
+    for (int j = 0; j < HALF_T; ++j) {
+      const int id = gtid + j * (NT / 2);
+      sv[(id / KCH) * VROW + (id % KCH)] = hreg[j];
+    }
+  };
+
+  f32x16 s[2];
+  auto qk = [&](int t) __attribute__((always_inline)) {
+    typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+    typedef __attribute__((address_space(3))) const u32x4 lds_u4;
+    const int kb_ = kbuf(t);
+    uint32_t ka = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) const char*)
+        reinterpret_cast<const char*>(smem + kb_ * K_STAGE + (lane & 31) * KROW + G);
+    asm volatile("" : "+v"(ka));
+    auto kfrag = [&](int st, uint4 (&f)[2]) __attribute__((always_inline)) {
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+        f[kb] = st < NKS ? __builtin_bit_cast(uint4, *(lds_u4*)(uintptr_t)(ka + ((kb * 32) * KROW + 2 * st) * 16))
+                         : make_uint4((has_bias && G == 0) ? sB[kb_ * kBK + kb * 32 + (lane & 31)] : 0u, 0u, 0u, 0u);
+    };
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) s[kb][i] = 0.0f;
+    uint4 f[NKS + 1][2];
+#pragma unroll
+    for (int j = 0; j < KAHEAD; ++j) kfrag(j, f[j]);
+#pragma unroll
+    for (int st = 0; st <= NKS; ++st) {
+      if (st + KAHEAD <= NKS) kfrag(st + KAHEAD, f[st + KAHEAD]);
+      __builtin_amdgcn_sched_barrier(0);
+      const bf16x8 bq = st < NKS ? qf[st < NKS ? st : 0] : q_one;
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) s[kb] = mfma32x32x16(as_bf16x8(f[st][kb]), bq, s[kb]);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  };
+  bf16x8 pb[2][2];
+  auto softmax = [&](int k0, auto mask_tag) __attribute__((always_inline)) {
+    constexpr bool MASK = decltype(mask_tag)::value;
+    float mx = -INFINITY;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        if (MASK) {
+          const int key = kb * 32 + acc_row(i, lane);
+          if ((k0 + key) > my_q) s[kb][i] = -INFINITY;
+        }
+        mx = fmaxf(mx, s[kb][i]);
+      }
+    mx = pair_max(mx);
+    if (__any(mx > m_run + rs_thr)) {
+      const float m_new = fmaxf(m_run, mx);
+      const float alpha = __builtin_amdgcn_exp2f((m_run - m_new) * qk_scale);
+      l_run *= alpha;
+#pragma unroll
+      for (int db = 0; db < NDB; ++db)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) o[db][i] *= alpha;
+      m_run = m_new;
+      nms = -m_new * qk_scale;
+    }
+    float psum = 0.0f;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        s[kb][i] = __builtin_amdgcn_exp2f(fmaf(s[kb][i], qk_scale, nms));
+        psum += s[kb][i];
+      }
+    l_run += psum;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int hh = 0; hh < 2; ++hh)
+#pragma unroll
+        for (int j = 0; j < 8; ++j) pb[kb][hh][j] = (__bf16)s[kb][8 * hh + j];
+  };
+  auto pv = [&](int t) __attribute__((always_inline)) {
+    const int gi = lane & 15, g = lane >> 4;
+    typedef short s4 __attribute__((ext_vector_type(4)));
+    typedef __attribute__((address_space(3))) s4 lds_s4;
+    uint32_t va = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) const char*)(
+        reinterpret_cast<const char*>(smem + 2 * K_STAGE + vbuf(t) * V_STAGE) +
+        (4 * (g >> 1) + (gi >> 2)) * (VROW * 16) + (16 * (g & 1) + 4 * (gi & 3)) * 2);
+    asm volatile("" : "+v"(va));
+    constexpr int NM = 4 * NDB;
+    auto vfrag = [&](int mi) __attribute__((always_inline)) {
+      const int kh = mi / NDB, db = mi % NDB;
+      const uint32_t a0 = va + ((kh >> 1) * 32 + 16 * (kh & 1)) * (VROW * 16) + db * 64;
+      const s4 lo4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s4*)(uintptr_t)a0);
+      const s4 hi4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s4*)(uintptr_t)(a0 + 8 * (VROW * 16)));
+      return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo4, hi4, 0, 1, 2, 3, 4, 5, 6, 7));
+    };
+    bf16x8 vf[NM];
+#pragma unroll
+    for (int j = 0; j < VAHEAD; ++j) vf[j] = vfrag(j);
+#pragma unroll
+    for (int mi = 0; mi < NM; ++mi) {
+      if (mi + VAHEAD < NM) vf[mi + VAHEAD] = vfrag(mi + VAHEAD);
+      __builtin_amdgcn_sched_barrier(0);
+      const int kh = mi / NDB, db = mi % NDB;
+      o[db] = mfma32x32x16(vf[mi], pb[kh >> 1][kh & 1], o[db]);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  };
+
+  // Schedule of group grp (its own tiles t = grp, grp + 2, ... up to the
+  // wave's diagonal tile; interval i ends with the i-th barrier):
+  //   interval t (MFMA):     V rows of t to LDS, load K of t + 2, PV(t - 2), QK(t)
+  //   interval t + 1 (VALU): softmax(t), K of t + 2 to LDS, load V of t + 2
+  // then one more MFMA interval for the last value product, and staging
+  // only until every wave has passed n_int barriers.
+  const int n_int = n_kt + 3;
+  if (grp == 0) {
+    load_k(0);
+    store_k(0);
+    load_v(0);
+  } else {
+    load_k(1);
+  }
+  __syncthreads();
+  int i = 0;
+  if (grp == 1) {  // interval 0 of the odd group: staging only
+    store_k(1);
+    load_v(1);
+    __syncthreads();
+    i = 1;
+  }
+  if (t_diag >= grp) {
+    int t = grp;
+    store_v(t);
+    load_k(t + 2);
+    qk(t);
+    __syncthreads();
+    if (t == t_diag) softmax(t * kBK, std::true_type{});
+    else softmax(t * kBK, std::false_type{});
+    store_k(t + 2);
+    load_v(t + 2);
+    __syncthreads();
+    t += 2;
+    for (; t < t_diag; t += 2) {
+      store_v(t);
+      load_k(t + 2);
+      pv(t - 2);
+      qk(t);
+      __syncthreads();
+      softmax(t * kBK, std::false_type{});
+      store_k(t + 2);
+      load_v(t + 2);
+      __syncthreads();
+    }
+    if (t == t_diag) {
+      store_v(t);
+      load_k(t + 2);
+      pv(t - 2);
+      qk(t);
+      __syncthreads();
+      softmax(t * kBK, std::true_type{});
+      store_k(t + 2);
+      load_v(t + 2);
+      __syncthreads();
+      t += 2;
+    }
+    store_v(t);  // the last value product
+    load_k(t + 2);
+    pv(t - 2);
+    __syncthreads();
+    store_k(t + 2);
+    load_v(t + 2);
+    __syncthreads();
+    i = t + 2;
+  }
+  for (; i < n_int; ++i) {
+    if (((i ^ grp) & 1) == 0) {
+      store_v(i);
+      load_k(i + 2);
+    } else {
+      store_k(i + 1);
+      load_v(i + 1);
+    }
+    __syncthreads();
+  }
+
+  // Merge: the odd-tile wave of each pair hands its partial state to the
+  // even-tile wave through LDS (the stages are no longer read).
+  float* mO = reinterpret_cast<float*>(smem);  // [pair][db][i][lane]
+  float* mM = mO + 4 * NDB * 16 * 64;          // [pair][lane]
+  float* mL = mM + 4 * 64;
+  if (grp == 1) {
+#pragma unroll
+    for (int db = 0; db < NDB; ++db)
+#pragma unroll
+      for (int i2 = 0; i2 < 16; ++i2) mO[((pair * NDB + db) * 16 + i2) * 64 + lane] = o[db][i2];
+    mM[pair * 64 + lane] = m_run;
+    mL[pair * 64 + lane] = l_run;
+  }
+  __syncthreads();
+  if (grp == 1 || !wave_active) return;
+  const float m1 = mM[pair * 64 + lane];
+  const float l1 = mL[pair * 64 + lane];
+  const float m_all = fmaxf(m_run, m1);  // finite: the diagonal tile is one group's
+  const float a0 = m_run == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f((m_run - m_all) * qk_scale);
+  const float a1 = m1 == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f((m1 - m_all) * qk_scale);
+#pragma unroll
+  for (int db = 0; db < NDB; ++db)
+#pragma unroll
+    for (int i2 = 0; i2 < 16; ++i2)
+      o[db][i2] = o[db][i2] * a0 + mO[((pair * NDB + db) * 16 + i2) * 64 + lane] * a1;
+  const float l_tot = pair_sum(l_run * a0 + l1 * a1);
+  if (my_q < n) {
+    const float inv = 1.0f / l_tot;
+    uint16_t* op = out + (int64_t)(lo + my_q) * ((int64_t)Hq * HD) + (int64_t)h * HD;
+#pragma unroll
+    for (int db = 0; db < NDB; ++db)
+#pragma unroll
+      for (int g4 = 0; g4 < 4; ++g4) {
+        const int d0 = db * 32 + 8 * g4 + 4 * G;
+        unsigned w[2];
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+          const __bf16 e0 = (__bf16)(o[db][4 * g4 + 2 * j] * inv);
+          const __bf16 e1 = (__bf16)(o[db][4 * g4 + 2 * j + 1] * inv);
+          w[j] = (unsigned)__builtin_bit_cast(uint16_t, e0) |
+                 ((unsigned)__builtin_bit_cast(uint16_t, e1) << 16);
+        }
+        *reinterpret_cast<uint2*>(op + d0) = make_uint2(w[0], w[1]);
+      }
+    if (lse != nullptr && G == 0) lse[(int64_t)h * Kt + lo + my_q] = (m_all * qk_scale + __log2f(l_tot)) * kLn2;
+  }
+}
+
 template <int HD>
 __global__ __launch_bounds__(64) void attn_f32_kernel(
     const float* __restrict__ q, const float* __restrict__ k, const float* __restrict__ v,
@@ -481,6 +862,24 @@ hipError_t launch_attn_bf16(const void* q, const void* k, const void* v, int64_t
   const auto* kk = static_cast<const uint16_t*>(k);
   const auto* vv = static_cast<const uint16_t*>(v);
   auto* oo = static_cast<uint16_t*>(out);
+  // Few 256-row query tiles (short inputs): the tile that sees every key
+  // sets the time, and the key-split schedule halves its intervals.
+  int n_cu = 0;
+  const hipError_t e = device_cu_count(&n_cu);
+  if (e != hipSuccess) return e;
+  if ((int64_t)Hq * ((Kt + 255) / 256) < 2 * (int64_t)n_cu) {
+    const int n_qt = (max_len + 127) / 128;
+    const dim3 g2((unsigned)Hq, (unsigned)B, (unsigned)n_qt);
+    if (d == 128)
+      hipLaunchKernelGGL((attn_bf16_ks_kernel<128>), g2, dim3(512), 0, s, qq, kk, vv, qs, ks, vs, bias,
+                         gain, qk_scale, cu_kept, Hq, group, swz, n_qt, Kt, oo, lse);
+    else if (d == 64)
+      hipLaunchKernelGGL((attn_bf16_ks_kernel<64>), g2, dim3(512), 0, s, qq, kk, vv, qs, ks, vs, bias,
+                         gain, qk_scale, cu_kept, Hq, group, swz, n_qt, Kt, oo, lse);
+    else
+      return hipErrorInvalidValue;
+    return hipGetLastError();
+  }
   const int n_qtiles = (max_len + 32 * NW - 1) / (32 * NW);
   const dim3 grid((unsigned)Hq, (unsigned)B, (unsigned)n_qtiles);
   if (d == 128) {

@@ -257,24 +257,32 @@ __global__ __launch_bounds__(256) void gate_f32_kernel(
 
 }  // namespace
 
-hipError_t launch_gate_bf16(const void* hidden, int64_t ld, int64_t T, int D, const void* W1,
-                            const float* b1, const float* w2, float b2, int F, float* scores,
-                            hipStream_t s) {
-  if (T == 0) return hipSuccess;
-  // one workgroup per CU, each looping over tiles; the CU count of each
-  // device is queried once (concurrent first calls store the same value)
+hipError_t device_cu_count(int* n) {
+  // queried once per device (concurrent first calls store the same value)
   static std::atomic<int> cu_count[64];
   int dev = 0;
   hipError_t e = hipGetDevice(&dev);
   if (e != hipSuccess) return e;
   if (dev < 0 || dev >= 64) return hipErrorInvalidDevice;
-  int n_cu = cu_count[dev].load(std::memory_order_relaxed);
-  if (n_cu == 0) {
-    e = hipDeviceGetAttribute(&n_cu, hipDeviceAttributeMultiprocessorCount, dev);
+  int c = cu_count[dev].load(std::memory_order_relaxed);
+  if (c == 0) {
+    e = hipDeviceGetAttribute(&c, hipDeviceAttributeMultiprocessorCount, dev);
     if (e != hipSuccess) return e;
-    n_cu = n_cu > 0 ? n_cu : 1;
-    cu_count[dev].store(n_cu, std::memory_order_relaxed);
+    c = c > 0 ? c : 1;
+    cu_count[dev].store(c, std::memory_order_relaxed);
   }
+  *n = c;
+  return hipSuccess;
+}
+
+hipError_t launch_gate_bf16(const void* hidden, int64_t ld, int64_t T, int D, const void* W1,
+                            const float* b1, const float* w2, float b2, int F, float* scores,
+                            hipStream_t s) {
+  if (T == 0) return hipSuccess;
+  // one workgroup per CU, each looping over tiles
+  int n_cu = 0;
+  const hipError_t e = device_cu_count(&n_cu);
+  if (e != hipSuccess) return e;
   // F split: the smallest that gives every CU a tile (256 / FS tokens each)
   const int nfb = F / 32;
   int fs = 1;

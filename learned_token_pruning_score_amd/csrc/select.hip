@@ -11,7 +11,7 @@
 // kept when it lies outside the document, or its key is above theta, or its
 // key equals theta and fewer than that many equal keys precede it.
 //
-// Up to 2^18 tokens, one workgroup per prompt runs the whole selection
+// Up to 2^15 tokens, one workgroup per prompt runs the whole selection
 // (sel_single): every pass re-reads the prompt's scores from L2, so there is
 // one launch.  Longer inputs are cut into chunks of C tokens per prompt,
 // from its first token, and take four kernels, all on the caller's stream,

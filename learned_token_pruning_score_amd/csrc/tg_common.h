@@ -40,6 +40,9 @@ __device__ __forceinline__ float pair_sum(float x) {
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
+// Compute units of the current device (queried once per device).
+hipError_t device_cu_count(int* n);
+
 // ---------------------------------------------------------------- launchers
 hipError_t launch_gate_bf16(const void* hidden, int64_t ld, int64_t T, int D, const void* W1,
                             const float* b1, const float* w2, float b2, int F, float* scores,

@@ -365,6 +365,32 @@ def test_attention_ragged_edges(dtype, d, Hq, Hkv):
                     None if gg is None else gg.astype(np.float64), tau, cu, dtype, None)
 
 
+# The same edge prompts next to one long prompt, so that the query tiles are
+# many enough for the 256-row schedule (the short batches above take the
+# key-split schedule); the oracle checks every edge row and a sample of the
+# long prompt.
+@pytest.mark.parametrize("d,Hq,Hkv,long_len", [
+    (128, 16, 8, 8300), (64, 4, 2, 33000), (128, 3, 3, 44000)])
+def test_attention_ragged_edges_long_batch(d, Hq, Hkv, long_len):
+    rng = np.random.default_rng(d + Hq + 1)
+    lens = [1, 2, 63, 64, 65, 0, 127, 128, 129, 300, 31, 33, long_len]
+    cu, q, k, v, bias, gain = _attn_inputs(rng, lens, Hq, Hkv, d, torch.bfloat16)
+    assert Hq * ((int(cu[-1]) + 255) // 256) >= 512
+    cud = torch.from_numpy(cu).to(DEV)
+    lo = int(cu[-2])
+    rows = np.concatenate([np.arange(lo), lo + np.array([0, 1, 63, 64, 255, 256, 257, 4000]),
+                           lo + long_len - 1 - np.arange(40)])
+    rows = np.unique(rows[rows < int(cu[-1])])
+    for tau, gg in [(1.15, gain), (1.0, None)]:
+        o, lse = tg.tg_gated_attn_fwd(q.to(DEV), k.to(DEV), v.to(DEV),
+                                      torch.from_numpy(bias).to(DEV),
+                                      None if gg is None else torch.from_numpy(gg).to(DEV), tau,
+                                      cud, max(lens), want_lse=True)
+        torch.cuda.synchronize()
+        _attn_check(o.cpu(), lse.cpu(), q, k, v, bias if gg is not None else None,
+                    None if gg is None else gg.astype(np.float64), tau, cu, torch.bfloat16, rows)
+
+
 def test_attention_properties_on_gpu():
     rng = np.random.default_rng(5)
     lens = [700, 1, 1500]
