@@ -12,9 +12,12 @@ import synth
 pytestmark = pytest.mark.gpu
 
 
-def test_graph_replay_matches_eager():
+# a small batch (one-launch top-K, key-split attention) and a 113k-token
+# ragged batch (four-kernel top-K, 256-row attention)
+@pytest.mark.parametrize("name", ["ragged_small_bf16", "ragged_8x_4k_32k"])
+def test_graph_replay_matches_eager(name):
     dev = "cuda"
-    w = synth.make_workload("ragged_small_bf16", seed=3)
+    w = synth.make_workload(name, seed=3)
     s = w.spec
     gp = tg.GatedPrefill(w.cu_seqlens, w.doc_begin, w.doc_end, w.budget, s.D, w.dtype)
     hidden, W1, b1, w2 = (t.to(dev) for t in (w.hidden, w.W1, w.b1, w.w2))
