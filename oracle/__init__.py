@@ -14,11 +14,14 @@ itself (library routines, brute force, closed forms, invariants); none is
 """
 
 from .tokengate import (  # noqa: F401
+    apply_rope,
     attention_rows_for_check,
     compact,
     gate_scores,
     gated_attention,
     plan,
+    qkv_rope,
+    rope_inv_freq,
     round_f32,
     select_topk,
 )

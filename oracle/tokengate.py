@@ -214,3 +214,53 @@ def attention_rows_for_check(cu_kept, per_prompt: int, seed: int = 0) -> np.ndar
         n = min(per_prompt, hi - lo)
         out.extend(g.choice(np.arange(lo, hi), size=n, replace=False).tolist())
     return np.unique(np.asarray(out, dtype=np.int64))
+
+
+def rope_inv_freq(d: int, theta: float) -> np.ndarray:
+    """Rotary frequencies ``theta ** (-2 i / d)`` for i = 0 .. d/2 - 1, fp64.
+
+    Reading (the article names Qwen3-1.7B as the model but not its position
+    encoding): the rotary embedding of the Qwen3 family, in the rotate-half
+    form, with its base ``theta`` (1e6 for Qwen3) as a parameter.
+    """
+    i = np.arange(d // 2, dtype=np.float64)
+    return np.power(float(theta), -2.0 * i / d)
+
+
+def apply_rope(x, pos, theta: float) -> np.ndarray:
+    """Rotate every head vector of ``x`` [n, H, d] at its row's position.
+
+    Article, "How does TokenGate learned token pruning work?": the layers
+    above the gate run on the kept tokens only, which keep their original
+    position ids.  Reading (rotate-half form): element i of a head is paired
+    with element i + d/2, and the pair is rotated by the angle
+    ``pos * theta ** (-2 i / d)``:
+        y_i        = x_i cos(a_i) - x_{i+d/2} sin(a_i)
+        y_{i+d/2}  = x_{i+d/2} cos(a_i) + x_i sin(a_i)
+    """
+    x = _f64(x)
+    d = x.shape[-1]
+    half = d // 2
+    ang = _f64(pos)[:, None] * rope_inv_freq(d, theta)[None, :]  # [n, d/2]
+    c = np.cos(ang)[:, None, :]
+    s = np.sin(ang)[:, None, :]
+    a, b = x[..., :half], x[..., half:]
+    return np.concatenate([a * c - b * s, b * c + a * s], axis=-1)
+
+
+def qkv_rope(hidden, W, pos, theta: float, Hq: int, Hkv: int, d: int):
+    """Attention inputs of a pruned layer from the kept rows.
+
+    Article, "How does TokenGate learned token pruning work?": above the gate
+    the model processes only the kept tokens, at their original positions.
+    Reading: ``y = hidden @ W.T`` with ``W`` [(Hq + 2 Hkv) d, D] whose rows are
+    the q heads, then the k heads, then the v heads (no bias, no per-head
+    normalisation); q and k are rotated at the rows' original positions,
+    v is not.  Returns fp64 (q [n, Hq, d], k [n, Hkv, d], v [n, Hkv, d]).
+    """
+    y = _f64(hidden) @ _f64(W).T
+    n = y.shape[0]
+    q = y[:, :Hq * d].reshape(n, Hq, d)
+    k = y[:, Hq * d:(Hq + Hkv) * d].reshape(n, Hkv, d)
+    v = y[:, (Hq + Hkv) * d:].reshape(n, Hkv, d)
+    return apply_rope(q, pos, theta), apply_rope(k, pos, theta), v

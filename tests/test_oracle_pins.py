@@ -7,7 +7,9 @@ Attention Makes Long-Context Prefill Up to 11.3x Faster") or plain mathematics
 fixes.  Plausible slips each fail at least one test here: a dropped bias term,
 a wrong SiLU, ties broken the wrong way, -0.0/NaN mishandled, a pruned
 question token, a wrong bias for non-document keys, temperature applied to the
-bias, an off-by-one causal mask, a wrong GQA head map, a wrong softmax scale.
+bias, an off-by-one causal mask, a wrong GQA head map, a wrong softmax scale,
+rotary pairs (2i, 2i+1) instead of (i, i + d/2), a wrong rotation sign or
+frequency, v rotated, q/k/v heads read from the wrong rows of the projection.
 """
 
 import itertools
@@ -389,3 +391,80 @@ def test_attention_rows_subset_and_prompt_isolation():
     o3, _ = oracle.gated_attention(q, k2, v, bias, gain, 1.1, cu)
     np.testing.assert_array_equal(o3[:15], o[:15])
     assert not np.allclose(o3[15:], o[15:])
+
+
+# ------------------------------------------- q/k/v of the kept rows, rotary
+# (slips each caught here: pairs (2i, 2i+1) instead of (i, i + d/2), a wrong
+# rotation sign, frequencies off by a factor, v rotated, q and k heads taken
+# from the wrong rows of W, a transposed projection)
+
+def test_rope_qkv_hand_worked():
+    g = _load("rope_qkv_hand_worked.json")
+    r = g["rope"]
+    for case in r["cases"]:
+        x = np.array(r["x"])[None, None, :]
+        y = oracle.apply_rope(x, np.array([case["pos"]]), r["theta"])
+        assert np.max(np.abs(y[0, 0] - np.array(case["y"]))) <= 1e-12
+    c = g["qkv"]
+    q, k, v = oracle.qkv_rope(np.array(c["hidden"]), np.array(c["W"]), np.array(c["pos"]),
+                              c["theta"], c["Hq"], c["Hkv"], c["d"])
+    for got, exp in ((q, c["q"]), (k, c["k"]), (v, c["v"])):
+        assert np.max(np.abs(got - np.array(exp))) <= 1e-12
+
+
+def test_rope_inv_freq_closed_form():
+    f = oracle.rope_inv_freq(8, 1.0e6)
+    exp = [1.0, 1.0e6 ** -0.25, 1.0e-3, 1.0e6 ** -0.75]
+    assert np.max(np.abs(f - np.array(exp)) / np.array(exp)) <= 1e-14
+
+
+@pytest.mark.parametrize("d,theta", [(128, 1.0e6), (64, 1.0e4), (2, 10.0)])
+def test_rope_equals_complex_rotation(d, theta):
+    # the rotate-half form read as complex numbers z_i = x_i + 1j x_{i+d/2}
+    # multiplied by exp(1j * pos * theta^(-2i/d)): numpy complex arithmetic
+    rng = np.random.default_rng(d)
+    n, H = 37, 3
+    x = rng.standard_normal((n, H, d))
+    pos = rng.integers(0, 200000, n)
+    half = d // 2
+    freq = 1.0 / theta ** (np.arange(0, d, 2, dtype=np.float64) / d)
+    z = (x[..., :half] + 1j * x[..., half:]) * np.exp(1j * pos[:, None, None] * freq[None, None, :])
+    y = oracle.apply_rope(x, pos, theta)
+    assert np.max(np.abs(y[..., :half] - z.real)) <= 1e-9
+    assert np.max(np.abs(y[..., half:] - z.imag)) <= 1e-9
+
+
+def test_rope_relative_position_identity_and_norm():
+    rng = np.random.default_rng(3)
+    d, theta = 64, 1.0e6
+    q = rng.standard_normal((1, 1, d))
+    k = rng.standard_normal((1, 1, d))
+    for m, n_ in [(5, 2), (1000, 999), (70000, 12), (3, 3)]:
+        lhs = np.sum(oracle.apply_rope(q, [m], theta) * oracle.apply_rope(k, [n_], theta))
+        rhs = np.sum(oracle.apply_rope(q, [m - n_], theta) * k)
+        assert abs(lhs - rhs) <= 1e-9 * max(1.0, abs(rhs))
+    x = rng.standard_normal((6, 2, d))
+    assert np.array_equal(oracle.apply_rope(x, np.zeros(6), theta), x)
+    y = oracle.apply_rope(x, np.arange(6) * 977, theta)
+    half = d // 2
+    assert np.allclose(x[..., :half] ** 2 + x[..., half:] ** 2, y[..., :half] ** 2 + y[..., half:] ** 2,
+                       rtol=1e-12, atol=1e-12)
+
+
+def test_qkv_projection_brute_force():
+    rng = np.random.default_rng(11)
+    n, D, Hq, Hkv, d = 3, 5, 2, 1, 4
+    h = rng.standard_normal((n, D))
+    W = rng.standard_normal(((Hq + 2 * Hkv) * d, D))
+    y = [[sum(h[r][c] * W[o][c] for c in range(D)) for o in range(W.shape[0])] for r in range(n)]
+    y = np.array(y)
+    q, k, v = oracle.qkv_rope(h, W, np.zeros(n), 1.0e6, Hq, Hkv, d)  # pos 0: no rotation
+    assert np.max(np.abs(q.reshape(n, -1) - y[:, :Hq * d])) <= 1e-12
+    assert np.max(np.abs(k.reshape(n, -1) - y[:, Hq * d:(Hq + Hkv) * d])) <= 1e-12
+    assert np.max(np.abs(v.reshape(n, -1) - y[:, (Hq + Hkv) * d:])) <= 1e-12
+    # at other positions v is untouched and q, k are the rotated projections
+    pos = np.array([7, 100, 3000])
+    q2, k2, v2 = oracle.qkv_rope(h, W, pos, 1.0e6, Hq, Hkv, d)
+    assert np.array_equal(v2, v)
+    assert np.max(np.abs(q2 - oracle.apply_rope(q, pos, 1.0e6))) <= 1e-12
+    assert np.max(np.abs(k2 - oracle.apply_rope(k, pos, 1.0e6))) <= 1e-12
