@@ -123,6 +123,9 @@ def reference_points(tg, w, gp, layers, outs, hidden, W1, b1, w2, stream, dev):
         bias) at 32768 tokens with the same head shapes;
       * gate and attention launches after a 1 GiB write that evicts L2 and
         the last-level cache (the timed step runs them back to back);
+      * a pruned layer's input step, beside the step: the rotary table of
+        the kept rows' positions and the fused q/k/v projection of the kept
+        rows with the rotary embedding (seeded weights of the layer's shape);
       * what the chip reaches here on plain library work: a bf16 GEMM of
         8192^3 and a 1 GiB device copy."""
     import torch
@@ -145,6 +148,20 @@ def reference_points(tg, w, gp, layers, outs, hidden, W1, b1, w2, stream, dev):
     work = algorithmic_work(w, gp.Kt, gp.cu_kept_h)
     r = {"attn_gated_us": t_gated * 1e3, "attn_no_bias_us": t_plain * 1e3,
          "key_bias_cost_ratio": t_gated / t_plain}
+
+    import synth
+    Wqkv = synth.qkv_weights(s, 0, seed=0).to(dev)
+    nq = (s.Hq + 2 * s.Hkv) * s.d
+    qkv_buf = torch.empty((gp.Kt, nq), dtype=Wqkv.dtype, device=dev)
+    rope = lambda: gp.rope(s.d, s.rope_theta)  # noqa: E731
+    proj = lambda: gp.project_qkv(Wqkv, s.Hq, s.Hkv, s.d, out=qkv_buf)  # noqa: E731
+    rope()
+    proj()
+    r["rope_table_us"] = time_launches(rope, stream, reps=7, n=5) * 1e3
+    t = time_launches(proj, stream, reps=7, n=5)
+    r["qkv_rope_us"] = t * 1e3
+    r["qkv_rope_TFLOPs"] = 2.0 * gp.Kt * s.D * nq / (t / 1e3) / 1e12
+    del Wqkv, qkv_buf
 
     flush_buf = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
     flush = lambda: flush_buf.fill_(1)  # noqa: E731

@@ -18,6 +18,10 @@
  *   tg_compact         stable gather of kept rows, positions and biases
  *   tg_gated_attn_fwd  causal GQA attention over the kept tokens with the
  *                      score bias: logit = tau * q.k / sqrt(d) + g_h * s_j
+ *   tg_rope_table      cos / sin of the rotary embedding at the kept rows'
+ *                      original positions
+ *   tg_qkv_rope        fused q/k/v projection of the kept rows, rotated at
+ *                      their original positions (the pruned layers' input)
  *
  * Conventions (every call):
  *   - Pointers are device pointers unless the parameter name ends in _h
@@ -182,6 +186,47 @@ int tg_gated_attn_fwd(const void* q, const void* k, const void* v,
                       const float* gain, float tau, const int32_t* cu_kept,
                       int B, int max_kept_len, int64_t Kt, int Hq, int Hkv,
                       int d, int dtype, void* out, float* lse, void* stream);
+
+/* Rotary table of the kept rows (section "How does TokenGate learned token
+ * pruning work?": the pruned forward keeps each kept token's original
+ * position id).  For row t and frequency index i < d/2:
+ *     a = pos[t] * rope_theta^(-2 i / d)
+ *     table[t, i] = (cos a, sin a)
+ * evaluated in fp64 and stored as an fp32 pair.  pos [Kt] int32 (device,
+ * e.g. tg_compact's pos_out); table [Kt, d/2, 2] fp32, 16-byte aligned.
+ * rope_theta is the rotary base (1e6 for the Qwen3 family), finite and > 1,
+ * else TG_ERR_RANGE.  d in {64, 128}.  The table depends on the positions
+ * only: a pruned forward builds it once and every layer reuses it.
+ */
+int tg_rope_table(const int32_t* pos, int64_t Kt, int d, double rope_theta, float* table,
+                  void* stream);
+
+/* Attention inputs of a pruned layer (section "How does TokenGate learned
+ * token pruning work?": the layers above the gate process the kept tokens
+ * only, at their original positions).  For kept row t:
+ *     y_t = W_qkv . x_t          W_qkv [(Hq + 2 Hkv) d, D], rows: the Hq q
+ *                                heads, then the Hkv k heads, then the Hkv
+ *                                v heads, d rows each
+ * then every q and k head is rotated in the rotate-half form with row t of
+ * rope_table (tg_rope_table, same d): for i < d/2, (c, s) = table[t, i],
+ *     y_i       <- y_i c - y_{i+d/2} s
+ *     y_{i+d/2} <- y_{i+d/2} c + y_i s
+ * and the v heads are stored as projected.  No bias, no per-head norm.
+ *
+ * x [Kt, D] with token stride ld_x (>= D) elements, e.g. tg_compact's
+ * hidden_out; w_qkv packed [(Hq + 2 Hkv) d, D]; qkv [Kt, (Hq + 2 Hkv) d]
+ * with token stride ld_qkv (>= (Hq + 2 Hkv) d): q at column 0, k at Hq d,
+ * v at (Hq + Hkv) d, so that tg_gated_attn_fwd reads q, k and v in place
+ * with token strides ld_qkv.  x, w_qkv and qkv share the dtype.
+ * Supported: d in {64, 128}; bf16 needs D % 64 == 0, ld_x and D below 2^22,
+ * x, w_qkv, qkv and rope_table 16-byte aligned and ld_x, ld_qkv multiples
+ * of 8; fp32 needs Kt * (Hq + 2 Hkv) d < 2^31 and an aligned rope_table.
+ * bf16 runs on MFMA with fp32 accumulation, rotates in fp32 and rounds to
+ * bf16 once; fp32 runs on vector ALUs.
+ */
+int tg_qkv_rope(const void* x, int64_t ld_x, int64_t Kt, int D, const void* w_qkv,
+                const float* rope_table, int Hq, int Hkv, int d, int dtype, void* qkv,
+                int64_t ld_qkv, void* stream);
 
 #ifdef __cplusplus
 }

@@ -2,7 +2,7 @@
 
 Python face of libtokengate.so: the C ABI calls under the same names
 (``tg_plan``, ``tg_gate_score``, ``tg_select_topk``, ``tg_compact``,
-``tg_gated_attn_fwd``) taking torch device tensors, and ``GatedPrefill``,
+``tg_gated_attn_fwd``, ``tg_rope_table``, ``tg_qkv_rope``) taking torch device tensors, and ``GatedPrefill``,
 which strings them together the way the three-phase prefill of the TokenGate
 article ("How does TokenGate learned token pruning work?") does.  Every step
 runs in the library's HIP kernels; without the built library or a GPU these
@@ -23,6 +23,8 @@ from ._lib import (  # noqa: F401
     tg_gate_score,
     tg_gated_attn_fwd,
     tg_plan,
+    tg_qkv_rope,
+    tg_rope_table,
     tg_select_topk,
     tg_select_topk_workspace,
 )

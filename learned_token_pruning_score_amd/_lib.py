@@ -48,6 +48,9 @@ SIGNATURES = {
     "tg_gated_attn_fwd": (_c_int, [_c_vp, _c_vp, _c_vp, _c_i64, _c_i64, _c_i64, _c_vp, _c_vp,
                                    _c_f32, _c_vp, _c_int, _c_int, _c_i64, _c_int, _c_int, _c_int,
                                    _c_int, _c_vp, _c_vp, _c_vp]),
+    "tg_rope_table": (_c_int, [_c_vp, _c_i64, _c_int, ctypes.c_double, _c_vp, _c_vp]),
+    "tg_qkv_rope": (_c_int, [_c_vp, _c_i64, _c_i64, _c_int, _c_vp, _c_vp, _c_int, _c_int, _c_int,
+                             _c_int, _c_vp, _c_i64, _c_vp]),
 }
 
 _lib = None
@@ -265,3 +268,58 @@ def tg_gated_attn_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
         _dev(cu_kept, "cu_kept", torch.int32), B, int(max_kept_len), Kt, Hq, Hkv, d,
         _dtype_code(q), _dev(out, "out"), _dev(lse, "lse", torch.float32), _stream(stream)))
     return out, lse
+
+
+def tg_rope_table(pos: torch.Tensor, d: int, rope_theta: float,
+                  out: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """cos / sin of the rotary embedding at positions pos [Kt] int32.
+
+    Returns table [Kt, d/2, 2] fp32: (cos, sin) of pos * rope_theta^(-2 i / d).
+    """
+    _require_gpu()
+    lib = load_library()
+    if pos.dim() != 1:
+        raise ValueError("pos must be 1-D")
+    Kt = pos.shape[0]
+    if out is None:
+        out = torch.empty((Kt, d // 2, 2), dtype=torch.float32, device=pos.device)
+    elif tuple(out.shape) != (Kt, d // 2, 2) or not out.is_contiguous():
+        raise ValueError(f"out has shape {tuple(out.shape)}")
+    _check("tg_rope_table", lib.tg_rope_table(
+        _dev(pos, "pos", torch.int32), Kt, int(d), float(rope_theta),
+        _dev(out, "out", torch.float32), _stream(stream)))
+    return out
+
+
+def tg_qkv_rope(x: torch.Tensor, w_qkv: torch.Tensor, rope_table: torch.Tensor, Hq: int, Hkv: int,
+                d: int, out: Optional[torch.Tensor] = None, stream=None):
+    """Fused q/k/v projection of the rows of x [Kt, D], q and k rotated.
+
+    w_qkv [(Hq + 2 Hkv) d, D] (q heads, k heads, v heads); rope_table from
+    tg_rope_table.  Returns (qkv [Kt, (Hq + 2 Hkv) d], q [Kt, Hq, d],
+    k [Kt, Hkv, d], v [Kt, Hkv, d]), the last three views into qkv.
+    """
+    _require_gpu()
+    lib = load_library()
+    if x.dim() != 2 or x.stride(1) != 1:
+        raise ValueError("x must be [Kt, D] with unit column stride")
+    Kt, D = x.shape
+    N = (Hq + 2 * Hkv) * d
+    if tuple(w_qkv.shape) != (N, D) or not w_qkv.is_contiguous() or w_qkv.dtype != x.dtype:
+        raise ValueError(f"w_qkv must be packed [{N}, {D}] of the dtype of x")
+    if tuple(rope_table.shape) != (Kt, d // 2, 2) or not rope_table.is_contiguous():
+        raise ValueError(f"rope_table has shape {tuple(rope_table.shape)}")
+    if out is None:
+        out = torch.empty((Kt, N), dtype=x.dtype, device=x.device)
+    elif out.dim() != 2 or out.shape[0] != Kt or out.shape[1] < N or out.stride(1) != 1:
+        raise ValueError(f"out has shape {tuple(out.shape)}")
+    if out.dtype != x.dtype:
+        raise TypeError("out must have the dtype of x")
+    _check("tg_qkv_rope", lib.tg_qkv_rope(
+        _dev(x, "x"), x.stride(0) if Kt else D, Kt, D, _dev(w_qkv, "w_qkv"),
+        _dev(rope_table, "rope_table", torch.float32), int(Hq), int(Hkv), int(d),
+        _dtype_code(x), _dev(out, "out"), out.stride(0) if Kt else N, _stream(stream)))
+    q = out[:, :Hq * d].unflatten(1, (Hq, d))
+    k = out[:, Hq * d:(Hq + Hkv) * d].unflatten(1, (Hkv, d))
+    v = out[:, (Hq + Hkv) * d:N].unflatten(1, (Hkv, d))
+    return out, q, k, v

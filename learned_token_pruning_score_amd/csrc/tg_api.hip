@@ -197,4 +197,49 @@ int tg_gated_attn_fwd(const void* q, const void* k, const void* v, int64_t q_tok
                                       as_stream(stream)));
 }
 
+int tg_rope_table(const int32_t* pos, int64_t Kt, int d, double rope_theta, float* table,
+                  void* stream) {
+  if (Kt < 0 || Kt > INT32_MAX || d <= 0 || d % 2 != 0) return TG_ERR_SHAPE;
+  if (!isfinite(rope_theta) || !(rope_theta > 1.0)) return TG_ERR_RANGE;
+  if (d != 64 && d != 128) return TG_ERR_UNSUPPORTED;
+  if (Kt == 0) return TG_OK;
+  if (!pos || !table) return TG_ERR_NULL;
+  if (!aligned16(table)) return TG_ERR_ALIGN;
+  return from_hip(tg::launch_rope_table(pos, Kt, d, rope_theta, table, as_stream(stream)));
+}
+
+int tg_qkv_rope(const void* x, int64_t ld_x, int64_t Kt, int D, const void* w_qkv,
+                const float* rope_table, int Hq, int Hkv, int d, int dtype, void* qkv,
+                int64_t ld_qkv, void* stream) {
+  const int eb = elem_bytes(dtype);
+  if (!eb) return TG_ERR_DTYPE;
+  if (Kt < 0 || Kt > INT32_MAX || D <= 0 || ld_x < D || Hq <= 0 || Hkv <= 0 || d <= 0)
+    return TG_ERR_SHAPE;
+  const int64_t N = ((int64_t)Hq + 2 * (int64_t)Hkv) * d;
+  if (N > INT32_MAX / 2 || ld_qkv < N) return TG_ERR_SHAPE;
+  if (d != 64 && d != 128) return TG_ERR_UNSUPPORTED;
+  if (dtype == TG_BF16) {
+    if (D % 64 != 0) return TG_ERR_UNSUPPORTED;
+    // a 256-row stage of x or W_qkv is addressed with 32-bit byte offsets;
+    // tiles are counted in int
+    if (ld_x >= (1 << 22) || D >= (1 << 22)) return TG_ERR_UNSUPPORTED;
+    if (((Kt + 255) / 256) * ((N + 255) / 256) > INT32_MAX) return TG_ERR_UNSUPPORTED;
+  } else if (Kt * N > INT32_MAX) {
+    return TG_ERR_UNSUPPORTED;  // one thread per output element
+  }
+  if (Kt == 0) return TG_OK;
+  if (!x || !w_qkv || !rope_table || !qkv) return TG_ERR_NULL;
+  if (!aligned16(rope_table)) return TG_ERR_ALIGN;
+  if (dtype == TG_BF16) {
+    if (!aligned16(x) || !aligned16(w_qkv) || !aligned16(qkv) || (ld_x * 2) % 16 != 0 ||
+        (ld_qkv * 2) % 16 != 0)
+      return TG_ERR_ALIGN;
+    return from_hip(tg::launch_qkv_rope_bf16(x, ld_x, Kt, D, w_qkv, rope_table, Hq, Hkv, d, qkv,
+                                             ld_qkv, as_stream(stream)));
+  }
+  return from_hip(tg::launch_qkv_rope_f32(static_cast<const float*>(x), ld_x, Kt, D,
+                                          static_cast<const float*>(w_qkv), rope_table, Hq, Hkv,
+                                          d, static_cast<float*>(qkv), ld_qkv, as_stream(stream)));
+}
+
 }  // extern "C"

@@ -72,4 +72,13 @@ hipError_t launch_attn_f32(const float* q, const float* k, const float* v, int64
                            const int32_t* cu_kept, int B, int max_len, int64_t Kt, int Hq,
                            int Hkv, int d, float* out, float* lse, hipStream_t s);
 
+hipError_t launch_rope_table(const int32_t* pos, int64_t n, int d, double theta, float* table,
+                             hipStream_t s);
+hipError_t launch_qkv_rope_bf16(const void* x, int64_t ld, int64_t Kt, int D, const void* W,
+                                const float* rope, int Hq, int Hkv, int d, void* out,
+                                int64_t ld_out, hipStream_t s);
+hipError_t launch_qkv_rope_f32(const float* x, int64_t ld, int64_t Kt, int D, const float* W,
+                               const float* rope, int Hq, int Hkv, int d, float* out,
+                               int64_t ld_out, hipStream_t s);
+
 }  // namespace tg

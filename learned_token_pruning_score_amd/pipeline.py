@@ -5,8 +5,10 @@ The TokenGate article ("How does TokenGate learned token pruning work?")
 splits prefill into a standard forward below the gate layer, the gate module
 (score every token, keep the top-K document tokens and the whole question),
 and a pruned forward over the kept tokens whose attention carries the score
-bias ("What is token-gated attention?").  This class runs the gate module
-and the pruned attention; the layers' projections are not part of it.
+bias ("What is token-gated attention?").  This class runs the gate module,
+the rotary table of the kept rows' original positions, a pruned layer's
+fused q/k/v projection with the rotary embedding, and its token-gated
+attention; the output projection and the MLP are not part of it.
 The kept count is known on the host from the metadata (``tg_plan``), so no
 step waits on the device.
 """
@@ -49,6 +51,7 @@ class GatedPrefill:
         self.pos_k = torch.empty(self.Kt, **i32)
         self.bias_s = torch.empty(self.Kt, dtype=torch.float32, device=dev)
         self.kept_idx = torch.empty(self.Kt, **i32) if with_index else None
+        self.rope_table = None
         self.ws_select = torch.empty(max(16, _lib.tg_select_topk_workspace(self.B, self.T)),
                                      dtype=torch.uint8, device=dev)
         self.ws_compact = torch.empty(max(16, _lib.tg_compact_workspace(self.B, self.T)),
@@ -65,6 +68,23 @@ class GatedPrefill:
                         self.doc_end, self.Kt,
                         out=(self.hidden_k, self.pos_k, self.bias_s, self.kept_idx),
                         workspace=self.ws_compact, stream=stream)
+
+    def rope(self, d: int, rope_theta: float, stream=None) -> torch.Tensor:
+        """cos / sin table of the kept rows' original positions (after
+        gate_and_select; shared by every pruned layer of the forward)."""
+        if getattr(self, "rope_table", None) is None or self.rope_table.shape[1] != d // 2:
+            self.rope_table = torch.empty((self.Kt, d // 2, 2), dtype=torch.float32,
+                                          device=self.device)
+        return _lib.tg_rope_table(self.pos_k, d, rope_theta, out=self.rope_table, stream=stream)
+
+    def project_qkv(self, w_qkv: torch.Tensor, Hq: int, Hkv: int, d: int,
+                    out: Optional[torch.Tensor] = None, stream=None):
+        """q, k, v of a pruned layer from the kept rows (after rope()).
+
+        Returns (qkv, q, k, v) as tg_qkv_rope does; q, k and v feed attend()
+        in place."""
+        return _lib.tg_qkv_rope(self.hidden_k, w_qkv, self.rope_table, Hq, Hkv, d, out=out,
+                                stream=stream)
 
     def attend(self, q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, gain: torch.Tensor,
                tau: float, out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None,

@@ -1,7 +1,7 @@
 """Seeded synthetic inputs for the TokenGate gated-prefill path.
 
 This package only draws random numbers and lays them out. It holds none of the
-method's arithmetic (no scoring, selection, compaction or attention) and is the
+method's arithmetic (no scoring, selection, compaction, projection or attention) and is the
 one module that both the oracle-side tests and the HIP-side callers share.
 """
 
@@ -13,6 +13,7 @@ from .workloads import (  # noqa: F401
     attention_inputs,
     dense_attention_inputs,
     make_workload,
+    qkv_weights,
     spec,
     with_overrides,
 )

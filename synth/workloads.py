@@ -33,6 +33,7 @@ _S_NEEDLE = 1
 _S_HIDDEN = 2
 _S_GATE = 3
 _S_LAYER0 = 10
+_S_QKV0 = 50
 _S_DENSE = 99
 
 
@@ -63,6 +64,7 @@ class WorkloadSpec:
     ragged_divs: Tuple[int, ...] = ()
     dense_comparator: bool = False
     b2: float = 0.0
+    rope_theta: float = 1e6  # rotary base of the Qwen3 family
 
 
 # The five workloads of the gated-prefill benchmark, plus small extra parity
@@ -270,6 +272,20 @@ def attention_inputs(which, layer: int, n_tokens: int, seed: int = 0):
     k = g.standard_normal((n_tokens, s.Hkv, s.d), dtype=np.float32)
     v = g.standard_normal((n_tokens, s.Hkv, s.d), dtype=np.float32)
     return _round(q, s.dtype), _round(k, s.dtype), _round(v, s.dtype), torch.from_numpy(gain)
+
+
+def qkv_weights(which, layer: int, seed: int = 0) -> torch.Tensor:
+    """Fused q/k/v projection weight of pruned layer ``layer``.
+
+    W_qkv [(Hq + 2 Hkv) d, D] in the spec dtype, rows: the q heads, then the
+    k heads, then the v heads; entries N(0, 1/D), so projected values of
+    N(0, 1) rows are about N(0, 1).
+    """
+    s = spec(which)
+    g = _rng(seed, _S_QKV0 + int(layer))
+    n = (s.Hq + 2 * s.Hkv) * s.d
+    w = g.standard_normal((n, s.D), dtype=np.float32) * np.float32(1.0 / np.sqrt(s.D))
+    return _round(w, s.dtype)
 
 
 def dense_attention_inputs(which, n_tokens: int, seed: int = 0):

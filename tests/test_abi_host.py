@@ -34,7 +34,7 @@ def _declared():
 def test_every_declared_symbol_is_exported_and_typed():
     lib = tg.load_library()
     names = _declared()
-    assert "tg_gated_attn_fwd" in names and len(names) == 9
+    assert "tg_gated_attn_fwd" in names and "tg_qkv_rope" in names and len(names) == 11
     for n in names:
         assert hasattr(lib, n), n
     assert set(names) == set(tg.SIGNATURES)
@@ -181,3 +181,44 @@ def test_attention_argument_checks():
     assert call(B=65536, Kt=70000, maxlen=100) == TG_ERR_UNSUPPORTED
     assert call(Kt=65536 * 256 + 1, maxlen=65536 * 256 + 1) == TG_ERR_UNSUPPORTED
     assert call(dtype=0, Hq=65536, Hkv=1, qs=65536 * 128) == TG_ERR_UNSUPPORTED
+
+
+def test_rope_table_and_qkv_argument_checks():
+    lib = tg.load_library()
+    r = lib.tg_rope_table
+    # (pos, Kt, d, theta, table, stream)
+    assert r(FAKE, -1, 128, 1e6, FAKE, None) == TG_ERR_SHAPE
+    assert r(FAKE, 10, 127, 1e6, FAKE, None) == TG_ERR_SHAPE
+    assert r(FAKE, 10, 128, float("nan"), FAKE, None) == TG_ERR_RANGE
+    assert r(FAKE, 10, 128, 1.0, FAKE, None) == TG_ERR_RANGE
+    assert r(FAKE, 10, 96, 1e6, FAKE, None) == TG_ERR_UNSUPPORTED
+    assert r(None, 10, 128, 1e6, FAKE, None) == TG_ERR_NULL
+    assert r(FAKE, 10, 128, 1e6, FAKE + 8, None) == TG_ERR_ALIGN
+    assert r(None, 0, 128, 1e6, None, None) == TG_OK  # empty: no device work
+
+    q = lib.tg_qkv_rope
+    # (x, ld_x, Kt, D, w, table, Hq, Hkv, d, dtype, qkv, ld_qkv, stream)
+    base = [FAKE, 2048, 100, 2048, FAKE, FAKE, 16, 8, 128, 1, FAKE, 4096, None]
+    names = ["x", "ld_x", "Kt", "D", "w", "table", "Hq", "Hkv", "d", "dtype", "qkv", "ld_qkv",
+             "stream"]
+
+    def call(**kw):
+        a = list(base)
+        for k, v in kw.items():
+            a[names.index(k)] = v
+        return q(*a)
+
+    assert call(dtype=5) == TG_ERR_DTYPE
+    assert call(ld_x=2000) == TG_ERR_SHAPE
+    assert call(ld_qkv=4095) == TG_ERR_SHAPE
+    assert call(Hkv=0) == TG_ERR_SHAPE and call(Kt=-1) == TG_ERR_SHAPE
+    assert call(d=96, ld_qkv=4096) == TG_ERR_UNSUPPORTED
+    assert call(D=1000, ld_x=1000) == TG_ERR_UNSUPPORTED  # bf16: D % 64
+    assert call(ld_x=1 << 22) == TG_ERR_UNSUPPORTED  # 32-bit stage offsets
+    assert call(dtype=0, Kt=1 << 20) == TG_ERR_UNSUPPORTED  # fp32: one thread per output
+    assert call(x=None) == TG_ERR_NULL and call(table=None) == TG_ERR_NULL
+    assert call(qkv=None) == TG_ERR_NULL and call(w=None) == TG_ERR_NULL
+    assert call(x=FAKE + 2) == TG_ERR_ALIGN and call(table=FAKE + 4) == TG_ERR_ALIGN
+    assert call(ld_x=2052) == TG_ERR_ALIGN and call(ld_qkv=4100) == TG_ERR_ALIGN
+    assert call(Kt=0, x=None, w=None, table=None, qkv=None) == TG_OK  # empty: no device work
+
