@@ -275,6 +275,184 @@ __global__ __launch_bounds__(512, 1) void qkv_rope_bf16_kernel(
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 }
 
+// Tail of the bf16 projection: tiles left over after the last full round of
+// the main kernel (at most a quarter of the CUs' worth) would run one per CU
+// while the rest of the chip idles, so each is cut into 16 sub-tiles of 64
+// rows x one rotation pair of 32-column blocks (blocks fb and fb + d/64 of a
+// head), one workgroup each.  The 4 waves of a workgroup split D into
+// quarters; each streams its quarter of the pair's 64 W_qkv rows and the 64
+// rows of x through its own two LDS stages of 64 columns (buffer-to-LDS
+// loads, 8 rows per instruction) and reads MFMA fragments from there.  The
+// four partial sums meet in LDS and are added in wave order
+// (bit-reproducible), then rotated and stored as in the main kernel.  The
+// four workgroups that share a pair's W_qkv rows sit on one XCD (workgroup
+// ids 8 apart), so those rows are fetched into one L2.
+template <int HD>
+__global__ __launch_bounds__(256) void qkv_rope_tail_kernel(
+    const uint16_t* __restrict__ x, int64_t ld, int64_t Kt, int D,
+    const uint16_t* __restrict__ W, int N, int rot_cols, int n_nt, int first_tile, int n_groups,
+    const float2* __restrict__ rope, uint16_t* __restrict__ out, int64_t ld_out) {
+  constexpr int BPH = HD / 32;
+  constexpr int P = BPH / 2;
+  constexpr int SB = 128 * 128;  // one wave's stage: 128 rows (2 W blocks, 2 x blocks) x 64 columns
+  __shared__ __attribute__((aligned(16))) char st0[4][SB], st1[4][SB];
+
+  // sub-tile s = xcd + 8 (tq + 4 g2): row quarter tq of (tile, pair) group xcd + 8 g2
+  const int sidx = blockIdx.x;
+  const int tq = (sidx >> 3) & 3;
+  const int grp = (sidx & 7) + 8 * (sidx >> 5);
+  if (grp >= n_groups) return;
+  const int tile = first_tile + grp / 4;
+  const int pr = grp % 4;
+  const int mt = tile / n_nt;
+  const int nt = tile - mt * n_nt;
+  const int fb0 = HD == 128 ? (pr >> 1) * 4 + (pr & 1) : 2 * pr;
+  const int f0 = nt * kQkvBN + 32 * fb0;  // first column of the pair's first block
+  const int f1 = f0 + 32 * P;
+  if (f0 >= N) return;  // heads are whole: the pair lies entirely past N
+  const int64_t t0 = (int64_t)mt * kQkvBM + 64 * tq;
+  if (t0 >= Kt) return;
+
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int rows = (int)min((int64_t)64, Kt - t0);
+  const int kq = D / 4;            // this wave's columns [kb, kb + kq), a multiple of 16
+  const int kb = wave * kq;
+  const int nst = (kq + 63) / 64;  // stages of 64 columns; k-steps past kq are skipped
+
+  // DMA j of a stage fills staged rows 8 j .. 8 j + 7: rows 0-31 are W_qkv
+  // rows f0 + r, 32-63 rows f1 + r - 32, 64-127 rows t0 + r - 64 of x.
+  // Lane l writes position l % 8 of row 8 j + l / 8, which holds logical
+  // chunk (l % 8) ^ ((row >> 1) & 7) of the row's 64 columns.
+  int voff[16];
+#pragma unroll
+  for (int j = 0; j < 16; ++j) {
+    const int row = 8 * j + (lane >> 3);
+    const int c = (lane & 7) ^ ((row >> 1) & 7);
+    if (j < 4) voff[j] = (row * D + c * 8) * 2;
+    else if (j < 8) voff[j] = ((32 * P + row - 32) * D + c * 8) * 2;
+    else voff[j] = ((row - 64) * (int)ld + c * 8) * 2;
+  }
+  // W_qkv rows f0 .. f1 + 31 and x rows t0 .. t0 + rows - 1 from column kb
+  // on; reads past the ranges (the last wave's partial stage, rows past Kt)
+  // give zeros.
+  auto issue = [&](char* buf, int st) __attribute__((always_inline)) {
+    const int k0 = kb + 64 * st;
+    const int wr = __builtin_amdgcn_readfirstlane((32 * P + 32) * D * 2 - k0 * 2);
+    const int xr = __builtin_amdgcn_readfirstlane(rows * (int)ld * 2 - k0 * 2);
+    const __amdgpu_buffer_rsrc_t rw = __builtin_amdgcn_make_buffer_rsrc((void*)(W + (int64_t)f0 * D + k0), (short)0, wr, kBufFlags);
+    const __amdgpu_buffer_rsrc_t rx = __builtin_amdgcn_make_buffer_rsrc((void*)(x + t0 * ld + k0), (short)0, xr, kBufFlags);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) qkv_lds_load16(rw, buf + 1024 * j, voff[j]);
+#pragma unroll
+    for (int j = 8; j < 16; ++j) qkv_lds_load16(rx, buf + 1024 * j, voff[j]);
+  };
+
+  f32x16 acc[2][2];
+#pragma unroll
+  for (int a = 0; a < 2; ++a)
+#pragma unroll
+    for (int b = 0; b < 2; ++b)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) acc[a][b][i] = 0.0f;
+  // fragment of staged block q (0, 1: W_qkv; 2, 3: x), k-step ks
+  const int r = lane & 31;
+  auto compute = [&](const char* buf, int st) __attribute__((always_inline)) {
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+      if (64 * st + 16 * ks < kq) {
+        const int c = 2 * ks + (lane >> 5);
+        bf16x8 f[4];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int row = 32 * q + r;
+          f[q] = *reinterpret_cast<const bf16x8*>(buf + row * 128 + ((c ^ ((row >> 1) & 7)) * 16));
+        }
+        acc[0][0] = mfma32x32x16(f[0], f[2], acc[0][0]);
+        acc[0][1] = mfma32x32x16(f[0], f[3], acc[0][1]);
+        acc[1][0] = mfma32x32x16(f[1], f[2], acc[1][0]);
+        acc[1][1] = mfma32x32x16(f[1], f[3], acc[1][1]);
+      }
+    }
+  };
+  char* b0 = st0[wave];
+  char* b1 = st1[wave];
+  issue(b0, 0);
+  if (nst > 1) issue(b1, 1);
+  for (int st = 0; st < nst; st += 2) {
+    compute(b0, st);
+    if (st + 2 < nst) {
+      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // reads of b0 done before it is refilled
+      issue(b0, st + 2);
+    }
+    if (st + 1 < nst) {
+      compute(b1, st + 1);
+      if (st + 3 < nst) {
+        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+        issue(b1, st + 3);
+      }
+    }
+  }
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  __syncthreads();  // every wave is done with its stages: st0 now holds the partial sums
+  float* red = reinterpret_cast<float*>(&st0[0][0]);  // [3][4][16][64]
+  if (wave > 0) {
+#pragma unroll
+    for (int a = 0; a < 2; ++a)
+#pragma unroll
+      for (int b = 0; b < 2; ++b)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) red[(((wave - 1) * 4 + 2 * a + b) * 16 + i) * 64 + lane] = acc[a][b][i];
+  }
+  __syncthreads();
+  if (wave > 0) return;
+#pragma unroll
+  for (int w = 0; w < 3; ++w)
+#pragma unroll
+    for (int a = 0; a < 2; ++a)
+#pragma unroll
+      for (int b = 0; b < 2; ++b)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) acc[a][b][i] += red[((w * 4 + 2 * a + b) * 16 + i) * 64 + lane];
+
+  const int hf = 4 * (lane >> 5);
+  const bool rot = f0 < rot_cols;
+#pragma unroll
+  for (int b = 0; b < 2; ++b) {
+    const int64_t t = t0 + 32 * b + r;
+    if (rot) {
+      const int64_t tl = t < Kt ? t : Kt - 1;
+      const float4* rr = reinterpret_cast<const float4*>(rope + tl * (HD / 2) + 32 * (fb0 % BPH) + hf);
+#pragma unroll
+      for (int i4 = 0; i4 < 4; ++i4) {
+        const float4 u0 = rr[4 * i4], u1 = rr[4 * i4 + 1];
+        const float cs[4] = {u0.x, u0.z, u1.x, u1.z}, sn[4] = {u0.y, u0.w, u1.y, u1.w};
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+          const float av = acc[0][b][4 * i4 + c], bv = acc[1][b][4 * i4 + c];
+          acc[0][b][4 * i4 + c] = av * cs[c] - bv * sn[c];
+          acc[1][b][4 * i4 + c] = bv * cs[c] + av * sn[c];
+        }
+      }
+    }
+    if (t < Kt) {
+#pragma unroll
+      for (int a = 0; a < 2; ++a) {
+        uint16_t* orow = out + t * ld_out + (a ? f1 : f0) + hf;
+#pragma unroll
+        for (int i4 = 0; i4 < 4; ++i4) {
+          const __bf16 e0 = (__bf16)acc[a][b][4 * i4 + 0], e1 = (__bf16)acc[a][b][4 * i4 + 1];
+          const __bf16 e2 = (__bf16)acc[a][b][4 * i4 + 2], e3 = (__bf16)acc[a][b][4 * i4 + 3];
+          uint2 pk;
+          pk.x = (uint32_t)__builtin_bit_cast(uint16_t, e0) | ((uint32_t)__builtin_bit_cast(uint16_t, e1) << 16);
+          pk.y = (uint32_t)__builtin_bit_cast(uint16_t, e2) | ((uint32_t)__builtin_bit_cast(uint16_t, e3) << 16);
+          *reinterpret_cast<uint2*>(orow + 8 * i4) = pk;
+        }
+      }
+    }
+  }
+}
+
 // fp32 path: one thread per output element; the dot products over D run
 // sequentially in fp32, a rotated element also forms its partner's.
 __global__ __launch_bounds__(256) void qkv_rope_f32_kernel(
@@ -333,19 +511,38 @@ hipError_t launch_qkv_rope_bf16(const void* x, int64_t ld, int64_t Kt, int D, co
   const int n_mt = (int)((Kt + kQkvBM - 1) / kQkvBM);
   const int n_nt = (N + kQkvBN - 1) / kQkvBN;
   const int n_tiles = n_mt * n_nt;
-  const dim3 grid((unsigned)min(n_tiles, n_cu));
+  if (d != 128 && d != 64) return hipErrorInvalidValue;
+  // Tiles past the last full round of one tile per CU go to the sub-tile
+  // kernel when there are few of them (at most a quarter of the CUs).
+  const int left = n_tiles % n_cu;
+  const int main_tiles = (left > 0 && left <= n_cu / 4) ? n_tiles - left : n_tiles;
   const auto* xp = static_cast<const uint16_t*>(x);
   const auto* wp = static_cast<const uint16_t*>(W);
   const auto* rp = reinterpret_cast<const float2*>(rope);
   auto* op = static_cast<uint16_t*>(out);
-  if (d == 128)
-    hipLaunchKernelGGL((qkv_rope_bf16_kernel<128>), grid, dim3(512), 0, s, xp, ld, Kt, D, wp, N,
-                       rot_cols, n_nt, n_tiles, rp, op, ld_out);
-  else if (d == 64)
-    hipLaunchKernelGGL((qkv_rope_bf16_kernel<64>), grid, dim3(512), 0, s, xp, ld, Kt, D, wp, N,
-                       rot_cols, n_nt, n_tiles, rp, op, ld_out);
-  else
-    return hipErrorInvalidValue;
+  if (main_tiles > 0) {
+    const dim3 grid((unsigned)min(main_tiles, n_cu));
+    if (d == 128)
+      hipLaunchKernelGGL((qkv_rope_bf16_kernel<128>), grid, dim3(512), 0, s, xp, ld, Kt, D, wp, N,
+                         rot_cols, n_nt, main_tiles, rp, op, ld_out);
+    else
+      hipLaunchKernelGGL((qkv_rope_bf16_kernel<64>), grid, dim3(512), 0, s, xp, ld, Kt, D, wp, N,
+                         rot_cols, n_nt, main_tiles, rp, op, ld_out);
+    const hipError_t e1 = hipGetLastError();
+    if (e1 != hipSuccess) return e1;
+  }
+  if (main_tiles < n_tiles) {
+    // 4 (tile, pair) groups per tile, 4 row quarters each; ids are laid out
+    // in blocks of 32 (8 groups x 4 quarters), the last block padded
+    const int n_groups = (n_tiles - main_tiles) * 4;
+    const dim3 grid((unsigned)((n_groups + 7) / 8 * 32));
+    if (d == 128)
+      hipLaunchKernelGGL((qkv_rope_tail_kernel<128>), grid, dim3(256), 0, s, xp, ld, Kt, D, wp, N,
+                         rot_cols, n_nt, main_tiles, n_groups, rp, op, ld_out);
+    else
+      hipLaunchKernelGGL((qkv_rope_tail_kernel<64>), grid, dim3(256), 0, s, xp, ld, Kt, D, wp, N,
+                         rot_cols, n_nt, main_tiles, n_groups, rp, op, ld_out);
+  }
   return hipGetLastError();
 }
 

@@ -138,6 +138,25 @@ def test_qkv_rope_bf16(shape):
     assert torch.equal(qkv2, qkv)
 
 
+# With 256 CUs: 128 tiles of 256 x 256 run as one launch of the tile kernel;
+# 272 tiles as one full round of it plus 16 tiles cut into 64-row sub-tiles
+# (the layout of the 128k kept rows: 528 tiles = two rounds + 16).  The
+# small shapes above (at most 64 tiles) run on sub-tiles alone.
+@pytest.mark.parametrize("Kt", [2000, 4352])
+def test_qkv_rope_bf16_tile_and_subtile_launches(Kt):
+    D, Hq, Hkv, d = 2048, 16, 8, 128
+    _note(f"[qkv bf16 launches] Kt={Kt}")
+    x, W, pos = _inputs(Kt, D, Hq, Hkv, d, torch.bfloat16, seed=Kt)
+    tab = tg.tg_rope_table(pos.to(DEV), d, THETA)
+    qkv, _, _, _ = tg.tg_qkv_rope(x.to(DEV), W.to(DEV), tab, Hq, Hkv, d)
+    torch.cuda.synchronize()
+    g = np.random.default_rng(Kt)
+    rows = np.unique(np.concatenate([[0, 255, 256, Kt - 257, Kt - 256, Kt - 1],
+                                     g.integers(0, Kt, 120), g.integers(Kt - 256, Kt, 40)]))
+    idx = torch.from_numpy(rows)
+    _check_qkv(qkv.cpu()[idx], x[idx], W, pos.numpy()[rows], Hq, Hkv, d, torch.bfloat16)
+
+
 @pytest.mark.parametrize("shape", [(50, 256, 4, 2, 64), (33, 128, 2, 1, 128), (1, 64, 1, 1, 64)])
 def test_qkv_rope_f32(shape):
     Kt, D, Hq, Hkv, d = shape
