@@ -19,9 +19,13 @@ from .tokengate import (  # noqa: F401
     compact,
     gate_scores,
     gated_attention,
+    linear_residual,
     plan,
+    pruned_layer,
     qkv_rope,
+    rms_norm,
     rope_inv_freq,
     round_f32,
     select_topk,
+    swiglu,
 )

@@ -264,3 +264,58 @@ def qkv_rope(hidden, W, pos, theta: float, Hq: int, Hkv: int, d: int):
     k = y[:, Hq * d:(Hq + Hkv) * d].reshape(n, Hkv, d)
     v = y[:, (Hq + Hkv) * d:].reshape(n, Hkv, d)
     return apply_rope(q, pos, theta), apply_rope(k, pos, theta), v
+
+
+def rms_norm(x, weight, eps: float) -> np.ndarray:
+    """RMSNorm of every row: ``y = weight * x / sqrt(mean(x^2) + eps)``.
+
+    Article, "How does TokenGate learned token pruning work?": the layers
+    above the gate run on the kept tokens.  Reading (the article names
+    Qwen3-1.7B as the model but not its layer): a pre-norm layer of the
+    Qwen3 family, with an RMSNorm (per-channel weight, eps 1e-6 there)
+    before the attention and before the MLP.
+    """
+    x = _f64(x)
+    ms = np.mean(x * x, axis=-1, keepdims=True)
+    return _f64(weight) * x / np.sqrt(ms + float(eps))
+
+
+def linear_residual(a, W, residual) -> np.ndarray:
+    """``residual + a @ W.T``: the attention output projection (a = the
+    heads' outputs [n, Hq d], W [D, Hq d]) and the MLP's down projection
+    (a = the SwiGLU activation [n, I], W [D, I]), each added to the
+    residual stream.  Reading as for rms_norm; no bias."""
+    return _f64(residual) + _f64(a) @ _f64(W).T
+
+
+def swiglu(h, W_gate, W_up) -> np.ndarray:
+    """SwiGLU activation of the MLP: ``silu(h W_gate^T) * (h W_up^T)`` with
+    ``silu(z) = z / (1 + exp(-z))``; W_gate and W_up [I, D].  Reading as for
+    rms_norm (the Qwen3 MLP), no bias."""
+    g = _f64(h) @ _f64(W_gate).T
+    u = _f64(h) @ _f64(W_up).T
+    return g / (1.0 + np.exp(-g)) * u
+
+
+def pruned_layer(x, pos, cu_kept, bias, gain, tau: float, theta: float, eps: float,
+                 w_in, W_qkv, Hq: int, Hkv: int, d: int, W_o, w_post, W_gate, W_up, W_down,
+                 rows=None) -> np.ndarray:
+    """One transformer layer above the gate, on the kept rows only.
+
+    Article, "How does TokenGate learned token pruning work?": the layers
+    above the gate see only the kept tokens, at their original positions;
+    "What is token-gated attention?": their attention carries the gate's
+    score bias.  Reading: the pre-norm layer
+        a = x + O(attention(rope(QKV(rms_norm(x)))))
+        y = a + Down(swiglu(rms_norm(a)))
+    with the attention of ``gated_attention``.  ``rows`` limits the output
+    to some rows (the attention still sees every earlier key).
+    """
+    x = _f64(x)
+    n = x.shape[0]
+    q, k, v = qkv_rope(rms_norm(x, w_in, eps), W_qkv, pos, theta, Hq, Hkv, d)
+    o, _ = gated_attention(q, k, v, bias, gain, tau, cu_kept, rows=rows)
+    sel = np.arange(n) if rows is None else np.asarray(rows)
+    a = linear_residual(o[sel].reshape(len(sel), Hq * d), W_o, x[sel])
+    return linear_residual(swiglu(rms_norm(a, w_post, eps), W_gate, W_up), W_down, a)
+

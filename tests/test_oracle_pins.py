@@ -468,3 +468,136 @@ def test_qkv_projection_brute_force():
     assert np.array_equal(v2, v)
     assert np.max(np.abs(q2 - oracle.apply_rope(q, pos, 1.0e6))) <= 1e-12
     assert np.max(np.abs(k2 - oracle.apply_rope(k, pos, 1.0e6))) <= 1e-12
+
+
+# ------------------------------------------------ the rest of a pruned layer
+# (slips each caught here: a mean instead of a mean of squares, eps outside
+# the root, the norm weight missing, sigmoid instead of SiLU, gate and up
+# swapped, a missing residual, a transposed weight, a norm in the wrong place
+# of the layer, the attention fed the un-normalised rows)
+
+def test_layer_hand_worked():
+    g = _load("layer_hand_worked.json")
+    r = g["rms_norm"]
+    for case in r["cases"]:
+        y = oracle.rms_norm(np.array([r["x"]]), np.array(r["weight"]), case["eps"])
+        assert np.max(np.abs(y[0] - np.array(case["y"]))) <= 1e-12
+    s = g["swiglu"]
+    a = oracle.swiglu(np.array(s["h"]), np.array(s["W_gate"]), np.array(s["W_up"]))
+    assert np.max(np.abs(a - np.array(s["a"]))) <= 1e-12
+    lr = g["linear_residual"]
+    out = oracle.linear_residual(np.array(lr["a"]), np.array(lr["W"]), np.array(lr["residual"]))
+    assert np.max(np.abs(out - np.array(lr["out"]))) <= 1e-12
+
+
+def test_rms_norm_library_and_invariants():
+    rng = np.random.default_rng(21)
+    x = rng.standard_normal((7, 48)) * rng.uniform(0.1, 10.0, (7, 1))
+    w = rng.standard_normal(48)
+    for eps in (0.0, 1e-6, 0.3):
+        lib = F.rms_norm(torch.from_numpy(x), (48,), torch.from_numpy(w), eps).numpy()
+        assert np.max(np.abs(oracle.rms_norm(x, w, eps) - lib)) <= 1e-12
+    y = oracle.rms_norm(x, np.ones(48), 0.0)
+    assert np.allclose(np.mean(y * y, axis=-1), 1.0, rtol=0, atol=1e-12)
+    assert np.allclose(oracle.rms_norm(3.5 * x, w, 0.0), oracle.rms_norm(x, w, 0.0), rtol=1e-12, atol=1e-12)
+    c = np.full((1, 48), -2.0)
+    assert np.allclose(oracle.rms_norm(c, w, 0.5), w * -2.0 / math.sqrt(4.5), rtol=1e-14, atol=0)
+    assert np.array_equal(oracle.rms_norm(np.zeros((2, 48)), w, 1e-6), np.zeros((2, 48)))
+
+
+def test_swiglu_library_and_special_values():
+    rng = np.random.default_rng(22)
+    h = rng.standard_normal((9, 16))
+    Wg = rng.standard_normal((24, 16))
+    Wu = rng.standard_normal((24, 16))
+    th = torch.from_numpy(h)
+    lib = (F.silu(F.linear(th, torch.from_numpy(Wg))) * F.linear(th, torch.from_numpy(Wu))).numpy()
+    assert np.max(np.abs(oracle.swiglu(h, Wg, Wu) - lib)) <= 1e-12
+    # silu(0) = 0, silu(z) - silu(-z) = z, silu(z) ~ z for large z and ~ 0 for very negative z
+    e = np.eye(1)
+    for z, exp in ((0.0, 0.0), (40.0, 40.0), (-40.0, 0.0)):
+        assert abs(oracle.swiglu(e, np.array([[z]]), np.array([[1.0]]))[0, 0] - exp) <= 1e-12
+    z = np.linspace(-6, 6, 13)[:, None]
+    diff = oracle.swiglu(e, z, np.ones_like(z)) - oracle.swiglu(e, -z, np.ones_like(z))
+    assert np.allclose(diff[0], z[:, 0], rtol=0, atol=1e-12)
+
+
+def test_linear_residual_brute_force():
+    rng = np.random.default_rng(23)
+    n, K, D = 3, 5, 4
+    a = rng.standard_normal((n, K))
+    W = rng.standard_normal((D, K))
+    r = rng.standard_normal((n, D))
+    exp = [[r[i][o] + sum(a[i][c] * W[o][c] for c in range(K)) for o in range(D)] for i in range(n)]
+    assert np.max(np.abs(oracle.linear_residual(a, W, r) - np.array(exp))) <= 1e-12
+    assert np.array_equal(oracle.linear_residual(a, np.zeros((D, K)), r), r)
+
+
+def _layer_brute_force(x, pos, cu, bias, gain, tau, theta, eps, w_in, Wqkv, d, Wo, w_post, Wg, Wu, Wd):
+    """One pruned layer with one q head and one kv head, in plain loops."""
+    n, D = len(x), len(x[0])
+
+    def norm(row, w):
+        ms = sum(v * v for v in row) / len(row)
+        return [w[c] * row[c] / math.sqrt(ms + eps) for c in range(len(row))]
+
+    def mat(row, M):
+        return [sum(M[o][c] * row[c] for c in range(len(row))) for o in range(len(M))]
+
+    def rot(vec, p):
+        h = d // 2
+        out = list(vec)
+        for i in range(h):
+            ang = p * theta ** (-2.0 * i / d)
+            out[i] = vec[i] * math.cos(ang) - vec[i + h] * math.sin(ang)
+            out[i + h] = vec[i + h] * math.cos(ang) + vec[i] * math.sin(ang)
+        return out
+
+    qs, ks, vs = [], [], []
+    for t in range(n):
+        y = mat(norm(x[t], w_in), Wqkv)
+        qs.append(rot(y[:d], pos[t]))
+        ks.append(rot(y[d:2 * d], pos[t]))
+        vs.append(y[2 * d:])
+    out = []
+    for i in range(n):
+        b = max(bb for bb in range(len(cu) - 1) if cu[bb] <= i)
+        js = range(cu[b], i + 1)
+        lg = [tau * sum(qs[i][c] * ks[j][c] for c in range(d)) / math.sqrt(d) + gain * bias[j] for j in js]
+        m = max(lg)
+        p = [math.exp(v - m) for v in lg]
+        o = [sum(p[jj] * vs[j][c] for jj, j in enumerate(js)) / sum(p) for c in range(d)]
+        a = [x[i][c] + v for c, v in enumerate(mat(o, Wo))]
+        hn = norm(a, w_post)
+        g, u = mat(hn, Wg), mat(hn, Wu)
+        act = [g[j] / (1 + math.exp(-g[j])) * u[j] for j in range(len(g))]
+        out.append([a[c] + v for c, v in enumerate(mat(act, Wd))])
+    return np.array(out)
+
+
+def test_pruned_layer_brute_force_and_residual_paths():
+    rng = np.random.default_rng(24)
+    n, D, d, I = 6, 4, 2, 3
+    cu = [0, 4, 6]
+    x = rng.standard_normal((n, D))
+    pos = np.array([0, 3, 9, 20, 0, 5])
+    bias = np.array([0.5, -1.0, 0.0, 2.0, 0.0, 1.5])
+    gain, tau, theta, eps = 0.7, 1.15, 100.0, 1e-6
+    w_in, w_post = rng.uniform(0.5, 1.5, D), rng.uniform(0.5, 1.5, D)
+    Wqkv = rng.standard_normal((3 * d, D))
+    Wo = rng.standard_normal((D, d))
+    Wg, Wu = rng.standard_normal((I, D)), rng.standard_normal((I, D))
+    Wd = rng.standard_normal((D, I))
+    args = (x, pos, np.array(cu), bias, np.array([gain]), tau, theta, eps, w_in, Wqkv, 1, 1, d, Wo,
+            w_post, Wg, Wu, Wd)
+    y = oracle.pruned_layer(*args)
+    exp = _layer_brute_force(x.tolist(), pos.tolist(), cu, bias.tolist(), gain, tau, theta, eps,
+                             w_in.tolist(), Wqkv.tolist(), d, Wo.tolist(), w_post.tolist(),
+                             Wg.tolist(), Wu.tolist(), Wd.tolist())
+    assert np.max(np.abs(y - exp)) <= 1e-10
+    rows = [5, 1]
+    assert np.max(np.abs(oracle.pruned_layer(*args, rows=rows) - exp[rows])) <= 1e-10
+    # both sublayers switched off: the residual stream passes unchanged
+    z = list(args)
+    z[13], z[17] = np.zeros_like(Wo), np.zeros_like(Wd)
+    assert np.array_equal(oracle.pruned_layer(*z), x)
