@@ -123,9 +123,12 @@ def reference_points(tg, w, gp, layers, outs, hidden, W1, b1, w2, stream, dev):
         bias) at 32768 tokens with the same head shapes;
       * gate and attention launches after a 1 GiB write that evicts L2 and
         the last-level cache (the timed step runs them back to back);
-      * a pruned layer's input step, beside the step: the rotary table of
-        the kept rows' positions and the fused q/k/v projection of the kept
-        rows with the rotary embedding (seeded weights of the layer's shape);
+      * a whole pruned layer on the kept rows, beside the step (seeded
+        weights of the layer's shapes): the rotary table of the kept rows'
+        positions, and per layer RMSNorm, the fused q/k/v projection with the
+        rotary embedding, the gated attention, the output projection added to
+        the residual, RMSNorm, the SwiGLU gate/up projection and the down
+        projection added to the residual; each kernel timed alone too;
       * what the chip reaches here on plain library work: a bf16 GEMM of
         8192^3 and a 1 GiB device copy."""
     import torch
@@ -150,18 +153,40 @@ def reference_points(tg, w, gp, layers, outs, hidden, W1, b1, w2, stream, dev):
          "key_bias_cost_ratio": t_gated / t_plain}
 
     import synth
+    Kt, D, HD = gp.Kt, s.D, s.Hq * s.d
     Wqkv = synth.qkv_weights(s, 0, seed=0).to(dev)
+    lw = {k_: v_.to(dev) for k_, v_ in synth.layer_weights(s, 0, seed=0).items()}
+    I = lw["W_gate"].shape[0]
     nq = (s.Hq + 2 * s.Hkv) * s.d
-    qkv_buf = torch.empty((gp.Kt, nq), dtype=Wqkv.dtype, device=dev)
+    mk = lambda *shape: torch.empty(shape, dtype=Wqkv.dtype, device=dev)  # noqa: E731
+    xk, xn, qkv_buf, att, act = mk(Kt, D), mk(Kt, D), mk(Kt, nq), mk(Kt, HD), mk(Kt, I)
+    xk.copy_(gp.hidden_k)
+    xn.copy_(gp.hidden_k)
+    att.normal_()
+    act.normal_()
     rope = lambda: gp.rope(s.d, s.rope_theta)  # noqa: E731
-    proj = lambda: gp.project_qkv(Wqkv, s.Hq, s.Hkv, s.d, out=qkv_buf)  # noqa: E731
     rope()
-    proj()
     r["rope_table_us"] = time_launches(rope, stream, reps=7, n=5) * 1e3
-    t = time_launches(proj, stream, reps=7, n=5)
-    r["qkv_rope_us"] = t * 1e3
-    r["qkv_rope_TFLOPs"] = 2.0 * gp.Kt * s.D * nq / (t / 1e3) / 1e12
-    del Wqkv, qkv_buf
+    parts = {
+        "rms_norm": (lambda: tg.tg_rms_norm(xk, lw["w_in"], s.norm_eps, out=xn), 0.0),
+        "qkv_rope": (lambda: gp.project_qkv(Wqkv, s.Hq, s.Hkv, s.d, out=qkv_buf, x=xn), 2.0 * Kt * D * nq),
+        "o_proj": (lambda: tg.tg_linear_residual(att, lw["W_o"], xk, out=xn), 2.0 * Kt * HD * D),
+        "swiglu": (lambda: tg.tg_swiglu(xn, lw["W_gate"], lw["W_up"], out=act), 4.0 * Kt * D * I),
+        "down_proj": (lambda: tg.tg_linear_residual(act, lw["W_down"], xk, out=xn), 2.0 * Kt * I * D),
+    }
+    for name, (fn, flop) in parts.items():
+        fn()
+        t = time_launches(fn, stream, reps=7, n=5)
+        r[f"{name}_us"] = t * 1e3
+        if flop:
+            r[f"{name}_TFLOPs"] = flop / (t / 1e3) / 1e12
+    r["rms_norm_GBps"] = 2.0 * Kt * D * xk.element_size() / (r["rms_norm_us"] / 1e6) / 1e9
+    layer = lambda: gp.pruned_layer(Wqkv, lw, s.Hq, s.Hkv, s.d, gain, s.tau, s.norm_eps, x=xk)  # noqa: E731
+    layer()
+    t = time_launches(layer, stream, reps=5, n=3)
+    r["pruned_layer_us"] = t * 1e3
+    r["pruned_layer_TFLOPs"] = (2.0 * Kt * D * (nq + HD + 3 * I) + work["attn_flop_per_layer"]) / (t / 1e3) / 1e12
+    del Wqkv, lw, xk, xn, qkv_buf, att, act
 
     flush_buf = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
     flush = lambda: flush_buf.fill_(1)  # noqa: E731

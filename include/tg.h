@@ -22,6 +22,10 @@
  *                      original positions
  *   tg_qkv_rope        fused q/k/v projection of the kept rows, rotated at
  *                      their original positions (the pruned layers' input)
+ *   tg_rms_norm        RMSNorm of the kept rows (before attention and MLP)
+ *   tg_linear_residual projection added to the residual stream (attention
+ *                      output projection, MLP down projection)
+ *   tg_swiglu          the MLP's gate and up projections with SiLU(gate) * up
  *
  * Conventions (every call):
  *   - Pointers are device pointers unless the parameter name ends in _h
@@ -227,6 +231,51 @@ int tg_rope_table(const int32_t* pos, int64_t Kt, int d, double rope_theta, floa
 int tg_qkv_rope(const void* x, int64_t ld_x, int64_t Kt, int D, const void* w_qkv,
                 const float* rope_table, int Hq, int Hkv, int d, int dtype, void* qkv,
                 int64_t ld_qkv, void* stream);
+
+/* The rest of a pruned layer (section "How does TokenGate learned token
+ * pruning work?": the layers above the gate process the kept tokens only).
+ * Reading: a pre-norm layer of the Qwen3 family, the model the article
+ * names,
+ *     a = x + W_o . attention(tg_qkv_rope(tg_rms_norm(x)))
+ *     y = a + W_down . tg_swiglu(tg_rms_norm(a))
+ * with the attention of tg_gated_attn_fwd.  No biases.
+ *
+ * RMSNorm of every row: out[t, c] = weight[c] * x[t, c] / sqrt(mean_c(x[t, :]^2) + eps),
+ * computed in fp32 (sum of squares in a fixed order), rounded once to the
+ * output dtype.  x [n, D] row stride ld_x, out [n, D] row stride ld_out,
+ * same dtype; weight [D] fp32.  out may be x itself (same pointer and
+ * stride), no other overlap.  eps finite and >= 0 (1e-6 in the Qwen3
+ * family), else TG_ERR_RANGE.  Supported: D % 8 == 0; x, out, weight
+ * 16-byte aligned, row strides multiples of 16 bytes.
+ */
+int tg_rms_norm(const void* x, int64_t ld_x, int64_t n, int D, const float* weight, float eps,
+                int dtype, void* out, int64_t ld_out, void* stream);
+
+/* out[t, :] = residual[t, :] + W . a[t, :]: a [n, K] row stride ld_a,
+ * W [N, K] packed, residual and out [n, N] with row strides ld_res and
+ * ld_out, one dtype.  The attention output projection (a = the attention
+ * output [Kt, Hq d], W = W_o [D, Hq d]) and the MLP's down projection
+ * (a = the SwiGLU activation [Kt, I], W = W_down [D, I]).  out may be the
+ * residual itself (same pointer and stride), no other overlap.
+ * bf16: MFMA with fp32 accumulation, the residual added in fp32, one
+ * rounding; needs K % 64 == 0, N % 64 == 0, ld_a and K below 2^22, 16-byte
+ * aligned pointers and row strides.  fp32: vector ALUs, n * N < 2^31,
+ * element alignment.
+ */
+int tg_linear_residual(const void* a, int64_t ld_a, int64_t n, int K, const void* W, int N,
+                       const void* residual, int64_t ld_res, int dtype, void* out, int64_t ld_out,
+                       void* stream);
+
+/* The MLP's activation: out[t, j] = silu(W_gate[j] . h[t]) * (W_up[j] . h[t]),
+ * silu(z) = z / (1 + exp(-z)).  h [n, D] row stride ld_h; W_gate and W_up
+ * [I, D] packed; out [n, I] row stride ld_out; one dtype.  bf16: both
+ * products on MFMA in one pass (a tile stages 128 rows of W_gate and the
+ * same rows of W_up), fp32 accumulation, one rounding; needs D % 64 == 0,
+ * I % 32 == 0, ld_h and D below 2^22, 16-byte aligned pointers and row
+ * strides.  fp32: vector ALUs, n * I < 2^31, element alignment.
+ */
+int tg_swiglu(const void* h, int64_t ld_h, int64_t n, int D, const void* w_gate, const void* w_up,
+              int I, int dtype, void* out, int64_t ld_out, void* stream);
 
 #ifdef __cplusplus
 }

@@ -2,7 +2,8 @@
 
 Python face of libtokengate.so: the C ABI calls under the same names
 (``tg_plan``, ``tg_gate_score``, ``tg_select_topk``, ``tg_compact``,
-``tg_gated_attn_fwd``, ``tg_rope_table``, ``tg_qkv_rope``) taking torch device tensors, and ``GatedPrefill``,
+``tg_gated_attn_fwd``, ``tg_rope_table``, ``tg_qkv_rope``, ``tg_rms_norm``,
+``tg_linear_residual``, ``tg_swiglu``) taking torch device tensors, and ``GatedPrefill``,
 which strings them together the way the three-phase prefill of the TokenGate
 article ("How does TokenGate learned token pruning work?") does.  Every step
 runs in the library's HIP kernels; without the built library or a GPU these
@@ -22,10 +23,13 @@ from ._lib import (  # noqa: F401
     tg_compact_workspace,
     tg_gate_score,
     tg_gated_attn_fwd,
+    tg_linear_residual,
     tg_plan,
     tg_qkv_rope,
+    tg_rms_norm,
     tg_rope_table,
     tg_select_topk,
     tg_select_topk_workspace,
+    tg_swiglu,
 )
 from .pipeline import GatedPrefill  # noqa: F401

@@ -51,6 +51,12 @@ SIGNATURES = {
     "tg_rope_table": (_c_int, [_c_vp, _c_i64, _c_int, ctypes.c_double, _c_vp, _c_vp]),
     "tg_qkv_rope": (_c_int, [_c_vp, _c_i64, _c_i64, _c_int, _c_vp, _c_vp, _c_int, _c_int, _c_int,
                              _c_int, _c_vp, _c_i64, _c_vp]),
+    "tg_rms_norm": (_c_int, [_c_vp, _c_i64, _c_i64, _c_int, _c_vp, _c_f32, _c_int, _c_vp, _c_i64,
+                             _c_vp]),
+    "tg_linear_residual": (_c_int, [_c_vp, _c_i64, _c_i64, _c_int, _c_vp, _c_int, _c_vp, _c_i64,
+                                    _c_int, _c_vp, _c_i64, _c_vp]),
+    "tg_swiglu": (_c_int, [_c_vp, _c_i64, _c_i64, _c_int, _c_vp, _c_vp, _c_int, _c_int, _c_vp,
+                           _c_i64, _c_vp]),
 }
 
 _lib = None
@@ -323,3 +329,79 @@ def tg_qkv_rope(x: torch.Tensor, w_qkv: torch.Tensor, rope_table: torch.Tensor, 
     k = out[:, Hq * d:(Hq + Hkv) * d].unflatten(1, (Hkv, d))
     v = out[:, (Hq + Hkv) * d:N].unflatten(1, (Hkv, d))
     return out, q, k, v
+
+
+def _rows2d(t: torch.Tensor, name: str) -> None:
+    if t.dim() != 2 or t.stride(1) != 1:
+        raise ValueError(f"{name} must be 2-D with unit column stride")
+
+
+def tg_rms_norm(x: torch.Tensor, weight: torch.Tensor, eps: float,
+                out: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """RMSNorm of the rows of x [n, D] with an fp32 weight [D]; out may be x."""
+    _require_gpu()
+    lib = load_library()
+    _rows2d(x, "x")
+    n, D = x.shape
+    if tuple(weight.shape) != (D,) or not weight.is_contiguous():
+        raise ValueError("weight must be a packed [D] vector")
+    if out is None:
+        out = torch.empty((n, D), dtype=x.dtype, device=x.device)
+    _rows2d(out, "out")
+    if tuple(out.shape) != (n, D) or out.dtype != x.dtype:
+        raise ValueError("out must match x")
+    _check("tg_rms_norm", lib.tg_rms_norm(
+        _dev(x, "x"), x.stride(0) if n else D, n, D, _dev(weight, "weight", torch.float32),
+        float(eps), _dtype_code(x), _dev(out, "out"), out.stride(0) if n else D, _stream(stream)))
+    return out
+
+
+def tg_linear_residual(a: torch.Tensor, W: torch.Tensor, residual: torch.Tensor,
+                       out: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """residual + a @ W.T: a [n, K], W [N, K], residual [n, N]; out may be residual."""
+    _require_gpu()
+    lib = load_library()
+    _rows2d(a, "a")
+    _rows2d(residual, "residual")
+    n, K = a.shape
+    N = W.shape[0]
+    if tuple(W.shape) != (N, K) or not W.is_contiguous():
+        raise ValueError(f"W must be packed [N, {K}]")
+    if tuple(residual.shape) != (n, N):
+        raise ValueError("residual must be [n, N]")
+    for t, nm in ((W, "W"), (residual, "residual")):
+        if t.dtype != a.dtype:
+            raise TypeError(f"{nm} must have the dtype of a")
+    if out is None:
+        out = torch.empty((n, N), dtype=a.dtype, device=a.device)
+    _rows2d(out, "out")
+    if tuple(out.shape) != (n, N) or out.dtype != a.dtype:
+        raise ValueError("out must be [n, N] of the dtype of a")
+    _check("tg_linear_residual", lib.tg_linear_residual(
+        _dev(a, "a"), a.stride(0) if n else K, n, K, _dev(W, "W"), N, _dev(residual, "residual"),
+        residual.stride(0) if n else N, _dtype_code(a), _dev(out, "out"),
+        out.stride(0) if n else N, _stream(stream)))
+    return out
+
+
+def tg_swiglu(h: torch.Tensor, w_gate: torch.Tensor, w_up: torch.Tensor,
+              out: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """silu(h @ w_gate.T) * (h @ w_up.T): h [n, D], w_gate / w_up [I, D]."""
+    _require_gpu()
+    lib = load_library()
+    _rows2d(h, "h")
+    n, D = h.shape
+    I = w_gate.shape[0]
+    for t, nm in ((w_gate, "w_gate"), (w_up, "w_up")):
+        if tuple(t.shape) != (I, D) or not t.is_contiguous() or t.dtype != h.dtype:
+            raise ValueError(f"{nm} must be packed [{I}, {D}] of the dtype of h")
+    if out is None:
+        out = torch.empty((n, I), dtype=h.dtype, device=h.device)
+    _rows2d(out, "out")
+    if tuple(out.shape) != (n, I) or out.dtype != h.dtype:
+        raise ValueError("out must be [n, I] of the dtype of h")
+    _check("tg_swiglu", lib.tg_swiglu(
+        _dev(h, "h"), h.stride(0) if n else D, n, D, _dev(w_gate, "w_gate"), _dev(w_up, "w_up"), I,
+        _dtype_code(h), _dev(out, "out"), out.stride(0) if n else I, _stream(stream)))
+    return out
+

@@ -12,6 +12,7 @@
 namespace {
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+bool aligned4(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 3u) == 0; }
 
 int elem_bytes(int dtype) { return dtype == TG_BF16 ? 2 : (dtype == TG_F32 ? 4 : 0); }
 
@@ -240,6 +241,81 @@ int tg_qkv_rope(const void* x, int64_t ld_x, int64_t Kt, int D, const void* w_qk
   return from_hip(tg::launch_qkv_rope_f32(static_cast<const float*>(x), ld_x, Kt, D,
                                           static_cast<const float*>(w_qkv), rope_table, Hq, Hkv,
                                           d, static_cast<float*>(qkv), ld_qkv, as_stream(stream)));
+}
+
+int tg_rms_norm(const void* x, int64_t ld_x, int64_t n, int D, const float* weight, float eps,
+                int dtype, void* out, int64_t ld_out, void* stream) {
+  const int eb = elem_bytes(dtype);
+  if (!eb) return TG_ERR_DTYPE;
+  if (n < 0 || n > INT32_MAX || D <= 0 || ld_x < D || ld_out < D) return TG_ERR_SHAPE;
+  if (!isfinite(eps) || eps < 0.0f) return TG_ERR_RANGE;
+  if (D % 8 != 0) return TG_ERR_UNSUPPORTED;
+  if (n == 0) return TG_OK;
+  if (!x || !weight || !out) return TG_ERR_NULL;
+  if (out == x && ld_out != ld_x) return TG_ERR_SHAPE;  // in place only row for row
+  if (!aligned16(x) || !aligned16(out) || !aligned16(weight) || (ld_x * eb) % 16 != 0 ||
+      (ld_out * eb) % 16 != 0)
+    return TG_ERR_ALIGN;
+  return from_hip(tg::launch_rms_norm(x, ld_x, n, D, weight, eps, eb, out, ld_out, as_stream(stream)));
+}
+
+namespace {
+// Shape limits shared by the bf16 projections: K a multiple of the 64-column
+// stage, 32-bit byte offsets inside a 256-row stage, tile count in int.
+int check_bf16_proj(int64_t n, int K, int64_t ld, int N) {
+  if (K % 64 != 0) return TG_ERR_UNSUPPORTED;
+  if (ld >= (1 << 22) || K >= (1 << 22)) return TG_ERR_UNSUPPORTED;
+  if (((n + 255) / 256) * (((int64_t)N + 127) / 128) > INT32_MAX) return TG_ERR_UNSUPPORTED;
+  return TG_OK;
+}
+}  // namespace
+
+int tg_linear_residual(const void* a, int64_t ld_a, int64_t n, int K, const void* W, int N,
+                       const void* residual, int64_t ld_res, int dtype, void* out, int64_t ld_out,
+                       void* stream) {
+  const int eb = elem_bytes(dtype);
+  if (!eb) return TG_ERR_DTYPE;
+  if (n < 0 || n > INT32_MAX || K <= 0 || N <= 0 || ld_a < K || ld_res < N || ld_out < N)
+    return TG_ERR_SHAPE;
+  if (dtype == TG_BF16) {
+    if (N % 64 != 0) return TG_ERR_UNSUPPORTED;
+    const int st = check_bf16_proj(n, K, ld_a, N);
+    if (st != TG_OK) return st;
+  } else if (n * N > INT32_MAX) {
+    return TG_ERR_UNSUPPORTED;  // one thread per output element
+  }
+  if (n == 0) return TG_OK;
+  if (!a || !W || !residual || !out) return TG_ERR_NULL;
+  if (out == residual && ld_out != ld_res) return TG_ERR_SHAPE;  // in place only row for row
+  if (dtype == TG_BF16 &&
+      (!aligned16(a) || !aligned16(W) || !aligned16(residual) || !aligned16(out) ||
+       (ld_a * eb) % 16 != 0 || (ld_res * eb) % 16 != 0 || (ld_out * eb) % 16 != 0))
+    return TG_ERR_ALIGN;
+  if (!aligned4(a) || !aligned4(W) || !aligned4(residual) || !aligned4(out)) return TG_ERR_ALIGN;
+  return from_hip(tg::launch_linear_residual(a, ld_a, n, K, W, N, residual, ld_res, eb, out, ld_out,
+                                             as_stream(stream)));
+}
+
+int tg_swiglu(const void* h, int64_t ld_h, int64_t n, int D, const void* w_gate, const void* w_up,
+              int I, int dtype, void* out, int64_t ld_out, void* stream) {
+  const int eb = elem_bytes(dtype);
+  if (!eb) return TG_ERR_DTYPE;
+  if (n < 0 || n > INT32_MAX || D <= 0 || I <= 0 || ld_h < D || ld_out < I) return TG_ERR_SHAPE;
+  if (dtype == TG_BF16) {
+    if (I % 32 != 0) return TG_ERR_UNSUPPORTED;
+    const int st = check_bf16_proj(n, D, ld_h, I);
+    if (st != TG_OK) return st;
+  } else if (n * I > INT32_MAX) {
+    return TG_ERR_UNSUPPORTED;
+  }
+  if (n == 0) return TG_OK;
+  if (!h || !w_gate || !w_up || !out) return TG_ERR_NULL;
+  if (dtype == TG_BF16 && (!aligned16(h) || !aligned16(w_gate) || !aligned16(w_up) ||
+                           !aligned16(out) || (ld_h * eb) % 16 != 0 || (ld_out * eb) % 16 != 0))
+    return TG_ERR_ALIGN;
+  if (!aligned4(h) || !aligned4(w_gate) || !aligned4(w_up) || !aligned4(out)) return TG_ERR_ALIGN;
+  return from_hip(tg::launch_swiglu(h, ld_h, n, D, w_gate, w_up, I, eb, out, ld_out,
+                                    as_stream(stream)));
 }
 
 }  // extern "C"

@@ -77,6 +77,13 @@ hipError_t launch_rope_table(const int32_t* pos, int64_t n, int d, double theta,
 hipError_t launch_qkv_rope_bf16(const void* x, int64_t ld, int64_t Kt, int D, const void* W,
                                 const float* rope, int Hq, int Hkv, int d, void* out,
                                 int64_t ld_out, hipStream_t s);
+hipError_t launch_rms_norm(const void* x, int64_t ld, int64_t n, int D, const float* w, float eps,
+                           int elem_bytes, void* out, int64_t ld_out, hipStream_t s);
+hipError_t launch_linear_residual(const void* a, int64_t ld, int64_t n, int K, const void* W, int N,
+                                  const void* res, int64_t ld_res, int elem_bytes, void* out,
+                                  int64_t ld_out, hipStream_t s);
+hipError_t launch_swiglu(const void* h, int64_t ld, int64_t n, int K, const void* Wg, const void* Wu,
+                         int I, int elem_bytes, void* out, int64_t ld_out, hipStream_t s);
 hipError_t launch_qkv_rope_f32(const float* x, int64_t ld, int64_t Kt, int D, const float* W,
                                const float* rope, int Hq, int Hkv, int d, float* out,
                                int64_t ld_out, hipStream_t s);

@@ -78,13 +78,43 @@ class GatedPrefill:
         return _lib.tg_rope_table(self.pos_k, d, rope_theta, out=self.rope_table, stream=stream)
 
     def project_qkv(self, w_qkv: torch.Tensor, Hq: int, Hkv: int, d: int,
-                    out: Optional[torch.Tensor] = None, stream=None):
-        """q, k, v of a pruned layer from the kept rows (after rope()).
+                    out: Optional[torch.Tensor] = None, x: Optional[torch.Tensor] = None,
+                    stream=None):
+        """q, k, v of a pruned layer from the kept rows x (default hidden_k;
+        after rope()).  Returns (qkv, q, k, v) as tg_qkv_rope does; q, k and
+        v feed attend() in place."""
+        x = self.hidden_k if x is None else x
+        return _lib.tg_qkv_rope(x, w_qkv, self.rope_table, Hq, Hkv, d, out=out, stream=stream)
 
-        Returns (qkv, q, k, v) as tg_qkv_rope does; q, k and v feed attend()
-        in place."""
-        return _lib.tg_qkv_rope(self.hidden_k, w_qkv, self.rope_table, Hq, Hkv, d, out=out,
-                                stream=stream)
+    def pruned_layer(self, W_qkv: torch.Tensor, weights: dict, Hq: int, Hkv: int, d: int,
+                     gain: torch.Tensor, tau: float, eps: float, x: Optional[torch.Tensor] = None,
+                     stream=None) -> torch.Tensor:
+        """One pre-norm layer above the gate on the kept rows x (default
+        hidden_k), updated in place (after rope()):
+            x += W_o . attention(rope(W_qkv . rms_norm(x)))
+            x += W_down . (silu(W_gate . rms_norm(x)) * (W_up . rms_norm(x)))
+        ``weights`` holds w_in, W_o, w_post, W_gate, W_up, W_down.  The
+        intermediates live in buffers allocated on the first call."""
+        x = self.hidden_k if x is None else x
+        Kt, D = x.shape
+        N = (Hq + 2 * Hkv) * d
+        I = weights["W_gate"].shape[0]
+        key = (Kt, D, N, Hq * d, I, x.dtype)
+        if getattr(self, "_layer_key", None) != key:
+            mk = lambda *shape: torch.empty(shape, dtype=x.dtype, device=x.device)  # noqa: E731
+            self._layer_bufs = {"xn": mk(Kt, D), "qkv": mk(Kt, N), "att": mk(Kt, Hq, d),
+                                "act": mk(Kt, I)}
+            self._layer_key = key
+        b = self._layer_bufs
+        _lib.tg_rms_norm(x, weights["w_in"], eps, out=b["xn"], stream=stream)
+        _, q, k, v = _lib.tg_qkv_rope(b["xn"], W_qkv, self.rope_table, Hq, Hkv, d, out=b["qkv"],
+                                      stream=stream)
+        self.attend(q, k, v, gain, tau, out=b["att"], stream=stream)
+        _lib.tg_linear_residual(b["att"].view(Kt, Hq * d), weights["W_o"], x, out=x, stream=stream)
+        _lib.tg_rms_norm(x, weights["w_post"], eps, out=b["xn"], stream=stream)
+        _lib.tg_swiglu(b["xn"], weights["W_gate"], weights["W_up"], out=b["act"], stream=stream)
+        _lib.tg_linear_residual(b["act"], weights["W_down"], x, out=x, stream=stream)
+        return x
 
     def attend(self, q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, gain: torch.Tensor,
                tau: float, out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None,

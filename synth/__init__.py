@@ -12,6 +12,7 @@ from .workloads import (  # noqa: F401
     WorkloadSpec,
     attention_inputs,
     dense_attention_inputs,
+    layer_weights,
     make_workload,
     qkv_weights,
     spec,

@@ -65,6 +65,8 @@ class WorkloadSpec:
     dense_comparator: bool = False
     b2: float = 0.0
     rope_theta: float = 1e6  # rotary base of the Qwen3 family
+    mlp_mult: int = 3        # MLP width I = mlp_mult * D (6144 for hidden 2048)
+    norm_eps: float = 1e-6   # RMSNorm eps of the Qwen3 family
 
 
 # The five workloads of the gated-prefill benchmark, plus small extra parity
@@ -286,6 +288,27 @@ def qkv_weights(which, layer: int, seed: int = 0) -> torch.Tensor:
     n = (s.Hq + 2 * s.Hkv) * s.d
     w = g.standard_normal((n, s.D), dtype=np.float32) * np.float32(1.0 / np.sqrt(s.D))
     return _round(w, s.dtype)
+
+
+def layer_weights(which, layer: int, seed: int = 0) -> dict:
+    """Weights of pruned layer ``layer`` besides W_qkv (``qkv_weights``).
+
+    Pre-norm layer of the Qwen3 family: ``w_in`` and ``w_post`` the two
+    RMSNorm weights [D] (float32, U(0.5, 1.5)); ``W_o`` [D, Hq d],
+    ``W_gate`` and ``W_up`` [I, D], ``W_down`` [D, I] in the spec dtype,
+    entries N(0, 1/fan_in).
+    """
+    s = spec(which)
+    g = _rng(seed, _S_QKV0 + 20 + int(layer))
+    D, I, HD = s.D, s.mlp_mult * s.D, s.Hq * s.d
+
+    def w(rows, cols):
+        return _round(g.standard_normal((rows, cols), dtype=np.float32) * np.float32(1.0 / np.sqrt(cols)), s.dtype)
+
+    w_in = torch.from_numpy(g.uniform(0.5, 1.5, D).astype(np.float32))
+    w_post = torch.from_numpy(g.uniform(0.5, 1.5, D).astype(np.float32))
+    return {"w_in": w_in, "W_o": w(D, HD), "w_post": w_post, "W_gate": w(I, D), "W_up": w(I, D),
+            "W_down": w(D, I)}
 
 
 def dense_attention_inputs(which, n_tokens: int, seed: int = 0):

@@ -34,7 +34,7 @@ def _declared():
 def test_every_declared_symbol_is_exported_and_typed():
     lib = tg.load_library()
     names = _declared()
-    assert "tg_gated_attn_fwd" in names and "tg_qkv_rope" in names and len(names) == 11
+    assert "tg_gated_attn_fwd" in names and "tg_swiglu" in names and len(names) == 14
     for n in names:
         assert hasattr(lib, n), n
     assert set(names) == set(tg.SIGNATURES)
@@ -221,4 +221,41 @@ def test_rope_table_and_qkv_argument_checks():
     assert call(x=FAKE + 2) == TG_ERR_ALIGN and call(table=FAKE + 4) == TG_ERR_ALIGN
     assert call(ld_x=2052) == TG_ERR_ALIGN and call(ld_qkv=4100) == TG_ERR_ALIGN
     assert call(Kt=0, x=None, w=None, table=None, qkv=None) == TG_OK  # empty: no device work
+
+
+def test_layer_argument_checks():
+    lib = tg.load_library()
+    r = lib.tg_rms_norm
+    # (x, ld_x, n, D, weight, eps, dtype, out, ld_out, stream)
+    assert r(FAKE, 2048, 10, 2048, FAKE, 1e-6, 4, FAKE, 2048, None) == TG_ERR_DTYPE
+    assert r(FAKE, 2000, 10, 2048, FAKE, 1e-6, 1, FAKE, 2048, None) == TG_ERR_SHAPE
+    assert r(FAKE, 2048, 10, 2048, FAKE, -1.0, 1, FAKE, 2048, None) == TG_ERR_RANGE
+    assert r(FAKE, 2048, 10, 2048, FAKE, float("nan"), 1, FAKE, 2048, None) == TG_ERR_RANGE
+    assert r(FAKE, 2044, 10, 2044, FAKE, 1e-6, 1, FAKE, 2044, None) == TG_ERR_UNSUPPORTED
+    assert r(FAKE, 2048, 10, 2048, None, 1e-6, 1, FAKE, 2048, None) == TG_ERR_NULL
+    assert r(FAKE, 2048, 10, 2048, FAKE, 1e-6, 1, FAKE, 4096, None) == TG_ERR_SHAPE  # aliased, other stride
+    assert r(FAKE, 2050, 10, 2048, FAKE, 1e-6, 0, FAKE + 64 * 1024, 2048, None) == TG_ERR_ALIGN
+    assert r(None, 2048, 0, 2048, None, 1e-6, 1, None, 2048, None) == TG_OK
+
+    lr = lib.tg_linear_residual
+    # (a, ld_a, n, K, W, N, res, ld_res, dtype, out, ld_out, stream)
+    assert lr(FAKE, 2048, 10, 2048, FAKE, 2048, FAKE, 2048, 2, FAKE, 2048, None) == TG_ERR_DTYPE
+    assert lr(FAKE, 1000, 10, 2048, FAKE, 2048, FAKE, 2048, 1, FAKE, 2048, None) == TG_ERR_SHAPE
+    assert lr(FAKE, 2048, 10, 2048, FAKE, 2048, FAKE, 2000, 1, FAKE + 4096, 2048, None) == TG_ERR_SHAPE
+    assert lr(FAKE, 2048, 10, 2048, FAKE, 2016, FAKE, 2048, 1, FAKE + 4096, 2048, None) == TG_ERR_UNSUPPORTED
+    assert lr(FAKE, 2000, 10, 2000, FAKE, 2048, FAKE, 2048, 1, FAKE + 4096, 2048, None) == TG_ERR_UNSUPPORTED
+    assert lr(FAKE, 2048, 10, 2048, FAKE, 2048, FAKE, 2048, 1, FAKE, 4096, None) == TG_ERR_SHAPE  # aliased
+    assert lr(FAKE, 2048, 10, 2048, None, 2048, FAKE, 2048, 1, FAKE + 4096, 2048, None) == TG_ERR_NULL
+    assert lr(FAKE, 2052, 10, 2048, FAKE, 2048, FAKE, 2048, 1, FAKE + 4096, 2048, None) == TG_ERR_ALIGN
+    assert lr(FAKE, 2048, 1 << 20, 2048, FAKE, 4096, FAKE, 4096, 0, FAKE + 64, 4096, None) == TG_ERR_UNSUPPORTED
+    assert lr(None, 2048, 0, 2048, None, 2048, None, 2048, 1, None, 2048, None) == TG_OK
+
+    sw = lib.tg_swiglu
+    # (h, ld_h, n, D, w_gate, w_up, I, dtype, out, ld_out, stream)
+    assert sw(FAKE, 2048, 10, 2048, FAKE, FAKE, 6144, 3, FAKE, 6144, None) == TG_ERR_DTYPE
+    assert sw(FAKE, 2048, 10, 2048, FAKE, FAKE, 6144, 1, FAKE, 6000, None) == TG_ERR_SHAPE
+    assert sw(FAKE, 2048, 10, 2048, FAKE, FAKE, 6000, 1, FAKE, 6000, None) == TG_ERR_UNSUPPORTED
+    assert sw(FAKE, 2048, 10, 2048, FAKE, None, 6144, 1, FAKE, 6144, None) == TG_ERR_NULL
+    assert sw(FAKE, 2048, 10, 2048, FAKE, FAKE + 8, 6144, 1, FAKE, 6144, None) == TG_ERR_ALIGN
+    assert sw(None, 2048, 0, 2048, None, None, 6144, 1, None, 6144, None) == TG_OK
 
