@@ -18,7 +18,9 @@ from .tokengate import (  # noqa: F401
     attention_rows_for_check,
     compact,
     gate_scores,
+    gate_backward,
     gated_attention,
+    gated_attention_backward,
     linear_residual,
     plan,
     pruned_layer,

@@ -319,3 +319,87 @@ def pruned_layer(x, pos, cu_kept, bias, gain, tau: float, theta: float, eps: flo
     a = linear_residual(o[sel].reshape(len(sel), Hq * d), W_o, x[sel])
     return linear_residual(swiglu(rms_norm(a, w_post, eps), W_gate, W_up), W_down, a)
 
+
+def gated_attention_backward(q, k, v, bias, gain, tau: float, cu_kept, dout):
+    """Gradients of ``sum(dout * o)``, o from ``gated_attention``.
+
+    Article, "What is token-gated attention?": top-K is not differentiable,
+    so the kept token's score enters the attention as a logit bias, which
+    gives the loss a gradient path back to the scorer; the per-head gain and
+    the temperature are learned as well.  With ``x_ij = tau q_i.k_j / sqrt(d)
+    + g_h s_j`` over visible keys, ``P = softmax_j(x)``, ``o = P v``, the
+    softmax derivative gives ``dx_ij = P_ij (dout_i.v_j - dout_i.o_i)`` and
+        dq_i  = tau / sqrt(d) sum_j dx_ij k_j
+        dk_j  = tau / sqrt(d) sum_(h in group, i) dx_ij q_i
+        dv_j  = sum_(h in group, i) P_ij dout_i
+        ds_j  = sum_h g_h sum_i dx_ij
+        dg_h  = sum_ij dx_ij s_j
+        dtau  = sum_(h, ij) dx_ij q_i.k_j / sqrt(d)
+    Returns fp64 (dq [Kt, Hq, d], dk, dv [Kt, Hkv, d], ds [Kt], dg [Hq],
+    dtau).  ``gain=None`` (no bias term): ds and dg are zero.
+    """
+    Q, K, V, dO = _f64(q), _f64(k), _f64(v), _f64(dout)
+    Kt, Hq, d = Q.shape
+    Hkv = K.shape[1]
+    group = Hq // Hkv
+    s = np.zeros(Kt) if bias is None else _f64(bias)
+    g = np.zeros(Hq) if gain is None else _f64(gain)
+    cu = _i64(cu_kept)
+    scale = float(tau) / math.sqrt(d)
+    dq = np.zeros_like(Q)
+    dk = np.zeros_like(K)
+    dv = np.zeros_like(V)
+    ds = np.zeros(Kt)
+    dg = np.zeros(Hq)
+    dtau = 0.0
+    for b in range(cu.shape[0] - 1):
+        lo, hi = int(cu[b]), int(cu[b + 1])
+        if hi == lo:
+            continue
+        n = hi - lo
+        visible = np.arange(n)[None, :] <= np.arange(n)[:, None]
+        sb = s[lo:hi]
+        for h in range(Hq):
+            kv = h // group
+            Qh, Kh, Vh, dOh = Q[lo:hi, h], K[lo:hi, kv], V[lo:hi, kv], dO[lo:hi, h]
+            qk = Qh @ Kh.T
+            x = scale * qk
+            if gain is not None:
+                x = x + g[h] * sb[None, :]
+            x = np.where(visible, x, -np.inf)
+            P = np.exp(x - x.max(axis=1, keepdims=True))
+            P /= P.sum(axis=1, keepdims=True)
+            O = P @ Vh
+            dP = dOh @ Vh.T
+            dx = P * (dP - np.sum(dOh * O, axis=1, keepdims=True))
+            dq[lo:hi, h] = scale * (dx @ Kh)
+            dk[lo:hi, kv] += scale * (dx.T @ Qh)
+            dv[lo:hi, kv] += P.T @ dOh
+            if gain is not None:
+                col = dx.sum(axis=0)
+                ds[lo:hi] += g[h] * col
+                dg[h] += float(col @ sb)
+            dtau += float(np.sum(dx * qk)) / math.sqrt(d)
+    return dq, dk, dv, ds, dg, dtau
+
+
+def gate_backward(hidden, W1, b1, w2, ds):
+    """Gradients of ``sum(ds * s)`` for the gate score ``s`` of
+    ``gate_scores`` (article, "What is token-gated attention?": the score
+    bias is the scorer's gradient path).  With ``a = W1 h + b1``,
+    ``z = silu(a)``, ``s = b2 + w2.z`` and ``silu'(a) = sig(a) (1 + a (1 - sig(a)))``:
+        dw2 = sum_t ds_t z_t,   db2 = sum_t ds_t,
+        da_t = ds_t w2 * silu'(a_t),   db1 = sum_t da_t,
+        dW1 = sum_t da_t h_t^T,   dh_t = W1^T da_t.
+    Returns fp64 (dh [T, D], dW1 [F, D], db1 [F], dw2 [F], db2).
+    """
+    H, W, w = _f64(hidden), _f64(W1), _f64(w2)
+    g = _f64(ds)
+    a = H @ W.T
+    if b1 is not None:
+        a = a + _f64(b1)[None, :]
+    sig = 1.0 / (1.0 + np.exp(-a))
+    z = a * sig
+    da = g[:, None] * w[None, :] * sig * (1.0 + a * (1.0 - sig))
+    return da @ W, da.T @ H, da.sum(axis=0), z.T @ g, float(g.sum())
+

@@ -9,7 +9,9 @@ a wrong SiLU, ties broken the wrong way, -0.0/NaN mishandled, a pruned
 question token, a wrong bias for non-document keys, temperature applied to the
 bias, an off-by-one causal mask, a wrong GQA head map, a wrong softmax scale,
 rotary pairs (2i, 2i+1) instead of (i, i + d/2), a wrong rotation sign or
-frequency, v rotated, q/k/v heads read from the wrong rows of the projection.
+frequency, v rotated, q/k/v heads read from the wrong rows of the projection,
+a norm or residual out of place in the pruned layer, a backward without the
+dout.o term, without the gain on the bias gradient or without the GQA sum.
 """
 
 import itertools
@@ -601,3 +603,112 @@ def test_pruned_layer_brute_force_and_residual_paths():
     z = list(args)
     z[13], z[17] = np.zeros_like(Wo), np.zeros_like(Wd)
     assert np.array_equal(oracle.pruned_layer(*z), x)
+
+
+# ------------------------------------------------------------- the backward
+# (slips each caught here: a missing D_i = dout.o term, the temperature or
+# 1/sqrt(d) left out of dq/dk, dk/dv not summed over a GQA group, the bias
+# gradient without the gain, dtau taken from the biased logits, a masked
+# key's gradient leaking, silu' written as sigmoid)
+
+def _sdpa_reference(q, k, v, bias, gain, tau, cu, dout):
+    """Gradients by torch autograd through scaled_dot_product_attention
+    (fp64, math backend) with the temperature on q and the bias as an
+    additive float mask: an independent derivation of the backward."""
+    tq = torch.tensor(q, requires_grad=True)
+    tk = torch.tensor(k, requires_grad=True)
+    tv = torch.tensor(v, requires_grad=True)
+    ts = torch.tensor(bias, requires_grad=True)
+    tg_ = torch.tensor(gain, requires_grad=True) if gain is not None else None
+    tt = torch.tensor(float(tau), dtype=torch.float64, requires_grad=True)
+    Hq, Hkv = q.shape[1], k.shape[1]
+    loss = 0.0
+    for b in range(len(cu) - 1):
+        lo, hi = cu[b], cu[b + 1]
+        n = hi - lo
+        causal = torch.full((n, n), -math.inf, dtype=torch.float64).triu(1)
+        mask = causal[None].expand(Hq, n, n)
+        if tg_ is not None:
+            mask = mask + tg_[:, None, None] * ts[lo:hi][None, None, :]
+        qq = (tt * tq[lo:hi]).permute(1, 0, 2)[None]
+        kk = tk[lo:hi].permute(1, 0, 2)[None]
+        vv = tv[lo:hi].permute(1, 0, 2)[None]
+        o = F.scaled_dot_product_attention(qq, kk, vv, attn_mask=mask[None], scale=1.0 / math.sqrt(q.shape[2]),
+                                           enable_gqa=(Hq != Hkv))
+        loss = loss + (o[0].permute(1, 0, 2) * torch.tensor(dout[lo:hi])).sum()
+    loss.backward()
+    dg = tg_.grad.numpy() if tg_ is not None else np.zeros(Hq)
+    dsb = ts.grad.numpy() if ts.grad is not None else np.zeros(len(bias))
+    return tq.grad.numpy(), tk.grad.numpy(), tv.grad.numpy(), dsb, dg, float(tt.grad)
+
+
+@pytest.mark.parametrize("with_bias", [True, False])
+def test_attention_backward_vs_sdpa_autograd(with_bias):
+    rng = np.random.default_rng(31)
+    cu = [0, 5, 12, 12, 15]
+    Kt, Hq, Hkv, d = 15, 4, 2, 8
+    q, k, v = rng.standard_normal((Kt, Hq, d)), rng.standard_normal((Kt, Hkv, d)), rng.standard_normal((Kt, Hkv, d))
+    bias = rng.standard_normal(Kt)
+    bias[[0, 7]] = 0.0
+    gain = rng.uniform(0.5, 2.0, Hq) if with_bias else None
+    dout = rng.standard_normal((Kt, Hq, d))
+    tau = 1.3
+    got = oracle.gated_attention_backward(q, k, v, bias, gain, tau, cu, dout)
+    ref = _sdpa_reference(q, k, v, bias, gain, tau, cu, dout)
+    for name, a, b in zip(["dq", "dk", "dv", "ds", "dg", "dtau"], got, ref):
+        assert np.max(np.abs(np.asarray(a) - np.asarray(b))) <= 1e-10, name
+
+
+def test_attention_backward_finite_differences():
+    rng = np.random.default_rng(32)
+    cu = [0, 6]
+    q, k, v = rng.standard_normal((6, 2, 4)), rng.standard_normal((6, 1, 4)), rng.standard_normal((6, 1, 4))
+    bias, gain, tau = rng.standard_normal(6), np.array([0.8, 1.7]), 0.9
+    dout = rng.standard_normal((6, 2, 4))
+
+    def loss(q_, k_, v_, b_, g_, t_):
+        o, _ = oracle.gated_attention(q_, k_, v_, b_, g_, t_, cu)
+        return float(np.sum(o * dout))
+
+    dq, dk, dv, ds, dg, dtau = oracle.gated_attention_backward(q, k, v, bias, gain, tau, cu, dout)
+    eps = 1e-6
+
+    def fd(fn):
+        return (fn(eps) - fn(-eps)) / (2 * eps)
+
+    def bump(x, idx, e):
+        y = x.copy()
+        y[idx] += e
+        return y
+
+    assert abs(fd(lambda e: loss(q, k, v, bias, gain, tau + e)) - dtau) <= 1e-7
+    assert abs(fd(lambda e: loss(q, k, v, bias, bump(gain, 1, e), tau)) - dg[1]) <= 1e-7
+    assert abs(fd(lambda e: loss(q, k, v, bump(bias, 2, e), gain, tau)) - ds[2]) <= 1e-7
+    assert abs(fd(lambda e: loss(bump(q, (4, 1, 3), e), k, v, bias, gain, tau)) - dq[4, 1, 3]) <= 1e-7
+    assert abs(fd(lambda e: loss(q, bump(k, (1, 0, 2), e), v, bias, gain, tau)) - dk[1, 0, 2]) <= 1e-7
+    assert abs(fd(lambda e: loss(q, k, bump(v, (3, 0, 0), e), bias, gain, tau)) - dv[3, 0, 0]) <= 1e-7
+    # the last key is seen only by the last query: its k gradient is the
+    # last query's alone, and the first key's bias gradient sums every row
+    assert np.all(np.isfinite(ds))
+
+
+def test_gate_backward_vs_autograd_and_finite_differences():
+    rng = np.random.default_rng(33)
+    T, D, Fh = 9, 6, 5
+    h, W1, b1, w2 = rng.standard_normal((T, D)), rng.standard_normal((Fh, D)), rng.standard_normal(Fh), rng.standard_normal(Fh)
+    ds = rng.standard_normal(T)
+    ds[[1, 4]] = 0.0
+    dh, dW1, db1, dw2, db2 = oracle.gate_backward(h, W1, b1, w2, ds)
+    th, tW, tb, tw = (torch.tensor(x, requires_grad=True) for x in (h, W1, b1, w2))
+    s = F.linear(F.silu(F.linear(th, tW, tb)), tw[None, :])[:, 0] + 0.25
+    (s * torch.tensor(ds)).sum().backward()
+    for a, b in ((dh, th.grad), (dW1, tW.grad), (db1, tb.grad), (dw2, tw.grad)):
+        assert np.max(np.abs(a - b.numpy())) <= 1e-10
+    assert abs(db2 - ds.sum()) <= 1e-12
+    assert np.all(dh[[1, 4]] == 0.0)
+    eps = 1e-6
+    f = lambda Wx: float(np.sum(ds * oracle.gate_scores(h, Wx, b1, w2, 0.25)))  # noqa: E731
+    Wp, Wm = W1.copy(), W1.copy()
+    Wp[2, 3] += eps
+    Wm[2, 3] -= eps
+    assert abs((f(Wp) - f(Wm)) / (2 * eps) - dW1[2, 3]) <= 1e-7
