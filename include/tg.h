@@ -18,6 +18,8 @@
  *   tg_compact         stable gather of kept rows, positions and biases
  *   tg_gated_attn_fwd  causal GQA attention over the kept tokens with the
  *                      score bias: logit = tau * q.k / sqrt(d) + g_h * s_j
+ *   tg_gated_attn_bwd  its backward: dq, dk, dv and the gradients of the
+ *                      bias, the gains and the temperature
  *   tg_rope_table      cos / sin of the rotary embedding at the kept rows'
  *                      original positions
  *   tg_qkv_rope        fused q/k/v projection of the kept rows, rotated at
@@ -190,6 +192,45 @@ int tg_gated_attn_fwd(const void* q, const void* k, const void* v,
                       const float* gain, float tau, const int32_t* cu_kept,
                       int B, int max_kept_len, int64_t Kt, int Hq, int Hkv,
                       int d, int dtype, void* out, float* lse, void* stream);
+
+/* Workspace bytes that tg_gated_attn_bwd needs. */
+int tg_gated_attn_bwd_workspace(int B, int64_t Kt, int Hq, int max_kept_len, size_t* bytes);
+
+/*
+ * Backward of tg_gated_attn_fwd (section "What is token-gated attention?":
+ * top-K is not differentiable, so the kept token's score enters the
+ * attention as a logit bias, which gives the loss a gradient path back to
+ * the scorer; the per-head gain and the temperature are learned too).
+ * Gradients of sum(dout * out) with, over visible keys j <= i of a prompt,
+ *     x_ij = tau q_i.k_j / sqrt(d) + g_h s_j,  P = softmax_j(x),
+ *     dx_ij = P_ij (dout_i.v_j - dout_i.out_i):
+ *     dq_i = tau/sqrt(d) sum_j dx_ij k_j
+ *     dk_j = tau/sqrt(d) sum_(h in group, i) dx_ij q_i
+ *     dv_j = sum_(h in group, i) P_ij dout_i
+ *     dbias_j = sum_h g_h sum_i dx_ij      dgain_h = sum_ij dx_ij s_j
+ *     dtau = sum_(h, ij) dx_ij q_i.k_j / sqrt(d)
+ * P is recomputed from lse, which must be the forward's (tg_gated_attn_fwd
+ * with the same inputs and lse != NULL); out is the forward's output.
+ * Inputs as tg_gated_attn_fwd (q, k, v with token strides); out, dout and dq
+ * packed [Kt, Hq, d], dk and dv packed [Kt, Hkv, d], all in dtype; dbias
+ * [Kt], dgain [Hq] and dtau [1] fp32, each may be NULL (not computed);
+ * with gain == NULL they are zero.  The gradient of a kept token's gate
+ * score is dbias_j inside the document (the bias there is the score) and
+ * nothing outside it (the bias there is a constant 0).
+ * bf16: the MFMA products take bf16 operands (P and dx rounded to bf16
+ * before the second products) with fp32 accumulation; dx, the column sums
+ * and the reductions are fp32.  Every sum runs in a fixed order.
+ * Supported: as tg_gated_attn_fwd, with token strides and Hq*d up to 2^23
+ * elements, max_kept_len <= 65535 * 128.  workspace >= the size from
+ * tg_gated_attn_bwd_workspace, 16-byte aligned.
+ */
+int tg_gated_attn_bwd(const void* q, const void* k, const void* v, int64_t q_tok_stride,
+                      int64_t k_tok_stride, int64_t v_tok_stride, const float* bias_s,
+                      const float* gain, float tau, const int32_t* cu_kept, int B,
+                      int max_kept_len, int64_t Kt, int Hq, int Hkv, int d, int dtype,
+                      const void* out, const float* lse, const void* dout, void* dq, void* dk,
+                      void* dv, float* dbias, float* dgain, float* dtau, void* workspace,
+                      size_t workspace_bytes, void* stream);
 
 /* Rotary table of the kept rows (section "How does TokenGate learned token
  * pruning work?": the pruned forward keeps each kept token's original

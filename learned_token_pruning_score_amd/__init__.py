@@ -2,7 +2,7 @@
 
 Python face of libtokengate.so: the C ABI calls under the same names
 (``tg_plan``, ``tg_gate_score``, ``tg_select_topk``, ``tg_compact``,
-``tg_gated_attn_fwd``, ``tg_rope_table``, ``tg_qkv_rope``, ``tg_rms_norm``,
+``tg_gated_attn_fwd``, ``tg_gated_attn_bwd``, ``tg_rope_table``, ``tg_qkv_rope``, ``tg_rms_norm``,
 ``tg_linear_residual``, ``tg_swiglu``) taking torch device tensors, and ``GatedPrefill``,
 which strings them together the way the three-phase prefill of the TokenGate
 article ("How does TokenGate learned token pruning work?") does.  Every step
@@ -22,6 +22,8 @@ from ._lib import (  # noqa: F401
     tg_compact,
     tg_compact_workspace,
     tg_gate_score,
+    tg_gated_attn_bwd,
+    tg_gated_attn_bwd_workspace,
     tg_gated_attn_fwd,
     tg_linear_residual,
     tg_plan,

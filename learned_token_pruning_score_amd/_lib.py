@@ -48,6 +48,11 @@ SIGNATURES = {
     "tg_gated_attn_fwd": (_c_int, [_c_vp, _c_vp, _c_vp, _c_i64, _c_i64, _c_i64, _c_vp, _c_vp,
                                    _c_f32, _c_vp, _c_int, _c_int, _c_i64, _c_int, _c_int, _c_int,
                                    _c_int, _c_vp, _c_vp, _c_vp]),
+    "tg_gated_attn_bwd_workspace": (_c_int, [_c_int, _c_i64, _c_int, _c_int, _c_size_p]),
+    "tg_gated_attn_bwd": (_c_int, [_c_vp, _c_vp, _c_vp, _c_i64, _c_i64, _c_i64, _c_vp, _c_vp,
+                                   _c_f32, _c_vp, _c_int, _c_int, _c_i64, _c_int, _c_int, _c_int,
+                                   _c_int, _c_vp, _c_vp, _c_vp, _c_vp, _c_vp, _c_vp, _c_vp, _c_vp,
+                                   _c_vp, _c_vp, ctypes.c_size_t, _c_vp]),
     "tg_rope_table": (_c_int, [_c_vp, _c_i64, _c_int, ctypes.c_double, _c_vp, _c_vp]),
     "tg_qkv_rope": (_c_int, [_c_vp, _c_i64, _c_i64, _c_int, _c_vp, _c_vp, _c_int, _c_int, _c_int,
                              _c_int, _c_vp, _c_i64, _c_vp]),
@@ -404,4 +409,52 @@ def tg_swiglu(h: torch.Tensor, w_gate: torch.Tensor, w_up: torch.Tensor,
         _dev(h, "h"), h.stride(0) if n else D, n, D, _dev(w_gate, "w_gate"), _dev(w_up, "w_up"), I,
         _dtype_code(h), _dev(out, "out"), out.stride(0) if n else I, _stream(stream)))
     return out
+
+
+def tg_gated_attn_bwd_workspace(B: int, Kt: int, Hq: int, max_kept_len: int) -> int:
+    n = ctypes.c_size_t(0)
+    _check("tg_gated_attn_bwd_workspace",
+           load_library().tg_gated_attn_bwd_workspace(B, Kt, Hq, max_kept_len, ctypes.byref(n)))
+    return int(n.value)
+
+
+def tg_gated_attn_bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
+                      bias_s: Optional[torch.Tensor], gain: Optional[torch.Tensor], tau: float,
+                      cu_kept: torch.Tensor, max_kept_len: int, out: torch.Tensor,
+                      lse: torch.Tensor, dout: torch.Tensor, workspace: Optional[torch.Tensor] = None,
+                      grads=None, stream=None):
+    """Backward of tg_gated_attn_fwd.  Returns (dq, dk, dv, dbias [Kt],
+    dgain [Hq], dtau [1]); ``grads`` may supply those six output tensors."""
+    _require_gpu()
+    lib = load_library()
+    Kt, Hq, d = q.shape
+    Hkv = k.shape[1]
+    B = cu_kept.shape[0] - 1
+    for name, t in (("out", out), ("dout", dout)):
+        if tuple(t.shape) != (Kt, Hq, d) or not t.is_contiguous() or t.dtype != q.dtype:
+            raise ValueError(f"{name} must be packed [Kt, Hq, d] of the dtype of q")
+    if tuple(lse.shape) != (Hq, Kt) or lse.dtype != torch.float32:
+        raise ValueError("lse must be [Hq, Kt] fp32")
+    if grads is None:
+        dev = q.device
+        grads = (torch.empty((Kt, Hq, d), dtype=q.dtype, device=dev),
+                 torch.empty((Kt, Hkv, d), dtype=q.dtype, device=dev),
+                 torch.empty((Kt, Hkv, d), dtype=q.dtype, device=dev),
+                 torch.empty(Kt, dtype=torch.float32, device=dev),
+                 torch.empty(Hq, dtype=torch.float32, device=dev),
+                 torch.empty(1, dtype=torch.float32, device=dev))
+    dq, dk, dv, db, dg, dt = grads
+    if workspace is None:
+        workspace = torch.empty(max(16, tg_gated_attn_bwd_workspace(B, Kt, Hq, max_kept_len)),
+                                dtype=torch.uint8, device=q.device)
+    _check("tg_gated_attn_bwd", lib.tg_gated_attn_bwd(
+        _dev(q, "q"), _dev(k, "k"), _dev(v, "v"), q.stride(0) if Kt else Hq * d,
+        k.stride(0) if Kt else Hkv * d, v.stride(0) if Kt else Hkv * d,
+        _dev(bias_s, "bias_s", torch.float32), _dev(gain, "gain", torch.float32), float(tau),
+        _dev(cu_kept, "cu_kept", torch.int32), B, int(max_kept_len), Kt, Hq, Hkv, d,
+        _dtype_code(q), _dev(out, "out"), _dev(lse, "lse", torch.float32), _dev(dout, "dout"),
+        _dev(dq, "dq"), _dev(dk, "dk"), _dev(dv, "dv"), _dev(db, "dbias", torch.float32),
+        _dev(dg, "dgain", torch.float32), _dev(dt, "dtau", torch.float32), _dev(workspace, "workspace"),
+        workspace.numel() * workspace.element_size(), _stream(stream)))
+    return dq, dk, dv, db, dg, dt
 

@@ -1,0 +1,693 @@
+// Backward of token-gated attention (TokenGate article, section "What is
+// token-gated attention?": top-K selection is not differentiable, so each
+// kept token's score enters the attention above the gate as a logit bias,
+// which gives the loss a gradient path back to the scorer; the per-head gain
+// and the temperature are learned too).  With
+//     x_ij = tau q_i.k_j / sqrt(d) + g_h s_j   (keys j <= i of i's prompt)
+//     P = softmax_j(x),  o_i = sum_j P_ij v_j,  D_i = dout_i . o_i
+//     dx_ij = P_ij (dout_i . v_j - D_i)
+// the gradients are
+//     dq_i = tau/sqrt(d) sum_j dx_ij k_j          (per query head)
+//     dk_j = tau/sqrt(d) sum_(h in group, i) dx_ij q_i
+//     dv_j = sum_(h in group, i) P_ij dout_i
+//     ds_j = sum_h g_h c_hj,  dg_h = sum_j s_j c_hj,  with c_hj = sum_i dx_ij
+//     dtau = sum_(h, ij) dx_ij q_i.k_j / sqrt(d)
+// P is recomputed from the forward's log-sum-exp.  Every sum runs in a fixed
+// order (no atomics), so the results are bit-reproducible:
+//   bwd_prep   D_i per (row, head).
+//   bwd_dq     query-parallel, the forward's layout: one workgroup of 4 waves
+//              per (head, prompt, 128-row query tile), 32 rows per wave; for
+//              each 64-key tile S^T = K Q^T and dP^T = V dO^T on the 32x32x16
+//              bf16 MFMA (lane = query, keys in registers), dx^T in fp32,
+//              dQ^T += K^T dx^T with a transposing LDS read of K (the
+//              forward's value product); partial sums of dx q.k for dtau.
+//   bwd_dkdv   key-parallel: one workgroup of 4 waves per (KV head, prompt,
+//              128-key tile), 32 keys per wave; for each head of the group and
+//              each 64-row query tile S = Q K^T and dP = dO V^T (lane = key,
+//              queries in registers), dV^T += dO^T P and dK^T += Q^T dx with
+//              transposing reads of dO and Q; column sums c_hj of dx in fp32.
+//   bwd_final  ds and dg from c_hj, dtau from the partial sums.
+// fp32 path: one thread per (query, head) for dq and per (key, KV head) for
+// dk / dv, on vector ALUs.
+#include <math.h>
+
+#include <algorithm>
+
+#include "tg_common.h"
+
+namespace tg {
+namespace {
+
+constexpr float kLog2eB = 1.4426950408889634f;
+constexpr int kBufFlagsB = 0x00020000;  // raw buffer: reads past num_records give 0
+constexpr int kT = 64;                  // rows per staged tile (keys in bwd_dq, queries in bwd_dkdv)
+
+typedef short s4v __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) s4v lds_s4v;
+typedef unsigned u32x4v __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) const u32x4v lds_u4v;
+
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return (uint32_t)(uintptr_t)(__attribute__((address_space(3))) const char*)(reinterpret_cast<const char*>(p));
+}
+
+// 16-byte fragment of a row-major staged tile: row r (of 64), 16-byte unit c.
+__device__ __forceinline__ bf16x8 frag_row(uint32_t base, int row_units, int r, int c) {
+  return __builtin_bit_cast(bf16x8, *(lds_u4v*)(uintptr_t)(base + (r * row_units + c) * 16));
+}
+
+// Transposed fragment of a row-major staged tile with rows of ROWT 16-byte
+// units (the forward's value-product read): within each 16-lane group,
+// lane i receives element i % 4 of the 8-byte chunks addressed by lanes
+// 4j + i / 4.  Lane s of group g addresses row 4 (g / 2) + s / 4 and columns
+// 16 (g % 2) + 4 (s % 4) .. +3 of a 16-row step, so lane l receives rows
+// 4G..4G+3 (then +8..+11) of column l % 32 of the 32-column block: the
+// A operand of an MFMA whose k index runs over the staged rows in the order
+// the score accumulator holds them.  kh: 16-row step (0..3), db: 32-column
+// block.
+template <int ROWT>
+__device__ __forceinline__ bf16x8 frag_tr(uint32_t tbase, int kh, int db) {
+  const uint32_t a0 = tbase + ((kh >> 1) * 32 + 16 * (kh & 1)) * (ROWT * 16) + db * 64;
+  const s4v lo4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s4v*)(uintptr_t)a0);
+  const s4v hi4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s4v*)(uintptr_t)(a0 + 8 * (ROWT * 16)));
+  return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo4, hi4, 0, 1, 2, 3, 4, 5, 6, 7));
+}
+
+template <int ROWT>
+__device__ __forceinline__ uint32_t tr_lane_base(const void* tile, int lane) {
+  const int gi = lane & 15, g = lane >> 4;
+  return lds_addr(reinterpret_cast<const char*>(tile) + (4 * (g >> 1) + (gi >> 2)) * (ROWT * 16) +
+                  (16 * (g & 1) + 4 * (gi & 3)) * 2);
+}
+
+// accumulator (two 32-row blocks) -> B operand of the second product, rows
+// relabelled as in frag_tr: pb[kb][hh] holds registers 8 hh .. 8 hh + 7
+__device__ __forceinline__ void to_b_operand(const float (&v)[2][16], bf16x8 (&pb)[2][2]) {
+#pragma unroll
+  for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+    for (int hh = 0; hh < 2; ++hh)
+#pragma unroll
+      for (int j = 0; j < 8; ++j) pb[kb][hh][j] = (__bf16)v[kb][8 * hh + j];
+}
+
+__device__ __forceinline__ void store_bf16_rows(uint16_t* p, const f32x16& a, float mul, int G) {
+#pragma unroll
+  for (int g4 = 0; g4 < 4; ++g4) {
+    const int e0 = 8 * g4 + 4 * G;
+    unsigned w[2];
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const __bf16 x0 = (__bf16)(a[4 * g4 + 2 * j] * mul);
+      const __bf16 x1 = (__bf16)(a[4 * g4 + 2 * j + 1] * mul);
+      w[j] = (unsigned)__builtin_bit_cast(uint16_t, x0) | ((unsigned)__builtin_bit_cast(uint16_t, x1) << 16);
+    }
+    *reinterpret_cast<uint2*>(p + e0) = make_uint2(w[0], w[1]);
+  }
+}
+
+// Fixed-order wave sum (butterfly over the 64 lanes).
+__device__ __forceinline__ float wave_sum(float x) {
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) x += __shfl_xor(x, off);
+  return x;
+}
+
+// D[h][i] = dout_i . o_i (fp32), one thread per (row, head).
+template <typename T>
+__global__ __launch_bounds__(256) void bwd_prep_kernel(const T* __restrict__ o, const T* __restrict__ dout,
+                                                       int64_t Kt, int Hq, int d, float* __restrict__ D) {
+  const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (idx >= Kt * Hq) return;
+  const int64_t i = idx / Hq;
+  const int h = (int)(idx - i * Hq);
+  const T* op = o + idx * d;
+  const T* gp = dout + idx * d;
+  float acc = 0.0f;
+  if constexpr (sizeof(T) == 2) {
+    for (int e = 0; e < d; e += 8) {
+      const uint4 a = *reinterpret_cast<const uint4*>(op + e);
+      const uint4 b = *reinterpret_cast<const uint4*>(gp + e);
+      const uint32_t av[4] = {a.x, a.y, a.z, a.w}, bv[4] = {b.x, b.y, b.z, b.w};
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        acc = fmaf(__uint_as_float(av[j] << 16), __uint_as_float(bv[j] << 16), acc);
+        acc = fmaf(__uint_as_float(av[j] & 0xffff0000u), __uint_as_float(bv[j] & 0xffff0000u), acc);
+      }
+    }
+  } else {
+    for (int e = 0; e < d; ++e) acc = fmaf(op[e], gp[e], acc);
+  }
+  D[(int64_t)h * Kt + i] = acc;
+}
+
+// ------------------------------------------------------------------- dq
+template <int HD>
+__global__ __launch_bounds__(256, 1) void bwd_dq_kernel(
+    const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
+    int64_t qs, int64_t ks, int64_t vs, const float* __restrict__ bias, const float* __restrict__ gain,
+    float tau, const int32_t* __restrict__ cu, int Hq, int group, int n_qt, int64_t Kt,
+    const uint16_t* __restrict__ dout, const float* __restrict__ lse, const float* __restrict__ Dv,
+    uint16_t* __restrict__ dq, float* __restrict__ tau_part) {
+  constexpr int KCH = HD / 8, NKS = HD / 16, NDB = HD / 32;
+  constexpr int ROWN = KCH + 1, ROWT = KCH + 4;
+  constexpr int ITEMS = kT * KCH / 256;  // 16-byte chunks per thread per tile (K, V each)
+  __shared__ uint4 sK[kT * ROWN], sKT[kT * ROWT], sV[kT * ROWN];
+  __shared__ float sS[kT];
+
+  const int h = blockIdx.x;
+  const int b = blockIdx.y;
+  const int tile = n_qt - 1 - (int)blockIdx.z;  // longest first
+  const int lo = cu[b];
+  const int n = cu[b + 1] - lo;
+  const int q0 = tile * 128;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int G = lane >> 5;
+  float* tp = tau_part + (((int64_t)h * gridDim.y + b) * n_qt + tile) * 4;
+  if (q0 >= n) {
+    if (tid < 4) tp[tid] = 0.0f;
+    return;
+  }
+  const int kvh = h / group;
+  const int qw = q0 + 32 * wave;
+  const int my_q = qw + (lane & 31);
+  const bool q_ok = my_q < n;
+  const float c1 = tau * rsqrtf((float)HD) * kLog2eB;  // log2-domain scale of q.k
+  const float gb = (bias && gain) ? gain[h] * kLog2eB : 0.0f;
+
+  bf16x8 qf[NKS], gf[NKS];
+  float lse2 = 0.0f, Di = 0.0f;
+  {
+    const uint16_t* qp = q + (int64_t)(lo + my_q) * qs + (int64_t)h * HD + 8 * G;
+    const uint16_t* gp = dout + ((int64_t)(lo + my_q) * Hq + h) * HD + 8 * G;
+#pragma unroll
+    for (int s = 0; s < NKS; ++s) {
+      uint4 a = make_uint4(0, 0, 0, 0), c = a;
+      if (q_ok) {
+        a = *reinterpret_cast<const uint4*>(qp + 16 * s);
+        c = *reinterpret_cast<const uint4*>(gp + 16 * s);
+      }
+      qf[s] = as_bf16x8(a);
+      gf[s] = as_bf16x8(c);
+    }
+    if (q_ok) {
+      lse2 = lse[(int64_t)h * Kt + lo + my_q] * kLog2eB;
+      Di = Dv[(int64_t)h * Kt + lo + my_q];
+    }
+  }
+  f32x16 acc[NDB];
+#pragma unroll
+  for (int db = 0; db < NDB; ++db)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) acc[db][i] = 0.0f;
+  float tsum = 0.0f;
+
+  const int kv_end = min(q0 + 128, n);
+  const int n_kt = (kv_end + kT - 1) / kT;
+  const uint16_t* kbase = k + (int64_t)lo * ks + (int64_t)kvh * HD;
+  const uint16_t* vbase = v + (int64_t)lo * vs + (int64_t)kvh * HD;
+  int offk[ITEMS], offv[ITEMS];
+#pragma unroll
+  for (int j = 0; j < ITEMS; ++j) {
+    const int id = tid + 256 * j;
+    offk[j] = ((id / KCH) * (int)ks + (id % KCH) * 8) * 2;
+    offv[j] = ((id / KCH) * (int)vs + (id % KCH) * 8) * 2;
+  }
+  uint4 rk[ITEMS], rv[ITEMS];
+  float rs = 0.0f;
+  auto prefetch = [&](int k0) __attribute__((always_inline)) {
+    const int rows = __builtin_amdgcn_readfirstlane(max(min(n - k0, kT), 0));
+    const __amdgpu_buffer_rsrc_t r1 = __builtin_amdgcn_make_buffer_rsrc((void*)(kbase + (int64_t)k0 * ks), (short)0, rows * (int)ks * 2, kBufFlagsB);
+    const __amdgpu_buffer_rsrc_t r2 = __builtin_amdgcn_make_buffer_rsrc((void*)(vbase + (int64_t)k0 * vs), (short)0, rows * (int)vs * 2, kBufFlagsB);
+#pragma unroll
+    for (int j = 0; j < ITEMS; ++j) {
+      rk[j] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r1, offk[j], 0, 0));
+      rv[j] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r2, offv[j], 0, 0));
+    }
+    if (tid < kT) rs = (bias && k0 + tid < n) ? bias[lo + k0 + tid] : 0.0f;
+  };
+  auto stage = [&]() __attribute__((always_inline)) {
+#pragma unroll
+    for (int j = 0; j < ITEMS; ++j) {
+      const int id = tid + 256 * j;
+      sK[(id / KCH) * ROWN + id % KCH] = rk[j];
+      sKT[(id / KCH) * ROWT + id % KCH] = rk[j];
+      sV[(id / KCH) * ROWN + id % KCH] = rv[j];
+    }
+    if (tid < kT) sS[tid] = rs;
+  };
+  const uint32_t kb_n = lds_addr(sK), vb_n = lds_addr(sV);
+  uint32_t ktb = tr_lane_base<ROWT>(sKT, lane);
+  asm volatile("" : "+v"(ktb));
+
+  prefetch(0);
+  for (int t = 0; t < n_kt; ++t) {
+    __syncthreads();  // every wave is done with the previous tile
+    stage();
+    if (t + 1 < n_kt) prefetch((t + 1) * kT);
+    __syncthreads();
+    const int k0 = t * kT;
+    if (k0 > qw + 31 || qw >= n) continue;  // the tile lies past every row of this wave
+    float s[2][16], dp[2][16];
+    {
+      f32x16 a0, a1, b0, b1;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) a0[i] = a1[i] = b0[i] = b1[i] = 0.0f;
+#pragma unroll
+      for (int st = 0; st < NKS; ++st) {
+        const bf16x8 k0f = frag_row(kb_n, ROWN, lane & 31, 2 * st + G);
+        const bf16x8 k1f = frag_row(kb_n, ROWN, 32 + (lane & 31), 2 * st + G);
+        const bf16x8 v0f = frag_row(vb_n, ROWN, lane & 31, 2 * st + G);
+        const bf16x8 v1f = frag_row(vb_n, ROWN, 32 + (lane & 31), 2 * st + G);
+        a0 = mfma32x32x16(k0f, qf[st], a0);
+        a1 = mfma32x32x16(k1f, qf[st], a1);
+        b0 = mfma32x32x16(v0f, gf[st], b0);
+        b1 = mfma32x32x16(v1f, gf[st], b1);
+      }
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        s[0][i] = a0[i]; s[1][i] = a1[i];
+        dp[0][i] = b0[i]; dp[1][i] = b1[i];
+      }
+    }
+    float dx[2][16];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int key = kb * 32 + acc_row(i, lane);
+        const float x2 = fmaf(s[kb][i], c1, gb * sS[key]);
+        const float p = (q_ok && k0 + key <= my_q) ? __builtin_amdgcn_exp2f(x2 - lse2) : 0.0f;
+        dx[kb][i] = p * (dp[kb][i] - Di);
+        tsum = fmaf(dx[kb][i], s[kb][i], tsum);
+      }
+    bf16x8 pb[2][2];
+    to_b_operand(dx, pb);
+#pragma unroll
+    for (int kh = 0; kh < 4; ++kh)
+#pragma unroll
+      for (int db = 0; db < NDB; ++db) acc[db] = mfma32x32x16(frag_tr<ROWT>(ktb, kh, db), pb[kh >> 1][kh & 1], acc[db]);
+  }
+  const float tw = wave_sum(tsum);
+  if (lane == 0) tp[wave] = tw;
+  if (!q_ok) return;
+  const float scale = tau * rsqrtf((float)HD);
+  uint16_t* dp_out = dq + ((int64_t)(lo + my_q) * Hq + h) * HD;
+#pragma unroll
+  for (int db = 0; db < NDB; ++db) store_bf16_rows(dp_out + 32 * db, acc[db], scale, G);
+}
+
+// ----------------------------------------------------------------- dk, dv
+template <int HD>
+__global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(
+    const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
+    int64_t qs, int64_t ks, int64_t vs, const float* __restrict__ bias, const float* __restrict__ gain,
+    float tau, const int32_t* __restrict__ cu, int Hq, int Hkv, int group, int64_t Kt,
+    const uint16_t* __restrict__ dout, const float* __restrict__ lse, const float* __restrict__ Dv,
+    uint16_t* __restrict__ dk, uint16_t* __restrict__ dv, float* __restrict__ colsum) {
+  constexpr int KCH = HD / 8, NKS = HD / 16, NDB = HD / 32;
+  constexpr int ROWN = KCH + 1, ROWT = KCH + 4;
+  constexpr int ITEMS = kT * KCH / 256;
+  __shared__ uint4 sQ[kT * ROWN], sQT[kT * ROWT], sO[kT * ROWN], sOT[kT * ROWT];
+  __shared__ float sL[kT], sD[kT];
+
+  const int kvh = blockIdx.x;
+  const int b = blockIdx.y;
+  const int tile = blockIdx.z;  // the first key tiles see the most queries: launched first
+  const int lo = cu[b];
+  const int n = cu[b + 1] - lo;
+  const int k0w = tile * 128;
+  if (k0w >= n) return;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int G = lane >> 5;
+  const int kw = k0w + 32 * wave;
+  const int my_k = kw + (lane & 31);
+  const bool k_ok = my_k < n;
+  const float c1 = tau * rsqrtf((float)HD) * kLog2eB;
+
+  bf16x8 kf[NKS], vf[NKS];
+  {
+    const uint16_t* kp = k + (int64_t)(lo + my_k) * ks + (int64_t)kvh * HD + 8 * G;
+    const uint16_t* vp = v + (int64_t)(lo + my_k) * vs + (int64_t)kvh * HD + 8 * G;
+#pragma unroll
+    for (int s = 0; s < NKS; ++s) {
+      uint4 a = make_uint4(0, 0, 0, 0), c = a;
+      if (k_ok) {
+        a = *reinterpret_cast<const uint4*>(kp + 16 * s);
+        c = *reinterpret_cast<const uint4*>(vp + 16 * s);
+      }
+      kf[s] = as_bf16x8(a);
+      vf[s] = as_bf16x8(c);
+    }
+  }
+  const float sj = (bias && k_ok) ? bias[lo + my_k] : 0.0f;
+  f32x16 ak[NDB], av[NDB];
+#pragma unroll
+  for (int db = 0; db < NDB; ++db)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) ak[db][i] = av[db][i] = 0.0f;
+
+  const int t_first = k0w / kT;
+  const int n_qtl = (n + kT - 1) / kT;
+  int offq[ITEMS], offo[ITEMS];
+#pragma unroll
+  for (int j = 0; j < ITEMS; ++j) {
+    const int id = tid + 256 * j;
+    offq[j] = ((id / KCH) * (int)qs + (id % KCH) * 8) * 2;
+    offo[j] = ((id / KCH) * Hq * HD + (id % KCH) * 8) * 2;
+  }
+  uint4 rq[ITEMS], ro[ITEMS];
+  float rl = 0.0f, rd = 0.0f;
+  auto prefetch = [&](int h, int i0) __attribute__((always_inline)) {
+    const int rows = __builtin_amdgcn_readfirstlane(max(min(n - i0, kT), 0));
+    const __amdgpu_buffer_rsrc_t r1 = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)(q + (int64_t)(lo + i0) * qs + (int64_t)h * HD), (short)0, rows * (int)qs * 2, kBufFlagsB);
+    const __amdgpu_buffer_rsrc_t r2 = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)(dout + ((int64_t)(lo + i0) * Hq + h) * HD), (short)0, rows * Hq * HD * 2, kBufFlagsB);
+#pragma unroll
+    for (int j = 0; j < ITEMS; ++j) {
+      rq[j] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r1, offq[j], 0, 0));
+      ro[j] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r2, offo[j], 0, 0));
+    }
+    if (tid < kT) {
+      const bool ok = i0 + tid < n;
+      rl = ok ? lse[(int64_t)h * Kt + lo + i0 + tid] * kLog2eB : 0.0f;
+      rd = ok ? Dv[(int64_t)h * Kt + lo + i0 + tid] : 0.0f;
+    }
+  };
+  auto stage = [&]() __attribute__((always_inline)) {
+#pragma unroll
+    for (int j = 0; j < ITEMS; ++j) {
+      const int id = tid + 256 * j;
+      sQ[(id / KCH) * ROWN + id % KCH] = rq[j];
+      sQT[(id / KCH) * ROWT + id % KCH] = rq[j];
+      sO[(id / KCH) * ROWN + id % KCH] = ro[j];
+      sOT[(id / KCH) * ROWT + id % KCH] = ro[j];
+    }
+    if (tid < kT) {
+      sL[tid] = rl;
+      sD[tid] = rd;
+    }
+  };
+  const uint32_t qb_n = lds_addr(sQ), ob_n = lds_addr(sO);
+  uint32_t qtb = tr_lane_base<ROWT>(sQT, lane), otb = tr_lane_base<ROWT>(sOT, lane);
+  asm volatile("" : "+v"(qtb), "+v"(otb));
+
+  const int n_steps = group * (n_qtl - t_first);  // (head, query tile) pairs, head-major
+  prefetch(kvh * group, t_first * kT);
+  float csum = 0.0f;
+  for (int st_i = 0; st_i < n_steps; ++st_i) {
+    const int hh = st_i / (n_qtl - t_first);
+    const int h = kvh * group + hh;
+    const int t = t_first + st_i % (n_qtl - t_first);
+    __syncthreads();
+    stage();
+    if (st_i + 1 < n_steps) {
+      const int hn = kvh * group + (st_i + 1) / (n_qtl - t_first);
+      const int tn = t_first + (st_i + 1) % (n_qtl - t_first);
+      prefetch(hn, tn * kT);
+    }
+    __syncthreads();
+    const int i0 = t * kT;
+    const bool active = (kw < n) && (i0 + kT - 1 >= kw);  // some query of the tile sees a key of the wave
+    if (active) {
+      const float gb = (bias && gain) ? gain[h] * kLog2eB : 0.0f;
+      const float bj = gb * sj;
+      float pr[2][16], dxr[2][16];
+      {
+        f32x16 a0, a1, b0, b1;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) a0[i] = a1[i] = b0[i] = b1[i] = 0.0f;
+#pragma unroll
+        for (int st = 0; st < NKS; ++st) {
+          const bf16x8 q0f = frag_row(qb_n, ROWN, lane & 31, 2 * st + G);
+          const bf16x8 q1f = frag_row(qb_n, ROWN, 32 + (lane & 31), 2 * st + G);
+          const bf16x8 o0f = frag_row(ob_n, ROWN, lane & 31, 2 * st + G);
+          const bf16x8 o1f = frag_row(ob_n, ROWN, 32 + (lane & 31), 2 * st + G);
+          a0 = mfma32x32x16(q0f, kf[st], a0);
+          a1 = mfma32x32x16(q1f, kf[st], a1);
+          b0 = mfma32x32x16(o0f, vf[st], b0);
+          b1 = mfma32x32x16(o1f, vf[st], b1);
+        }
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const int r0 = acc_row(i, lane);
+#pragma unroll
+          for (int qb = 0; qb < 2; ++qb) {
+            const int qr = qb * 32 + r0;
+            const float sv = qb ? a1[i] : a0[i];
+            const float dpv = qb ? b1[i] : b0[i];
+            const bool ok = k_ok && (i0 + qr >= my_k) && (i0 + qr < n);
+            const float p = ok ? __builtin_amdgcn_exp2f(fmaf(sv, c1, bj) - sL[qr]) : 0.0f;
+            pr[qb][i] = p;
+            dxr[qb][i] = p * (dpv - sD[qr]);
+            csum += dxr[qb][i];
+          }
+        }
+      }
+      bf16x8 pb[2][2], xb[2][2];
+      to_b_operand(pr, pb);
+      to_b_operand(dxr, xb);
+#pragma unroll
+      for (int kh = 0; kh < 4; ++kh)
+#pragma unroll
+        for (int db = 0; db < NDB; ++db) {
+          av[db] = mfma32x32x16(frag_tr<ROWT>(otb, kh, db), pb[kh >> 1][kh & 1], av[db]);
+          ak[db] = mfma32x32x16(frag_tr<ROWT>(qtb, kh, db), xb[kh >> 1][kh & 1], ak[db]);
+        }
+    }
+    if (t == n_qtl - 1) {  // last query tile of head h: its column sums are complete
+      const float c = pair_sum(csum);
+      if (k_ok && G == 0) colsum[(int64_t)h * Kt + lo + my_k] = c;
+      csum = 0.0f;
+    }
+  }
+  if (!k_ok) return;
+  const float scale = tau * rsqrtf((float)HD);
+  uint16_t* kp = dk + ((int64_t)(lo + my_k) * Hkv + kvh) * HD;
+  uint16_t* vp = dv + ((int64_t)(lo + my_k) * Hkv + kvh) * HD;
+#pragma unroll
+  for (int db = 0; db < NDB; ++db) {
+    store_bf16_rows(kp + 32 * db, ak[db], scale, G);
+    store_bf16_rows(vp + 32 * db, av[db], 1.0f, G);
+  }
+}
+
+// ------------------------------------------------------------- fp32 paths
+__global__ __launch_bounds__(256) void bwd_dq_f32_kernel(
+    const float* __restrict__ q, const float* __restrict__ k, const float* __restrict__ v,
+    int64_t qs, int64_t ks, int64_t vs, const float* __restrict__ bias, const float* __restrict__ gain,
+    float tau, const int32_t* __restrict__ cu, int B, int Hq, int group, int d, int64_t Kt,
+    const float* __restrict__ dout, const float* __restrict__ lse, const float* __restrict__ Dv,
+    float* __restrict__ dq, float* __restrict__ tau_part) {
+  const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (idx >= Kt * Hq) return;
+  const int64_t i = idx / Hq;
+  const int h = (int)(idx - i * Hq);
+  int b = 0;
+  while (b + 1 < B && cu[b + 1] <= i) ++b;
+  const int64_t lo = cu[b];
+  const int kvh = h / group;
+  const float sc = tau / sqrtf((float)d);
+  const float g = (bias && gain) ? gain[h] : 0.0f;
+  const float L = lse[(int64_t)h * Kt + i], Di = Dv[(int64_t)h * Kt + i];
+  const float* qi = q + i * qs + (int64_t)h * d;
+  const float* gi = dout + (i * Hq + h) * d;
+  float acc[128];
+  for (int e = 0; e < d; ++e) acc[e] = 0.0f;
+  float ts = 0.0f;
+  for (int64_t j = lo; j <= i; ++j) {
+    const float* kj = k + j * ks + (int64_t)kvh * d;
+    const float* vj = v + j * vs + (int64_t)kvh * d;
+    float qk = 0.0f, dp = 0.0f;
+    for (int e = 0; e < d; ++e) {
+      qk = fmaf(qi[e], kj[e], qk);
+      dp = fmaf(gi[e], vj[e], dp);
+    }
+    const float p = expf(sc * qk + (g != 0.0f ? g * bias[j] : 0.0f) - L);
+    const float dx = p * (dp - Di);
+    ts = fmaf(dx, qk, ts);
+    for (int e = 0; e < d; ++e) acc[e] = fmaf(dx, kj[e], acc[e]);
+  }
+  float* out = dq + (i * Hq + h) * d;
+  for (int e = 0; e < d; ++e) out[e] = sc * acc[e];
+  tau_part[idx] = ts;
+}
+
+__global__ __launch_bounds__(256) void bwd_dkdv_f32_kernel(
+    const float* __restrict__ q, const float* __restrict__ k, const float* __restrict__ v,
+    int64_t qs, int64_t ks, int64_t vs, const float* __restrict__ bias, const float* __restrict__ gain,
+    float tau, const int32_t* __restrict__ cu, int B, int Hq, int Hkv, int group, int d, int64_t Kt,
+    const float* __restrict__ dout, const float* __restrict__ lse, const float* __restrict__ Dv,
+    float* __restrict__ dk, float* __restrict__ dv, float* __restrict__ colsum) {
+  const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (idx >= Kt * Hkv) return;
+  const int64_t j = idx / Hkv;
+  const int kvh = (int)(idx - j * Hkv);
+  int b = 0;
+  while (b + 1 < B && cu[b + 1] <= j) ++b;
+  const int64_t hi = cu[b + 1];
+  const float sc = tau / sqrtf((float)d);
+  const float* kj = k + j * ks + (int64_t)kvh * d;
+  const float* vj = v + j * vs + (int64_t)kvh * d;
+  float ak[128], av[128];
+  for (int e = 0; e < d; ++e) ak[e] = av[e] = 0.0f;
+  for (int hh = 0; hh < group; ++hh) {
+    const int h = kvh * group + hh;
+    const float g = (bias && gain) ? gain[h] : 0.0f;
+    float cs = 0.0f;
+    for (int64_t i = j; i < hi; ++i) {
+      const float* qi = q + i * qs + (int64_t)h * d;
+      const float* gi = dout + (i * Hq + h) * d;
+      float qk = 0.0f, dp = 0.0f;
+      for (int e = 0; e < d; ++e) {
+        qk = fmaf(qi[e], kj[e], qk);
+        dp = fmaf(gi[e], vj[e], dp);
+      }
+      const float p = expf(sc * qk + (g != 0.0f ? g * bias[j] : 0.0f) - lse[(int64_t)h * Kt + i]);
+      const float dx = p * (dp - Dv[(int64_t)h * Kt + i]);
+      cs += dx;
+      for (int e = 0; e < d; ++e) {
+        ak[e] = fmaf(dx, qi[e], ak[e]);
+        av[e] = fmaf(p, gi[e], av[e]);
+      }
+    }
+    colsum[(int64_t)h * Kt + j] = cs;
+  }
+  float* ko = dk + (j * Hkv + kvh) * d;
+  float* vo = dv + (j * Hkv + kvh) * d;
+  for (int e = 0; e < d; ++e) {
+    ko[e] = sc * ak[e];
+    vo[e] = av[e];
+  }
+}
+
+// ------------------------------------------------------------- finalize
+// ds_j = sum_h g_h c_hj (h in order), one thread per key.
+__global__ __launch_bounds__(256) void bwd_ds_kernel(const float* __restrict__ colsum, const float* __restrict__ gain,
+                                                     int Hq, int64_t Kt, float* __restrict__ ds) {
+  const int64_t j = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (j >= Kt) return;
+  float acc = 0.0f;
+  for (int h = 0; h < Hq; ++h) acc = fmaf(gain[h], colsum[(int64_t)h * Kt + j], acc);
+  ds[j] = acc;
+}
+
+// Workgroup h < Hq: dg_h = sum_j s_j c_hj; workgroup Hq: dtau = sum of the
+// partials / sqrt(d).  Strided per-thread sums, then a fixed tree in LDS.
+__global__ __launch_bounds__(256) void bwd_reduce_kernel(const float* __restrict__ colsum, const float* __restrict__ bias,
+                                                         int Hq, int64_t Kt, const float* __restrict__ tau_part,
+                                                         int64_t n_part, float inv_sqrt_d, float* __restrict__ dg,
+                                                         float* __restrict__ dtau) {
+  __shared__ float red[256];
+  const int tid = threadIdx.x;
+  const int h = blockIdx.x;
+  float acc = 0.0f;
+  if (h < Hq) {
+    if (dg) for (int64_t j = tid; j < Kt; j += 256) acc = fmaf(bias[j], colsum[(int64_t)h * Kt + j], acc);
+  } else {
+    for (int64_t j = tid; j < n_part; j += 256) acc += tau_part[j];
+  }
+  red[tid] = acc;
+  __syncthreads();
+  for (int w = 128; w >= 1; w >>= 1) {
+    if (tid < w) red[tid] += red[tid + w];
+    __syncthreads();
+  }
+  if (tid == 0) {
+    if (h < Hq) {
+      if (dg) dg[h] = red[0];
+    } else if (dtau) {
+      *dtau = red[0] * inv_sqrt_d;
+    }
+  }
+}
+
+__global__ __launch_bounds__(256) void bwd_zero_kernel(float* __restrict__ p, int64_t n) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i < n) p[i] = 0.0f;
+}
+
+size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+}  // namespace
+
+size_t attn_bwd_workspace_bytes(int B, int64_t Kt, int Hq, int max_len) {
+  const int64_t n_qt = ((int64_t)max_len + 127) / 128;
+  const int64_t n_part = std::max<int64_t>((int64_t)Hq * B * n_qt * 4, Kt * Hq);
+  return 2 * align256((size_t)Hq * Kt * 4) + align256((size_t)n_part * 4);
+}
+
+hipError_t launch_attn_bwd(const void* q, const void* k, const void* v, int64_t qs, int64_t ks, int64_t vs,
+                           const float* bias, const float* gain, float tau, const int32_t* cu, int B,
+                           int max_len, int64_t Kt, int Hq, int Hkv, int d, int elem_bytes, const void* out,
+                           const float* lse, const void* dout, void* dq, void* dk, void* dv, float* ds,
+                           float* dg, float* dtau, void* ws, hipStream_t s) {
+  char* w = static_cast<char*>(ws);
+  float* Dv = reinterpret_cast<float*>(w);
+  float* colsum = reinterpret_cast<float*>(w + align256((size_t)Hq * Kt * 4));
+  float* tpart = reinterpret_cast<float*>(w + 2 * align256((size_t)Hq * Kt * 4));
+  const int group = Hq / Hkv;
+  const int64_t rows = Kt * Hq;
+  const bool has_bias = bias && gain;
+  if (elem_bytes == 2)
+    hipLaunchKernelGGL(bwd_prep_kernel<uint16_t>, dim3((unsigned)((rows + 255) / 256)), dim3(256), 0, s,
+                       static_cast<const uint16_t*>(out), static_cast<const uint16_t*>(dout), Kt, Hq, d, Dv);
+  else
+    hipLaunchKernelGGL(bwd_prep_kernel<float>, dim3((unsigned)((rows + 255) / 256)), dim3(256), 0, s,
+                       static_cast<const float*>(out), static_cast<const float*>(dout), Kt, Hq, d, Dv);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  int64_t n_part;
+  if (elem_bytes == 2) {
+    const int n_qt = (max_len + 127) / 128;
+    n_part = (int64_t)Hq * B * n_qt * 4;
+    const auto* qp = static_cast<const uint16_t*>(q);
+    const auto* kp = static_cast<const uint16_t*>(k);
+    const auto* vp = static_cast<const uint16_t*>(v);
+    const auto* gp = static_cast<const uint16_t*>(dout);
+    const dim3 gq((unsigned)Hq, (unsigned)B, (unsigned)n_qt);
+    const dim3 gk((unsigned)Hkv, (unsigned)B, (unsigned)n_qt);
+    if (d == 128) {
+      hipLaunchKernelGGL(bwd_dq_kernel<128>, gq, dim3(256), 0, s, qp, kp, vp, qs, ks, vs, bias, gain, tau, cu, Hq,
+                         group, n_qt, Kt, gp, lse, Dv, static_cast<uint16_t*>(dq), tpart);
+      hipLaunchKernelGGL(bwd_dkdv_kernel<128>, gk, dim3(256), 0, s, qp, kp, vp, qs, ks, vs, bias, gain, tau, cu, Hq,
+                         Hkv, group, Kt, gp, lse, Dv, static_cast<uint16_t*>(dk), static_cast<uint16_t*>(dv), colsum);
+    } else {
+      hipLaunchKernelGGL(bwd_dq_kernel<64>, gq, dim3(256), 0, s, qp, kp, vp, qs, ks, vs, bias, gain, tau, cu, Hq,
+                         group, n_qt, Kt, gp, lse, Dv, static_cast<uint16_t*>(dq), tpart);
+      hipLaunchKernelGGL(bwd_dkdv_kernel<64>, gk, dim3(256), 0, s, qp, kp, vp, qs, ks, vs, bias, gain, tau, cu, Hq,
+                         Hkv, group, Kt, gp, lse, Dv, static_cast<uint16_t*>(dk), static_cast<uint16_t*>(dv), colsum);
+    }
+  } else {
+    n_part = rows;
+    const auto* qp = static_cast<const float*>(q);
+    const auto* kp = static_cast<const float*>(k);
+    const auto* vp = static_cast<const float*>(v);
+    const auto* gp = static_cast<const float*>(dout);
+    hipLaunchKernelGGL(bwd_dq_f32_kernel, dim3((unsigned)((rows + 255) / 256)), dim3(256), 0, s, qp, kp, vp, qs, ks,
+                       vs, bias, gain, tau, cu, B, Hq, group, d, Kt, gp, lse, Dv, static_cast<float*>(dq), tpart);
+    hipLaunchKernelGGL(bwd_dkdv_f32_kernel, dim3((unsigned)((Kt * Hkv + 255) / 256)), dim3(256), 0, s, qp, kp, vp,
+                       qs, ks, vs, bias, gain, tau, cu, B, Hq, Hkv, group, d, Kt, gp, lse, Dv,
+                       static_cast<float*>(dk), static_cast<float*>(dv), colsum);
+  }
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  // without the bias term ds and dg are zero (filled by a kernel, so that a
+  // captured graph holds no memset node)
+  if (ds) {
+    if (has_bias)
+      hipLaunchKernelGGL(bwd_ds_kernel, dim3((unsigned)((Kt + 255) / 256)), dim3(256), 0, s, colsum, gain, Hq, Kt, ds);
+    else
+      hipLaunchKernelGGL(bwd_zero_kernel, dim3((unsigned)((Kt + 255) / 256)), dim3(256), 0, s, ds, Kt);
+  }
+  if (dg && !has_bias)
+    hipLaunchKernelGGL(bwd_zero_kernel, dim3((unsigned)((Hq + 255) / 256)), dim3(256), 0, s, dg, (int64_t)Hq);
+  hipLaunchKernelGGL(bwd_reduce_kernel, dim3((unsigned)Hq + 1), dim3(256), 0, s, colsum, bias, Hq, Kt, tpart, n_part,
+                     1.0f / sqrtf((float)d), has_bias ? dg : nullptr, dtau);
+  return hipGetLastError();
+}
+
+}  // namespace tg

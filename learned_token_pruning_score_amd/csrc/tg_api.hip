@@ -318,4 +318,54 @@ int tg_swiglu(const void* h, int64_t ld_h, int64_t n, int D, const void* w_gate,
                                     as_stream(stream)));
 }
 
+int tg_gated_attn_bwd_workspace(int B, int64_t Kt, int Hq, int max_kept_len, size_t* bytes) {
+  if (!bytes) return TG_ERR_NULL;
+  if (B < 0 || Kt < 0 || Hq <= 0 || max_kept_len < 0) return TG_ERR_SHAPE;
+  *bytes = tg::attn_bwd_workspace_bytes(B, Kt, Hq, max_kept_len);
+  return TG_OK;
+}
+
+int tg_gated_attn_bwd(const void* q, const void* k, const void* v, int64_t q_tok_stride,
+                      int64_t k_tok_stride, int64_t v_tok_stride, const float* bias_s,
+                      const float* gain, float tau, const int32_t* cu_kept, int B,
+                      int max_kept_len, int64_t Kt, int Hq, int Hkv, int d, int dtype,
+                      const void* out, const float* lse, const void* dout, void* dq, void* dk,
+                      void* dv, float* dbias, float* dgain, float* dtau, void* workspace,
+                      size_t workspace_bytes, void* stream) {
+  const int eb = elem_bytes(dtype);
+  if (!eb) return TG_ERR_DTYPE;
+  if (B < 0 || Kt < 0 || Kt > INT32_MAX || max_kept_len < 0 || max_kept_len > Kt || Hq <= 0 ||
+      Hkv <= 0 || d <= 0)
+    return TG_ERR_SHAPE;
+  if (Hq % Hkv != 0) return TG_ERR_SHAPE;
+  if (q_tok_stride < (int64_t)Hq * d || k_tok_stride < (int64_t)Hkv * d ||
+      v_tok_stride < (int64_t)Hkv * d)
+    return TG_ERR_SHAPE;
+  if (!isfinite(tau) || !(tau > 0.0f)) return TG_ERR_RANGE;
+  if (d != 64 && d != 128) return TG_ERR_UNSUPPORTED;
+  // 64-row tiles of q, k, v and dout are addressed with 32-bit byte offsets;
+  // launch grids: prompts and 128-row tiles in the second and third dimension
+  if (q_tok_stride > (1 << 23) || k_tok_stride > (1 << 23) || v_tok_stride > (1 << 23) ||
+      (int64_t)Hq * d > (1 << 23))
+    return TG_ERR_UNSUPPORTED;
+  if (B > kMaxGridYZ || (max_kept_len + 127) / 128 > kMaxGridYZ) return TG_ERR_UNSUPPORTED;
+  if (dtype == TG_F32 && (Kt * Hq > INT32_MAX)) return TG_ERR_UNSUPPORTED;
+  if (B == 0 || Kt == 0) return TG_OK;
+  if (!q || !k || !v || !cu_kept || !out || !lse || !dout || !dq || !dk || !dv) return TG_ERR_NULL;
+  if (gain && !bias_s) return TG_ERR_NULL;
+  const size_t need = tg::attn_bwd_workspace_bytes(B, Kt, Hq, max_kept_len);
+  if (!workspace || workspace_bytes < need) return TG_ERR_WORKSPACE;
+  if (!aligned16(workspace)) return TG_ERR_ALIGN;
+  if (dtype == TG_BF16) {
+    if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out) || !aligned16(dout) ||
+        !aligned16(dq) || !aligned16(dk) || !aligned16(dv) || (q_tok_stride * 2) % 16 != 0 ||
+        (k_tok_stride * 2) % 16 != 0 || (v_tok_stride * 2) % 16 != 0)
+      return TG_ERR_ALIGN;
+  }
+  return from_hip(tg::launch_attn_bwd(q, k, v, q_tok_stride, k_tok_stride, v_tok_stride, bias_s,
+                                      gain, tau, cu_kept, B, max_kept_len, Kt, Hq, Hkv, d, eb, out,
+                                      lse, dout, dq, dk, dv, dbias, dgain, dtau, workspace,
+                                      as_stream(stream)));
+}
+
 }  // extern "C"

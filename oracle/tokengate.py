@@ -320,7 +320,8 @@ def pruned_layer(x, pos, cu_kept, bias, gain, tau: float, theta: float, eps: flo
     return linear_residual(swiglu(rms_norm(a, w_post, eps), W_gate, W_up), W_down, a)
 
 
-def gated_attention_backward(q, k, v, bias, gain, tau: float, cu_kept, dout):
+def gated_attention_backward(q, k, v, bias, gain, tau: float, cu_kept, dout,
+                             rows: Optional[Sequence[int]] = None, out=None):
     """Gradients of ``sum(dout * o)``, o from ``gated_attention``.
 
     Article, "What is token-gated attention?": top-K is not differentiable,
@@ -336,8 +337,16 @@ def gated_attention_backward(q, k, v, bias, gain, tau: float, cu_kept, dout):
         dg_h  = sum_ij dx_ij s_j
         dtau  = sum_(h, ij) dx_ij q_i.k_j / sqrt(d)
     Returns fp64 (dq [Kt, Hq, d], dk, dv [Kt, Hkv, d], ds [Kt], dg [Hq],
-    dtau).  ``gain=None`` (no bias term): ds and dg are zero.
+    dtau).  ``gain=None`` (no bias term): ds and dg are zero.  ``rows``
+    restricts the work to dq of those global rows (each row's softmax needs
+    only its own logits); the other results are then None and other dq rows
+    NaN.  ``out`` [Kt, Hq, d]: the forward output as stored (e.g. rounded to
+    bf16), used for ``D_i = dout_i . out_i`` in place of the exact o, as a
+    backward that keeps the forward's output does.
     """
+    if rows is not None:
+        return _dq_rows(q, k, v, bias, gain, tau, cu_kept, dout, rows)
+    Ost = None if out is None else _f64(out)
     Q, K, V, dO = _f64(q), _f64(k), _f64(v), _f64(dout)
     Kt, Hq, d = Q.shape
     Hkv = K.shape[1]
@@ -369,7 +378,7 @@ def gated_attention_backward(q, k, v, bias, gain, tau: float, cu_kept, dout):
             x = np.where(visible, x, -np.inf)
             P = np.exp(x - x.max(axis=1, keepdims=True))
             P /= P.sum(axis=1, keepdims=True)
-            O = P @ Vh
+            O = P @ Vh if Ost is None else Ost[lo:hi, h]
             dP = dOh @ Vh.T
             dx = P * (dP - np.sum(dOh * O, axis=1, keepdims=True))
             dq[lo:hi, h] = scale * (dx @ Kh)
@@ -381,6 +390,33 @@ def gated_attention_backward(q, k, v, bias, gain, tau: float, cu_kept, dout):
                 dg[h] += float(col @ sb)
             dtau += float(np.sum(dx * qk)) / math.sqrt(d)
     return dq, dk, dv, ds, dg, dtau
+
+
+def _dq_rows(q, k, v, bias, gain, tau, cu_kept, dout, rows):
+    """dq of some query rows: the same formulas as gated_attention_backward,
+    one row at a time."""
+    Q, K, V, dO = _f64(q), _f64(k), _f64(v), _f64(dout)
+    Kt, Hq, d = Q.shape
+    group = Hq // K.shape[1]
+    s = np.zeros(Kt) if bias is None else _f64(bias)
+    cu = _i64(cu_kept)
+    scale = float(tau) / math.sqrt(d)
+    dq = np.full_like(Q, np.nan)
+    for i in np.unique(_i64(rows)):
+        b = int(np.searchsorted(cu, i, side="right")) - 1
+        lo = int(cu[b])
+        for h in range(Hq):
+            kv = h // group
+            Kh, Vh = K[lo:i + 1, kv], V[lo:i + 1, kv]
+            x = scale * (Kh @ Q[i, h])
+            if gain is not None:
+                x = x + _f64(gain)[h] * s[lo:i + 1]
+            P = np.exp(x - x.max())
+            P /= P.sum()
+            dP = Vh @ dO[i, h]
+            dx = P * (dP - dO[i, h] @ (P @ Vh))
+            dq[i, h] = scale * (dx @ Kh)
+    return dq, None, None, None, None, None
 
 
 def gate_backward(hidden, W1, b1, w2, ds):

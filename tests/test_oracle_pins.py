@@ -712,3 +712,42 @@ def test_gate_backward_vs_autograd_and_finite_differences():
     Wp[2, 3] += eps
     Wm[2, 3] -= eps
     assert abs((f(Wp) - f(Wm)) / (2 * eps) - dW1[2, 3]) <= 1e-7
+
+
+def test_attention_backward_row_subset_matches_full():
+    rng = np.random.default_rng(34)
+    cu = [0, 9, 20]
+    q, k, v = rng.standard_normal((20, 4, 8)), rng.standard_normal((20, 2, 8)), rng.standard_normal((20, 2, 8))
+    bias, gain, dout = rng.standard_normal(20), rng.uniform(0.5, 2, 4), rng.standard_normal((20, 4, 8))
+    full = oracle.gated_attention_backward(q, k, v, bias, gain, 1.1, cu, dout)[0]
+    rows = [0, 8, 9, 19, 13]
+    part = oracle.gated_attention_backward(q, k, v, bias, gain, 1.1, cu, dout, rows=rows)[0]
+    assert np.max(np.abs(part[rows] - full[rows])) <= 1e-12
+    assert np.all(np.isnan(part[[1, 10]]))
+
+
+def test_attention_backward_stored_output_variant():
+    # with the exact forward output stored, the variant is the plain backward;
+    # a perturbed stored output shifts every dx_ij by -P_ij delta_i, which a
+    # brute-force loop over one head checks on ds
+    rng = np.random.default_rng(35)
+    cu = [0, 7]
+    q, k, v = rng.standard_normal((7, 1, 4)), rng.standard_normal((7, 1, 4)), rng.standard_normal((7, 1, 4))
+    bias, gain, tau = rng.standard_normal(7), np.array([1.3]), 0.7
+    dout = rng.standard_normal((7, 1, 4))
+    o, _ = oracle.gated_attention(q, k, v, bias, gain, tau, cu)
+    plain = oracle.gated_attention_backward(q, k, v, bias, gain, tau, cu, dout)
+    same = oracle.gated_attention_backward(q, k, v, bias, gain, tau, cu, dout, out=o)
+    for a, b in zip(plain, same):
+        assert np.max(np.abs(np.asarray(a) - np.asarray(b))) <= 1e-12
+    pert = o + 1e-3 * rng.standard_normal(o.shape)
+    shifted = oracle.gated_attention_backward(q, k, v, bias, gain, tau, cu, dout, out=pert)
+    delta = np.sum(dout[:, 0] * (pert[:, 0] - o[:, 0]), axis=1)
+    x = tau * (q[:, 0] @ k[:, 0].T) / 2.0 + gain[0] * bias[None, :]
+    exp_shift = np.zeros(7)
+    for i in range(7):
+        e = [math.exp(x[i, j]) for j in range(i + 1)]
+        z = sum(e)
+        for j in range(i + 1):
+            exp_shift[j] -= gain[0] * e[j] / z * delta[i]
+    assert np.max(np.abs((shifted[3] - plain[3]) - exp_shift)) <= 1e-12
