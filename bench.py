@@ -129,6 +129,8 @@ def reference_points(tg, w, gp, layers, outs, hidden, W1, b1, w2, stream, dev):
         rotary embedding, the gated attention, the output projection added to
         the residual, RMSNorm, the SwiGLU gate/up projection and the down
         projection added to the residual; each kernel timed alone too;
+      * the backward of one gated attention layer (dq, dk, dv and the bias,
+        gain and temperature gradients) on the step's kept rows;
       * what the chip reaches here on plain library work: a bf16 GEMM of
         8192^3 and a 1 GiB device copy."""
     import torch
@@ -187,6 +189,24 @@ def reference_points(tg, w, gp, layers, outs, hidden, W1, b1, w2, stream, dev):
     r["pruned_layer_us"] = t * 1e3
     r["pruned_layer_TFLOPs"] = (2.0 * Kt * D * (nq + HD + 3 * I) + work["attn_flop_per_layer"]) / (t / 1e3) / 1e12
     del Wqkv, lw, xk, xn, qkv_buf, att, act
+
+    # backward of one gated attention layer (seeded dout), on the step's
+    # kept rows: algorithmic work 2.5x the forward's (S, dP, dQ, dK, dV)
+    lse0 = torch.empty((s.Hq, Kt), dtype=torch.float32, device=dev)
+    out0, _ = tg.tg_gated_attn_fwd(q, k, v, gp.bias_s, gain, s.tau, gp.cu_kept, gp.max_kept_len, lse=lse0)
+    dout = torch.randn(out0.shape, device=dev).to(out0.dtype)
+    wsb = torch.empty(max(16, tg.tg_gated_attn_bwd_workspace(gp.B, Kt, s.Hq, gp.max_kept_len)),
+                      dtype=torch.uint8, device=dev)
+    grads = (torch.empty_like(q), torch.empty_like(k), torch.empty_like(v),
+             torch.empty(Kt, dtype=torch.float32, device=dev), torch.empty(s.Hq, dtype=torch.float32, device=dev),
+             torch.empty(1, dtype=torch.float32, device=dev))
+    bwd = lambda: tg.tg_gated_attn_bwd(q, k, v, gp.bias_s, gain, s.tau, gp.cu_kept, gp.max_kept_len,  # noqa: E731
+                                       out0, lse0, dout, workspace=wsb, grads=grads)
+    bwd()
+    t = time_launches(bwd, stream, reps=5, n=3)
+    r["attn_bwd_us"] = t * 1e3
+    r["attn_bwd_TFLOPs"] = 2.5 * work["attn_flop_per_layer"] / (t / 1e3) / 1e12
+    del lse0, out0, dout, wsb, grads
 
     flush_buf = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
     flush = lambda: flush_buf.fill_(1)  # noqa: E731

@@ -143,7 +143,7 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(const T* __restrict__ o, 
 
 // ------------------------------------------------------------------- dq
 template <int HD>
-__global__ __launch_bounds__(256, 1) void bwd_dq_kernel(
+__global__ __launch_bounds__(256, 2) void bwd_dq_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
     int64_t qs, int64_t ks, int64_t vs, const float* __restrict__ bias, const float* __restrict__ gain,
     float tau, const int32_t* __restrict__ cu, int Hq, int group, int n_qt, int64_t Kt,
@@ -241,49 +241,41 @@ __global__ __launch_bounds__(256, 1) void bwd_dq_kernel(
   uint32_t ktb = tr_lane_base<ROWT>(sKT, lane);
   asm volatile("" : "+v"(ktb));
 
-  prefetch(0);
+  // Two workgroups share a CU: while one stages a tile (global loads, then
+  // LDS writes, between two barriers), the other computes.
   for (int t = 0; t < n_kt; ++t) {
+    prefetch(t * kT);
     __syncthreads();  // every wave is done with the previous tile
     stage();
-    if (t + 1 < n_kt) prefetch((t + 1) * kT);
     __syncthreads();
     const int k0 = t * kT;
     if (k0 > qw + 31 || qw >= n) continue;  // the tile lies past every row of this wave
-    float s[2][16], dp[2][16];
-    {
-      f32x16 a0, a1, b0, b1;
+    // S^T (sa) and dP^T (sb) of the two 32-key blocks, then dx^T straight
+    // into the bf16 B operand of dQ^T += K^T dx^T
+    f32x16 sa[2], sb[2];
 #pragma unroll
-      for (int i = 0; i < 16; ++i) a0[i] = a1[i] = b0[i] = b1[i] = 0.0f;
+    for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-      for (int st = 0; st < NKS; ++st) {
-        const bf16x8 k0f = frag_row(kb_n, ROWN, lane & 31, 2 * st + G);
-        const bf16x8 k1f = frag_row(kb_n, ROWN, 32 + (lane & 31), 2 * st + G);
-        const bf16x8 v0f = frag_row(vb_n, ROWN, lane & 31, 2 * st + G);
-        const bf16x8 v1f = frag_row(vb_n, ROWN, 32 + (lane & 31), 2 * st + G);
-        a0 = mfma32x32x16(k0f, qf[st], a0);
-        a1 = mfma32x32x16(k1f, qf[st], a1);
-        b0 = mfma32x32x16(v0f, gf[st], b0);
-        b1 = mfma32x32x16(v1f, gf[st], b1);
+      for (int i = 0; i < 16; ++i) sa[kb][i] = sb[kb][i] = 0.0f;
+#pragma unroll
+    for (int st = 0; st < NKS; ++st)
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+        sa[kb] = mfma32x32x16(frag_row(kb_n, ROWN, 32 * kb + (lane & 31), 2 * st + G), qf[st], sa[kb]);
+        sb[kb] = mfma32x32x16(frag_row(vb_n, ROWN, 32 * kb + (lane & 31), 2 * st + G), gf[st], sb[kb]);
       }
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        s[0][i] = a0[i]; s[1][i] = a1[i];
-        dp[0][i] = b0[i]; dp[1][i] = b1[i];
-      }
-    }
-    float dx[2][16];
+    bf16x8 pb[2][2];
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
         const int key = kb * 32 + acc_row(i, lane);
-        const float x2 = fmaf(s[kb][i], c1, gb * sS[key]);
+        const float x2 = fmaf(sa[kb][i], c1, gb * sS[key]);
         const float p = (q_ok && k0 + key <= my_q) ? __builtin_amdgcn_exp2f(x2 - lse2) : 0.0f;
-        dx[kb][i] = p * (dp[kb][i] - Di);
-        tsum = fmaf(dx[kb][i], s[kb][i], tsum);
+        const float dxv = p * (sb[kb][i] - Di);
+        tsum = fmaf(dxv, sa[kb][i], tsum);
+        pb[kb][i >> 3][i & 7] = (__bf16)dxv;
       }
-    bf16x8 pb[2][2];
-    to_b_operand(dx, pb);
 #pragma unroll
     for (int kh = 0; kh < 4; ++kh)
 #pragma unroll
