@@ -28,6 +28,7 @@ from .tokengate import (  # noqa: F401
     rms_norm,
     rope_inv_freq,
     round_f32,
+    score_grad_from_bias,
     select_topk,
     swiglu,
 )

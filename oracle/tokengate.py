@@ -439,3 +439,25 @@ def gate_backward(hidden, W1, b1, w2, ds):
     da = g[:, None] * w[None, :] * sig * (1.0 + a * (1.0 - sig))
     return da @ W, da.T @ H, da.sum(axis=0), z.T @ g, float(g.sum())
 
+
+def score_grad_from_bias(dbias, kept_idx, cu_seqlens, doc_begin, doc_end, T: int) -> np.ndarray:
+    """Gradient of the loss with respect to every token's gate score, from
+    the bias gradient of the kept rows (summed over the pruned layers).
+
+    Article, "What is token-gated attention?": each kept token's score
+    becomes its attention bias, so the bias is the scorer's gradient path;
+    top-K passes none.  Reading (as in ``compact``): inside its prompt's
+    document a kept token's bias is its score, outside it the bias is the
+    constant 0.  Returns fp64 ds [T]: ``dbias[r]`` at token ``kept_idx[r]``
+    when that token lies in its document, 0 for every other token.
+    """
+    g = np.zeros(int(T))
+    cu = _i64(cu_seqlens)
+    db, de = _i64(doc_begin), _i64(doc_end)
+    for r, t in enumerate(_i64(kept_idx)):
+        b = int(np.searchsorted(cu, t, side="right")) - 1
+        rel = int(t - cu[b])
+        if db[b] <= rel < de[b]:
+            g[t] += float(dbias[r])
+    return g
+

@@ -751,3 +751,30 @@ def test_attention_backward_stored_output_variant():
         for j in range(i + 1):
             exp_shift[j] -= gain[0] * e[j] / z * delta[i]
     assert np.max(np.abs((shifted[3] - plain[3]) - exp_shift)) <= 1e-12
+
+
+def test_score_grad_from_bias_brute_force_and_chain():
+    # two prompts: [doc 0..4 | question 5..6], [empty doc | question 7..9]
+    cu, db, de = [0, 7, 10], [0, 0], [5, 0]
+    kept = np.array([1, 3, 5, 6, 7, 9])
+    dbias = np.array([0.5, -2.0, 7.0, 1.0, 3.0, -1.0])
+    g = oracle.score_grad_from_bias(dbias, kept, cu, db, de, 10)
+    exp = np.zeros(10)
+    exp[1], exp[3] = 0.5, -2.0   # only document tokens carry their score as bias
+    assert np.array_equal(g, exp)
+    # chained through the compaction's bias: the gradient of
+    # sum(dbias * bias_k) with bias_k = compacted scores equals the score
+    # gradient above (finite differences on a score)
+    rng = np.random.default_rng(36)
+    s = rng.standard_normal(10)
+    keep = np.zeros(10, dtype=np.uint8)
+    keep[kept] = 1
+
+    def loss(sc):
+        _, _, bias, _ = oracle.compact(np.zeros((10, 2)), np.arange(10), sc, keep, cu, db, de)
+        return float(np.sum(dbias * bias))
+
+    for t in range(10):  # the loss is linear in the scores: a wide step is exact up to fp32 rounding
+        e = np.zeros(10)
+        e[t] = 0.25
+        assert abs((loss(s + e) - loss(s - e)) / 0.5 - g[t]) <= 1e-5
