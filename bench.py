@@ -130,7 +130,8 @@ def reference_points(tg, w, gp, layers, outs, hidden, W1, b1, w2, stream, dev):
         the residual, RMSNorm, the SwiGLU gate/up projection and the down
         projection added to the residual; each kernel timed alone too;
       * the backward of one gated attention layer (dq, dk, dv and the bias,
-        gain and temperature gradients) on the step's kept rows;
+        gain and temperature gradients) on the step's kept rows, and the
+        gate MLP's backward from the kept rows' bias gradient;
       * what the chip reaches here on plain library work: a bf16 GEMM of
         8192^3 and a 1 GiB device copy."""
     import torch
@@ -207,6 +208,18 @@ def reference_points(tg, w, gp, layers, outs, hidden, W1, b1, w2, stream, dev):
     r["attn_bwd_us"] = t * 1e3
     r["attn_bwd_TFLOPs"] = 2.5 * work["attn_flop_per_layer"] / (t / 1e3) / 1e12
     del lse0, out0, dout, wsb, grads
+
+    # gate MLP backward from the kept rows' bias gradient
+    dbias = torch.randn(Kt, device=dev)
+    wsg = torch.empty(max(16, tg.tg_gate_bwd_workspace(Kt, s.D, s.F, hidden.dtype)), dtype=torch.uint8,
+                      device=dev)
+    gbwd = lambda: tg.tg_gate_bwd(  # noqa: E731
+        gp.hidden_k, W1, b1, w2, dbias, gp.kept_idx, gp.cu_seqlens, gp.doc_begin, gp.doc_end, workspace=wsg)
+    gbwd()
+    t = time_launches(gbwd, stream, reps=5, n=3)
+    r["gate_bwd_us"] = t * 1e3
+    r["gate_bwd_TFLOPs"] = 6.0 * Kt * s.D * s.F / (t / 1e3) / 1e12
+    del dbias, wsg
 
     flush_buf = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
     flush = lambda: flush_buf.fill_(1)  # noqa: E731

@@ -20,6 +20,8 @@
  *                      score bias: logit = tau * q.k / sqrt(d) + g_h * s_j
  *   tg_gated_attn_bwd  its backward: dq, dk, dv and the gradients of the
  *                      bias, the gains and the temperature
+ *   tg_gate_bwd        backward of the gate MLP from the kept rows' bias
+ *                      gradient (the scorer's gradient path)
  *   tg_rope_table      cos / sin of the rotary embedding at the kept rows'
  *                      original positions
  *   tg_qkv_rope        fused q/k/v projection of the kept rows, rotated at
@@ -231,6 +233,37 @@ int tg_gated_attn_bwd(const void* q, const void* k, const void* v, int64_t q_tok
                       const void* out, const float* lse, const void* dout, void* dq, void* dk,
                       void* dv, float* dbias, float* dgain, float* dtau, void* workspace,
                       size_t workspace_bytes, void* stream);
+
+/* Workspace bytes that tg_gate_bwd needs. */
+int tg_gate_bwd_workspace(int64_t Kt, int D, int F, int dtype, size_t* bytes);
+
+/*
+ * Backward of the gate MLP (section "What is token-gated attention?": the
+ * kept token's score is its attention bias above the gate, the scorer's
+ * gradient path; top-K passes none).  dbias [Kt] fp32 is the bias gradient
+ * of the kept rows (tg_gated_attn_bwd's dbias summed over the pruned
+ * layers).  Row r's token t = kept_idx[r] gets ds_t = dbias[r] when t lies
+ * in its prompt's document (the bias there is the score) and 0 otherwise;
+ * every other token gets nothing.  With a_r = W1 h_r + b1 (h_r = hidden_k
+ * row r, the gate input of token t):
+ *     da_r = ds_r w2 * silu'(a_r)    dhidden_k[r] = W1^T da_r
+ *     dW1 = sum_r da_r h_r^T   db1 = sum_r da_r   dw2 = sum_r ds_r silu(a_r)
+ *     db2 = sum_r ds_r
+ * hidden_k [Kt, D] row stride ld_hidden (tg_compact's hidden_out), W1
+ * [F, D] in its dtype; b1 [F] (may be NULL), w2 [F] fp32, 16-byte aligned;
+ * kept_idx [Kt] int32 (tg_compact's kept_idx_out); cu_seqlens [B+1],
+ * doc_begin / doc_end [B] as for tg_select_topk (device).  Outputs:
+ * dhidden_k [Kt, D] packed in the dtype; dW1 [F, D], db1 [F] (may be NULL),
+ * dw2 [F], db2 [1] fp32.  bf16: MFMA for the three products (da rounded to
+ * bf16 for dhidden_k and dW1), fp32 sums in fixed order.  Supported:
+ * F in {64, 128, 256}; bf16 needs D % 64 == 0, ld_hidden and D below 2^22,
+ * aligned pointers and row stride.  workspace >= tg_gate_bwd_workspace.
+ */
+int tg_gate_bwd(const void* hidden_k, int64_t ld_hidden, int64_t Kt, int D, const void* W1,
+                const float* b1, const float* w2, int F, const float* dbias,
+                const int32_t* kept_idx, const int32_t* cu_seqlens, const int32_t* doc_begin,
+                const int32_t* doc_end, int B, int dtype, void* dhidden_k, float* dW1, float* db1,
+                float* dw2, float* db2, void* workspace, size_t workspace_bytes, void* stream);
 
 /* Rotary table of the kept rows (section "How does TokenGate learned token
  * pruning work?": the pruned forward keeps each kept token's original

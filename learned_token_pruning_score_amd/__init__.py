@@ -21,6 +21,8 @@ from ._lib import (  # noqa: F401
     tg_abi_version,
     tg_compact,
     tg_compact_workspace,
+    tg_gate_bwd,
+    tg_gate_bwd_workspace,
     tg_gate_score,
     tg_gated_attn_bwd,
     tg_gated_attn_bwd_workspace,

@@ -53,6 +53,10 @@ SIGNATURES = {
                                    _c_f32, _c_vp, _c_int, _c_int, _c_i64, _c_int, _c_int, _c_int,
                                    _c_int, _c_vp, _c_vp, _c_vp, _c_vp, _c_vp, _c_vp, _c_vp, _c_vp,
                                    _c_vp, _c_vp, ctypes.c_size_t, _c_vp]),
+    "tg_gate_bwd_workspace": (_c_int, [_c_i64, _c_int, _c_int, _c_int, _c_size_p]),
+    "tg_gate_bwd": (_c_int, [_c_vp, _c_i64, _c_i64, _c_int, _c_vp, _c_vp, _c_vp, _c_int, _c_vp, _c_vp,
+                             _c_vp, _c_vp, _c_vp, _c_int, _c_int, _c_vp, _c_vp, _c_vp, _c_vp, _c_vp,
+                             _c_vp, ctypes.c_size_t, _c_vp]),
     "tg_rope_table": (_c_int, [_c_vp, _c_i64, _c_int, ctypes.c_double, _c_vp, _c_vp]),
     "tg_qkv_rope": (_c_int, [_c_vp, _c_i64, _c_i64, _c_int, _c_vp, _c_vp, _c_int, _c_int, _c_int,
                              _c_int, _c_vp, _c_i64, _c_vp]),
@@ -457,4 +461,46 @@ def tg_gated_attn_bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
         _dev(dg, "dgain", torch.float32), _dev(dt, "dtau", torch.float32), _dev(workspace, "workspace"),
         workspace.numel() * workspace.element_size(), _stream(stream)))
     return dq, dk, dv, db, dg, dt
+
+
+def tg_gate_bwd_workspace(Kt: int, D: int, F: int, dtype: torch.dtype) -> int:
+    n = ctypes.c_size_t(0)
+    code = TG_BF16 if dtype == torch.bfloat16 else TG_F32
+    _check("tg_gate_bwd_workspace", load_library().tg_gate_bwd_workspace(Kt, D, F, code, ctypes.byref(n)))
+    return int(n.value)
+
+
+def tg_gate_bwd(hidden_k: torch.Tensor, W1: torch.Tensor, b1: Optional[torch.Tensor], w2: torch.Tensor,
+                dbias: torch.Tensor, kept_idx: torch.Tensor, cu_seqlens: torch.Tensor,
+                doc_begin: torch.Tensor, doc_end: torch.Tensor, workspace: Optional[torch.Tensor] = None,
+                stream=None):
+    """Backward of the gate MLP over the kept rows.  Returns (dhidden_k
+    [Kt, D], dW1 [F, D] fp32, db1 [F] fp32, dw2 [F] fp32, db2 [1] fp32)."""
+    _require_gpu()
+    lib = load_library()
+    if hidden_k.dim() != 2 or hidden_k.stride(1) != 1:
+        raise ValueError("hidden_k must be [Kt, D] with unit column stride")
+    Kt, D = hidden_k.shape
+    F = W1.shape[0]
+    if tuple(W1.shape) != (F, D) or not W1.is_contiguous() or W1.dtype != hidden_k.dtype:
+        raise ValueError("W1 must be packed [F, D] of the dtype of hidden_k")
+    B = cu_seqlens.shape[0] - 1
+    dev = hidden_k.device
+    dh = torch.empty((Kt, D), dtype=hidden_k.dtype, device=dev)
+    dW1 = torch.empty((F, D), dtype=torch.float32, device=dev)
+    db1 = torch.empty(F, dtype=torch.float32, device=dev) if b1 is not None else None
+    dw2 = torch.empty(F, dtype=torch.float32, device=dev)
+    db2 = torch.empty(1, dtype=torch.float32, device=dev)
+    if workspace is None:
+        workspace = torch.empty(max(16, tg_gate_bwd_workspace(Kt, D, F, hidden_k.dtype)),
+                                dtype=torch.uint8, device=dev)
+    _check("tg_gate_bwd", lib.tg_gate_bwd(
+        _dev(hidden_k, "hidden_k"), hidden_k.stride(0) if Kt else D, Kt, D, _dev(W1, "W1"),
+        _dev(b1, "b1", torch.float32), _dev(w2, "w2", torch.float32), F,
+        _dev(dbias, "dbias", torch.float32), _dev(kept_idx, "kept_idx", torch.int32),
+        _dev(cu_seqlens, "cu_seqlens", torch.int32), _dev(doc_begin, "doc_begin", torch.int32),
+        _dev(doc_end, "doc_end", torch.int32), B, _dtype_code(hidden_k), _dev(dh, "dhidden_k"),
+        _dev(dW1, "dW1"), _dev(db1, "db1"), _dev(dw2, "dw2"), _dev(db2, "db2"),
+        _dev(workspace, "workspace"), workspace.numel() * workspace.element_size(), _stream(stream)))
+    return dh, dW1, db1, dw2, db2
 

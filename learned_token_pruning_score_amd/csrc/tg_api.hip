@@ -368,4 +368,44 @@ int tg_gated_attn_bwd(const void* q, const void* k, const void* v, int64_t q_tok
                                       as_stream(stream)));
 }
 
+int tg_gate_bwd_workspace(int64_t Kt, int D, int F, int dtype, size_t* bytes) {
+  if (!bytes) return TG_ERR_NULL;
+  const int eb = elem_bytes(dtype);
+  if (!eb) return TG_ERR_DTYPE;
+  if (Kt < 0 || D <= 0 || F <= 0) return TG_ERR_SHAPE;
+  *bytes = tg::gate_bwd_workspace_bytes(Kt, D, F, eb);
+  return TG_OK;
+}
+
+int tg_gate_bwd(const void* hidden_k, int64_t ld_hidden, int64_t Kt, int D, const void* W1,
+                const float* b1, const float* w2, int F, const float* dbias,
+                const int32_t* kept_idx, const int32_t* cu_seqlens, const int32_t* doc_begin,
+                const int32_t* doc_end, int B, int dtype, void* dhidden_k, float* dW1, float* db1,
+                float* dw2, float* db2, void* workspace, size_t workspace_bytes, void* stream) {
+  const int eb = elem_bytes(dtype);
+  if (!eb) return TG_ERR_DTYPE;
+  if (Kt < 0 || Kt > INT32_MAX || D <= 0 || F <= 0 || ld_hidden < D || B < 0) return TG_ERR_SHAPE;
+  if (Kt > 0 && B == 0) return TG_ERR_SHAPE;
+  if (!(F == 64 || F == 128 || F == 256)) return TG_ERR_UNSUPPORTED;
+  if (dtype == TG_BF16) {
+    if (D % 64 != 0 || ld_hidden >= (1 << 22) || D >= (1 << 22)) return TG_ERR_UNSUPPORTED;
+  } else if (Kt * F > INT32_MAX || Kt * D > INT32_MAX) {
+    return TG_ERR_UNSUPPORTED;
+  }
+  if ((int64_t)F * D > INT32_MAX / 2) return TG_ERR_UNSUPPORTED;
+  if (!W1 || !w2 || !dW1 || !dw2 || !db2) return TG_ERR_NULL;
+  const size_t need = tg::gate_bwd_workspace_bytes(Kt, D, F, eb);
+  if (!workspace || workspace_bytes < need) return TG_ERR_WORKSPACE;
+  if (Kt > 0 && (!hidden_k || !dbias || !kept_idx || !cu_seqlens || !doc_begin || !doc_end ||
+                 !dhidden_k))
+    return TG_ERR_NULL;
+  if (!aligned16(workspace) || !aligned16(w2) || (b1 && !aligned16(b1))) return TG_ERR_ALIGN;
+  if (dtype == TG_BF16 && (!aligned16(hidden_k) || !aligned16(W1) || !aligned16(dhidden_k) ||
+                           (ld_hidden * 2) % 16 != 0))
+    return TG_ERR_ALIGN;
+  return from_hip(tg::launch_gate_bwd(hidden_k, ld_hidden, Kt, D, W1, b1, w2, F, dbias, kept_idx,
+                                      cu_seqlens, doc_begin, doc_end, B, eb, dhidden_k, dW1, db1,
+                                      dw2, db2, workspace, as_stream(stream)));
+}
+
 }  // extern "C"

@@ -83,6 +83,17 @@ hipError_t launch_attn_bwd(const void* q, const void* k, const void* v, int64_t 
                            int max_len, int64_t Kt, int Hq, int Hkv, int d, int elem_bytes, const void* out,
                            const float* lse, const void* dout, void* dq, void* dk, void* dv, float* ds,
                            float* dg, float* dtau, void* ws, hipStream_t s);
+hipError_t launch_proj_store(const void* x, int64_t ld, int64_t n, int K, const void* W, int N, void* out,
+                             int64_t ld_out, hipStream_t s);
+hipError_t launch_gate_bwd_da(const void* h, int64_t ld, int64_t n, int D, const void* W1, int F,
+                              const float* b1, const float* w2, const float* ds, void* da,
+                              float* part_db1, float* part_dw2, hipStream_t s);
+size_t gate_bwd_workspace_bytes(int64_t Kt, int D, int F, int elem_bytes);
+hipError_t launch_gate_bwd(const void* h, int64_t ld, int64_t Kt, int D, const void* W1, const float* b1,
+                           const float* w2, int F, const float* dbias, const int32_t* kept_idx,
+                           const int32_t* cu, const int32_t* db, const int32_t* de, int B, int elem_bytes,
+                           void* dh, float* dW1, float* db1, float* dw2, float* db2, void* ws,
+                           hipStream_t s);
 hipError_t launch_rms_norm(const void* x, int64_t ld, int64_t n, int D, const float* w, float eps,
                            int elem_bytes, void* out, int64_t ld_out, hipStream_t s);
 hipError_t launch_linear_residual(const void* a, int64_t ld, int64_t n, int K, const void* W, int N,

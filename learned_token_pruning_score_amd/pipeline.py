@@ -116,6 +116,16 @@ class GatedPrefill:
         _lib.tg_linear_residual(b["act"], weights["W_down"], x, out=x, stream=stream)
         return x
 
+    def gate_backward(self, dbias: torch.Tensor, W1: torch.Tensor, b1: Optional[torch.Tensor],
+                      w2: torch.Tensor, stream=None):
+        """Backward of the gate MLP from the kept rows' bias gradient dbias
+        [Kt] (summed over the pruned layers), after gate_and_select with
+        with_index.  Returns (dhidden_k [Kt, D], dW1, db1, dw2, db2); the
+        gradient of hidden at token kept_idx[r] is dhidden_k[r], zero at the
+        other tokens."""
+        return _lib.tg_gate_bwd(self.hidden_k, W1, b1, w2, dbias, self.kept_idx, self.cu_seqlens,
+                                self.doc_begin, self.doc_end, stream=stream)
+
     def attend(self, q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, gain: torch.Tensor,
                tau: float, out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None,
                stream=None):
