@@ -18,7 +18,7 @@
 //   gbwd_dw1      dW1 = da^T h: one workgroup per (64-column slice of h, chunk
 //                 of rows), both MFMA operands through transposing LDS reads
 //                 of the row-major tiles, fp32 partial sums per chunk.
-//   gbwd_reduce   dW1, db1, dw2, db2 as fixed-order sums of the partials.
+//   sums          dW1, db1, dw2, db2 as fixed-order sums of the partials.
 // fp32 path: one thread per output element on vector ALUs.
 #include <math.h>
 
@@ -168,34 +168,56 @@ __global__ __launch_bounds__(256) void gbwd_dw1_kernel(const uint16_t* __restric
   }
 }
 
-// Fixed-order sums of the partials: thread i < F*D sums dW1 over the
-// chunks, the next F threads db1 and dw2 over the 32-row blocks, the last
-// one db2 over the rows.
-__global__ __launch_bounds__(256) void gbwd_reduce_kernel(const float* __restrict__ part, int n_chunks, int F, int D,
-                                                          const float* __restrict__ p1, const float* __restrict__ p2,
-                                                          int64_t n_blk, const float* __restrict__ ds, int64_t Kt,
-                                                          float* __restrict__ dW1, float* __restrict__ db1,
-                                                          float* __restrict__ dw2, float* __restrict__ db2) {
+// Fixed-order sums of the partials.  dW1: one thread per element over the
+// chunks.  db1 / dw2: one workgroup per 64 columns; thread (g, c) sums the
+// 32-row blocks g, g + 4, ... of column c, then the four partials are added
+// in order.  db2: one workgroup, a strided sum per thread, then a tree.
+__global__ __launch_bounds__(256) void gbwd_dw1_sum_kernel(const float* __restrict__ part, int n_chunks, int64_t FD,
+                                                           float* __restrict__ dW1) {
   const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  const int64_t FD = (int64_t)F * D;
-  if (i < FD) {
-    float acc = 0.0f;
-    for (int c = 0; c < n_chunks; ++c) acc += part[(int64_t)c * FD + i];
-    dW1[i] = acc;
-  } else if (i < FD + F) {
-    const int f = (int)(i - FD);
-    float a1 = 0.0f, a2 = 0.0f;
-    for (int64_t b = 0; b < n_blk; ++b) {
+  if (i >= FD) return;
+  float acc = 0.0f;
+  for (int c = 0; c < n_chunks; ++c) acc += part[(int64_t)c * FD + i];
+  dW1[i] = acc;
+}
+
+__global__ __launch_bounds__(256) void gbwd_col_sum_kernel(const float* __restrict__ p1, const float* __restrict__ p2,
+                                                           int64_t n_blk, int F, float* __restrict__ db1,
+                                                           float* __restrict__ dw2) {
+  __shared__ float r1[4][64], r2[4][64];
+  const int tid = threadIdx.x;
+  const int grp = tid >> 6;
+  const int f = blockIdx.x * 64 + (tid & 63);
+  float a1 = 0.0f, a2 = 0.0f;
+  if (f < F) {
+    for (int64_t b = grp; b < n_blk; b += 4) {
       a1 += p1[b * F + f];
       a2 += p2[b * F + f];
     }
-    if (db1) db1[f] = a1;
-    dw2[f] = a2;
-  } else if (i == FD + F) {
-    float acc = 0.0f;
-    for (int64_t r = 0; r < Kt; ++r) acc += ds[r];
-    *db2 = acc;
   }
+  r1[grp][tid & 63] = a1;
+  r2[grp][tid & 63] = a2;
+  __syncthreads();
+  if (tid < 64 && f < F) {
+    const float s1 = ((r1[0][tid] + r1[1][tid]) + r1[2][tid]) + r1[3][tid];
+    const float s2 = ((r2[0][tid] + r2[1][tid]) + r2[2][tid]) + r2[3][tid];
+    if (db1) db1[f] = s1;
+    dw2[f] = s2;
+  }
+}
+
+__global__ __launch_bounds__(256) void gbwd_sum_ds_kernel(const float* __restrict__ ds, int64_t Kt, float* __restrict__ db2) {
+  __shared__ float red[256];
+  const int tid = threadIdx.x;
+  float acc = 0.0f;
+  for (int64_t r = tid; r < Kt; r += 256) acc += ds[r];
+  red[tid] = acc;
+  __syncthreads();
+  for (int w = 128; w >= 1; w >>= 1) {
+    if (tid < w) red[tid] += red[tid + w];
+    __syncthreads();
+  }
+  if (tid == 0) *db2 = red[0];
 }
 
 // ---------------------------------------------------------------- fp32
@@ -333,8 +355,11 @@ hipError_t launch_gate_bwd(const void* h, int64_t ld, int64_t Kt, int D, const v
     if (e != hipSuccess) return e;
     // the 32-row blocks holding a kept row are written by the da launch
     // (blocks past them may belong to sub-tiles that had no rows)
-    hipLaunchKernelGGL(gbwd_reduce_kernel, dim3((unsigned)((n_red + 255) / 256)), blk, 0, s, part, L.n_chunks, F, D,
-                       p1, p2, (Kt + 31) / 32, ds, Kt, dW1, db1, dw2, db2);
+    const int64_t FD = (int64_t)F * D;
+    hipLaunchKernelGGL(gbwd_dw1_sum_kernel, dim3((unsigned)((FD + 255) / 256)), blk, 0, s, part, L.n_chunks, FD, dW1);
+    hipLaunchKernelGGL(gbwd_col_sum_kernel, dim3((unsigned)((F + 63) / 64)), blk, 0, s, p1, p2, (Kt + 31) / 32, F, db1,
+                       dw2);
+    hipLaunchKernelGGL(gbwd_sum_ds_kernel, dim3(1), blk, 0, s, ds, Kt, db2);
     return hipGetLastError();
   }
   float* da = reinterpret_cast<float*>(w + L.off_da);
