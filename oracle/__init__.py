@@ -17,6 +17,7 @@ from .tokengate import (  # noqa: F401
     apply_rope,
     attention_rows_for_check,
     compact,
+    decode_attention,
     gate_scores,
     gate_backward,
     gated_attention,

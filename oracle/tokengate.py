@@ -461,3 +461,41 @@ def score_grad_from_bias(dbias, kept_idx, cu_seqlens, doc_begin, doc_end, T: int
             g[t] += float(dbias[r])
     return g
 
+
+def decode_attention(q, k_cache, v_cache, bias_cache, start, lens, gain, tau: float):
+    """One decode step of token-gated attention over the kept-only KV cache.
+
+    Article, "How does TokenGate learned token pruning work?": layers above
+    the gate never create KV entries for pruned tokens, so generation reads
+    only the kept ones; "What is token-gated attention?": each kept token's
+    score stays its bias.  Reading: the bias is persistent — document keys
+    keep their gate score, question keys and generated keys carry 0 — and the
+    new token sees every cached key of its sequence (including its own,
+    appended before the step).  For sequence b, query head h (KV head
+    ``h // (Hq / Hkv)``) and cache rows ``start[b] .. start[b] + lens[b]``:
+    ``x_j = tau q.k_j / sqrt(d) + g_h bias_j``, ``o = softmax(x) v``,
+    ``lse = log sum exp x``.  ``q`` [B, Hq, d]; caches [rows, Hkv, d] and
+    [rows].  Returns fp64 (o [B, Hq, d], lse [B, Hq]); a sequence of length
+    0 gives NaN.
+    """
+    Q, K, V = _f64(q), _f64(k_cache), _f64(v_cache)
+    s = _f64(bias_cache)
+    B, Hq, d = Q.shape
+    group = Hq // K.shape[1]
+    g = np.zeros(Hq) if gain is None else _f64(gain)
+    scale = float(tau) / math.sqrt(d)
+    o = np.full((B, Hq, d), np.nan)
+    lse = np.full((B, Hq), np.nan)
+    for b in range(B):
+        lo, n = int(start[b]), int(lens[b])
+        if n == 0:
+            continue
+        for h in range(Hq):
+            kv = h // group
+            x = scale * (K[lo:lo + n, kv] @ Q[b, h]) + g[h] * s[lo:lo + n]
+            m = x.max()
+            e = np.exp(x - m)
+            o[b, h] = e @ V[lo:lo + n, kv] / e.sum()
+            lse[b, h] = m + math.log(e.sum())
+    return o, lse
+

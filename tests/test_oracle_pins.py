@@ -778,3 +778,48 @@ def test_score_grad_from_bias_brute_force_and_chain():
         e = np.zeros(10)
         e[t] = 0.25
         assert abs((loss(s + e) - loss(s - e)) / 0.5 - g[t]) <= 1e-5
+
+
+# ------------------------------------------------------------------ decode
+# (slips caught here: the new token not seeing itself, the persistent bias
+# dropped or applied to generated keys, a wrong sequence window)
+
+def test_decode_attention_is_the_last_row_of_the_prefill_attention():
+    # a sequence of n cached keys decoded with query q equals the causal
+    # gated attention's last row when q is that row's query
+    rng = np.random.default_rng(41)
+    n, Hq, Hkv, d = 9, 4, 2, 8
+    q = rng.standard_normal((n, Hq, d))
+    k = rng.standard_normal((n, Hkv, d))
+    v = rng.standard_normal((n, Hkv, d))
+    bias = rng.standard_normal(n)
+    bias[-3:] = 0.0  # question / generated keys
+    gain = rng.uniform(0.5, 2, Hq)
+    o_ref, lse_ref = oracle.gated_attention(q, k, v, bias, gain, 1.2, [0, n])
+    # the cache sits at rows 5.. of a larger buffer; the sequence length is n
+    pad = 5
+    kc = np.concatenate([rng.standard_normal((pad, Hkv, d)), k, rng.standard_normal((3, Hkv, d))])
+    vc = np.concatenate([rng.standard_normal((pad, Hkv, d)), v, rng.standard_normal((3, Hkv, d))])
+    bc = np.concatenate([rng.standard_normal(pad), bias, rng.standard_normal(3)])
+    o, lse = oracle.decode_attention(q[-1:], kc, vc, bc, [pad], [n], gain, 1.2)
+    assert np.max(np.abs(o[0] - o_ref[-1])) <= 1e-12
+    assert np.max(np.abs(lse[0] - lse_ref[:, -1])) <= 1e-12
+
+
+def test_decode_attention_vs_sdpa_and_empty_sequence():
+    rng = np.random.default_rng(42)
+    B, Hq, Hkv, d = 3, 4, 1, 16
+    start, lens = [0, 20, 20], [20, 0, 11]
+    kc, vc = rng.standard_normal((31, Hkv, d)), rng.standard_normal((31, Hkv, d))
+    bc, q = rng.standard_normal(31), rng.standard_normal((B, Hq, d))
+    gain, tau = rng.uniform(0.5, 2, Hq), 0.8
+    o, lse = oracle.decode_attention(q, kc, vc, bc, start, lens, gain, tau)
+    for b in (0, 2):
+        lo, n = start[b], lens[b]
+        mask = torch.tensor(gain)[:, None, None] * torch.tensor(bc[lo:lo + n])[None, None, :]
+        ref = F.scaled_dot_product_attention(
+            torch.tensor(q[b])[:, None, :][None], torch.tensor(kc[lo:lo + n]).permute(1, 0, 2)[None],
+            torch.tensor(vc[lo:lo + n]).permute(1, 0, 2)[None], attn_mask=mask[None],
+            scale=tau / math.sqrt(d), enable_gqa=True)
+        assert np.max(np.abs(o[b] - ref[0, :, 0].numpy())) <= 1e-12
+    assert np.all(np.isnan(o[1])) and np.all(np.isnan(lse[1]))
