@@ -132,6 +132,8 @@ def reference_points(tg, w, gp, layers, outs, hidden, W1, b1, w2, stream, dev):
       * the backward of one gated attention layer (dq, dk, dv and the bias,
         gain and temperature gradients) on the step's kept rows, and the
         gate MLP's backward from the kept rows' bias gradient;
+      * one decode step over the kept rows as a kept-only KV cache (one new
+        query per prompt), with the bytes of cached keys and values it reads;
       * what the chip reaches here on plain library work: a bf16 GEMM of
         8192^3 and a 1 GiB device copy."""
     import torch
@@ -208,6 +210,22 @@ def reference_points(tg, w, gp, layers, outs, hidden, W1, b1, w2, stream, dev):
     r["attn_bwd_us"] = t * 1e3
     r["attn_bwd_TFLOPs"] = 2.5 * work["attn_flop_per_layer"] / (t / 1e3) / 1e12
     del lse0, out0, dout, wsb, grads
+
+    # one decode step of one layer over the kept-only cache (every kept row
+    # of the step, one new query per prompt): HBM-bound, reads each cached
+    # key and value once
+    lens = torch.from_numpy(np.diff(gp.cu_kept_h).astype(np.int32)).to(dev)
+    qd = torch.randn((gp.B, s.Hq, s.d), device=dev).to(q.dtype)
+    wsd = torch.empty(max(16, tg.tg_decode_attn_workspace(gp.B, s.Hq, s.d, gp.max_kept_len)), dtype=torch.uint8,
+                      device=dev)
+    outd = torch.empty_like(qd)
+    dec = lambda: tg.tg_decode_attn(qd, k, v, gp.bias_s, gain, s.tau, gp.cu_kept[:-1], lens,  # noqa: E731
+                                    gp.max_kept_len, out=outd, workspace=wsd)
+    dec()
+    t = time_launches(dec, stream, reps=7, n=10)
+    r["decode_step_us"] = t * 1e3
+    r["decode_step_GBps"] = 2.0 * Kt * s.Hkv * s.d * q.element_size() / (t / 1e3) / 1e9
+    del lens, qd, wsd, outd
 
     # gate MLP backward from the kept rows' bias gradient
     dbias = torch.randn(Kt, device=dev)

@@ -22,6 +22,10 @@
  *                      bias, the gains and the temperature
  *   tg_gate_bwd        backward of the gate MLP from the kept rows' bias
  *                      gradient (the scorer's gradient path)
+ *   tg_kv_scatter      the prefill's kept k, v and bias into a decode cache
+ *   tg_kv_append       a decode step's new k, v into the cache (bias 0)
+ *   tg_decode_attn     one decode step of token-gated attention over the
+ *                      kept-only cache
  *   tg_rope_table      cos / sin of the rotary embedding at the kept rows'
  *                      original positions
  *   tg_qkv_rope        fused q/k/v projection of the kept rows, rotated at
@@ -264,6 +268,57 @@ int tg_gate_bwd(const void* hidden_k, int64_t ld_hidden, int64_t Kt, int D, cons
                 const int32_t* kept_idx, const int32_t* cu_seqlens, const int32_t* doc_begin,
                 const int32_t* doc_end, int B, int dtype, void* dhidden_k, float* dW1, float* db1,
                 float* dw2, float* db2, void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Decode over the kept-only KV cache (section "How does TokenGate learned
+ * token pruning work?": the layers above the gate never create KV entries
+ * for pruned tokens, so generation reads only the kept ones; "What is
+ * token-gated attention?": a kept token's score is its bias).  The bias is
+ * persistent: a document key keeps its gate score, question and generated
+ * keys carry 0.
+ *
+ * Cache of one pruned layer: k_cache, v_cache [rows, Hkv, d] with token
+ * strides cache_k_stride / cache_v_stride (elements, >= Hkv*d, multiples of
+ * 16 bytes), bias_cache [rows] fp32.  Sequence b owns rows start[b] ..
+ * start[b] + len - 1 (start [B] int32, device), with room after them for
+ * its generated tokens; the caller tracks the lengths.
+ *
+ * tg_kv_scatter: kept row r of prompt b (rows [cu_kept[b], cu_kept[b+1]) of
+ * k, v [Kt, Hkv, d] with token strides, bias_s [Kt] or NULL for 0) goes to
+ * cache row start[b] + r - cu_kept[b].
+ */
+int tg_kv_scatter(const void* k, const void* v, int64_t k_tok_stride, int64_t v_tok_stride,
+                  const float* bias_s, const int32_t* cu_kept, int B, int64_t Kt, int Hkv, int d,
+                  int dtype, void* k_cache, void* v_cache, int64_t cache_k_stride,
+                  int64_t cache_v_stride, float* bias_cache, const int32_t* start, void* stream);
+
+/* tg_kv_append: k_new, v_new packed [B, Hkv, d] go to cache row
+ * start[b] + pos[b] (pos [B] int32, device: the length before the step);
+ * their bias is 0. */
+int tg_kv_append(const void* k_new, const void* v_new, int B, int Hkv, int d, int dtype,
+                 void* k_cache, void* v_cache, int64_t cache_k_stride, int64_t cache_v_stride,
+                 float* bias_cache, const int32_t* start, const int32_t* pos, void* stream);
+
+/* Workspace bytes that tg_decode_attn needs. */
+int tg_decode_attn_workspace(int B, int Hq, int d, int max_len, size_t* bytes);
+
+/* One decode step: for sequence b (lens[b] cached keys, the new token's own
+ * included; lens [B] int32, device, each <= max_len), query head h (KV head
+ * h / (Hq / Hkv)):
+ *     x_j = tau * q_bh . k_j / sqrt(d) + gain[h] * bias_cache[j]
+ *     out[b, h] = softmax(x) v,   lse[b, h] = ln sum_j exp(x_j)
+ * q and out packed [B, Hq, d] in dtype; lse [B, Hq] fp32 or NULL; gain
+ * NULL drops the bias term.  A sequence of length 0 gives NaN.  Vector-ALU
+ * kernel (a step reads each cached key once: HBM-bound), fp32 arithmetic,
+ * key splits of 128 merged in a fixed order.  Supported: d in {64, 128},
+ * Hq / Hkv <= 8, max_len <= 65535 * 128; q, caches and workspace 16-byte
+ * aligned.
+ */
+int tg_decode_attn(const void* q, const void* k_cache, const void* v_cache, int64_t cache_k_stride,
+                   int64_t cache_v_stride, const float* bias_cache, const float* gain, float tau,
+                   const int32_t* start, const int32_t* lens, int B, int max_len, int Hq, int Hkv,
+                   int d, int dtype, void* out, float* lse, void* workspace,
+                   size_t workspace_bytes, void* stream);
 
 /* Rotary table of the kept rows (section "How does TokenGate learned token
  * pruning work?": the pruned forward keeps each kept token's original

@@ -27,6 +27,10 @@ from ._lib import (  # noqa: F401
     tg_gated_attn_bwd,
     tg_gated_attn_bwd_workspace,
     tg_gated_attn_fwd,
+    tg_decode_attn,
+    tg_decode_attn_workspace,
+    tg_kv_append,
+    tg_kv_scatter,
     tg_linear_residual,
     tg_plan,
     tg_qkv_rope,

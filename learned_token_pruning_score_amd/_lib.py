@@ -57,6 +57,14 @@ SIGNATURES = {
     "tg_gate_bwd": (_c_int, [_c_vp, _c_i64, _c_i64, _c_int, _c_vp, _c_vp, _c_vp, _c_int, _c_vp, _c_vp,
                              _c_vp, _c_vp, _c_vp, _c_int, _c_int, _c_vp, _c_vp, _c_vp, _c_vp, _c_vp,
                              _c_vp, ctypes.c_size_t, _c_vp]),
+    "tg_kv_scatter": (_c_int, [_c_vp, _c_vp, _c_i64, _c_i64, _c_vp, _c_vp, _c_int, _c_i64, _c_int, _c_int,
+                               _c_int, _c_vp, _c_vp, _c_i64, _c_i64, _c_vp, _c_vp, _c_vp]),
+    "tg_kv_append": (_c_int, [_c_vp, _c_vp, _c_int, _c_int, _c_int, _c_int, _c_vp, _c_vp, _c_i64, _c_i64,
+                              _c_vp, _c_vp, _c_vp, _c_vp]),
+    "tg_decode_attn_workspace": (_c_int, [_c_int, _c_int, _c_int, _c_int, _c_size_p]),
+    "tg_decode_attn": (_c_int, [_c_vp, _c_vp, _c_vp, _c_i64, _c_i64, _c_vp, _c_vp, _c_f32, _c_vp, _c_vp,
+                                _c_int, _c_int, _c_int, _c_int, _c_int, _c_int, _c_vp, _c_vp, _c_vp,
+                                ctypes.c_size_t, _c_vp]),
     "tg_rope_table": (_c_int, [_c_vp, _c_i64, _c_int, ctypes.c_double, _c_vp, _c_vp]),
     "tg_qkv_rope": (_c_int, [_c_vp, _c_i64, _c_i64, _c_int, _c_vp, _c_vp, _c_int, _c_int, _c_int,
                              _c_int, _c_vp, _c_i64, _c_vp]),
@@ -503,4 +511,63 @@ def tg_gate_bwd(hidden_k: torch.Tensor, W1: torch.Tensor, b1: Optional[torch.Ten
         _dev(dW1, "dW1"), _dev(db1, "db1"), _dev(dw2, "dw2"), _dev(db2, "db2"),
         _dev(workspace, "workspace"), workspace.numel() * workspace.element_size(), _stream(stream)))
     return dh, dW1, db1, dw2, db2
+
+
+def tg_kv_scatter(k: torch.Tensor, v: torch.Tensor, bias_s: Optional[torch.Tensor], cu_kept: torch.Tensor,
+                  k_cache: torch.Tensor, v_cache: torch.Tensor, bias_cache: torch.Tensor, start: torch.Tensor,
+                  stream=None) -> None:
+    """Kept rows k, v [Kt, Hkv, d] (ragged by cu_kept) into caches [rows, Hkv, d]
+    at rows start[b] + (r - cu_kept[b]), with their bias."""
+    _require_gpu()
+    Kt, Hkv, d = k.shape
+    B = cu_kept.shape[0] - 1
+    _check("tg_kv_scatter", load_library().tg_kv_scatter(
+        _dev(k, "k"), _dev(v, "v"), k.stride(0) if Kt else Hkv * d, v.stride(0) if Kt else Hkv * d,
+        _dev(bias_s, "bias_s", torch.float32), _dev(cu_kept, "cu_kept", torch.int32), B, Kt, Hkv, d,
+        _dtype_code(k), _dev(k_cache, "k_cache"), _dev(v_cache, "v_cache"), k_cache.stride(0),
+        v_cache.stride(0), _dev(bias_cache, "bias_cache", torch.float32), _dev(start, "start", torch.int32),
+        _stream(stream)))
+
+
+def tg_kv_append(k_new: torch.Tensor, v_new: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
+                 bias_cache: torch.Tensor, start: torch.Tensor, pos: torch.Tensor, stream=None) -> None:
+    """New k, v [B, Hkv, d] into cache rows start[b] + pos[b], bias 0."""
+    _require_gpu()
+    B, Hkv, d = k_new.shape
+    _check("tg_kv_append", load_library().tg_kv_append(
+        _dev(k_new, "k_new"), _dev(v_new, "v_new"), B, Hkv, d, _dtype_code(k_new), _dev(k_cache, "k_cache"),
+        _dev(v_cache, "v_cache"), k_cache.stride(0), v_cache.stride(0),
+        _dev(bias_cache, "bias_cache", torch.float32), _dev(start, "start", torch.int32),
+        _dev(pos, "pos", torch.int32), _stream(stream)))
+
+
+def tg_decode_attn_workspace(B: int, Hq: int, d: int, max_len: int) -> int:
+    n = ctypes.c_size_t(0)
+    _check("tg_decode_attn_workspace",
+           load_library().tg_decode_attn_workspace(B, Hq, d, max_len, ctypes.byref(n)))
+    return int(n.value)
+
+
+def tg_decode_attn(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
+                   bias_cache: Optional[torch.Tensor], gain: Optional[torch.Tensor], tau: float,
+                   start: torch.Tensor, lens: torch.Tensor, max_len: int, out: Optional[torch.Tensor] = None,
+                   lse: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None, stream=None):
+    """One decode step; q [B, Hq, d].  Returns (out [B, Hq, d], lse [B, Hq] or None)."""
+    _require_gpu()
+    B, Hq, d = q.shape
+    Hkv = k_cache.shape[1]
+    if not q.is_contiguous():
+        raise ValueError("q must be packed [B, Hq, d]")
+    if out is None:
+        out = torch.empty_like(q)
+    if workspace is None:
+        workspace = torch.empty(max(16, tg_decode_attn_workspace(B, Hq, d, max_len)), dtype=torch.uint8,
+                                device=q.device)
+    _check("tg_decode_attn", load_library().tg_decode_attn(
+        _dev(q, "q"), _dev(k_cache, "k_cache"), _dev(v_cache, "v_cache"), k_cache.stride(0), v_cache.stride(0),
+        _dev(bias_cache, "bias_cache", torch.float32), _dev(gain, "gain", torch.float32), float(tau),
+        _dev(start, "start", torch.int32), _dev(lens, "lens", torch.int32), B, int(max_len), Hq, Hkv, d,
+        _dtype_code(q), _dev(out, "out"), _dev(lse, "lse", torch.float32), _dev(workspace, "workspace"),
+        workspace.numel() * workspace.element_size(), _stream(stream)))
+    return out, lse
 

@@ -17,7 +17,7 @@ CSRC = os.path.join(PKG_DIR, "csrc")
 BUILD_DIR = os.path.join(PKG_DIR, "_build")
 LIB_NAME = "libtokengate.so"
 LIB_PATH = os.path.join(PKG_DIR, LIB_NAME)
-SOURCES = ["tg_api.hip", "gate.hip", "select.hip", "compact.hip", "attn.hip", "attn_bwd.hip", "proj.hip", "gate_bwd.hip"]
+SOURCES = ["tg_api.hip", "gate.hip", "select.hip", "compact.hip", "attn.hip", "attn_bwd.hip", "proj.hip", "gate_bwd.hip", "decode.hip"]
 ARCH = "gfx950"
 
 HIPCC_FLAGS = [

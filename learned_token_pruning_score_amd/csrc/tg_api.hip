@@ -408,4 +408,70 @@ int tg_gate_bwd(const void* hidden_k, int64_t ld_hidden, int64_t Kt, int D, cons
                                       dw2, db2, workspace, as_stream(stream)));
 }
 
+int tg_kv_scatter(const void* k, const void* v, int64_t k_tok_stride, int64_t v_tok_stride,
+                  const float* bias_s, const int32_t* cu_kept, int B, int64_t Kt, int Hkv, int d,
+                  int dtype, void* k_cache, void* v_cache, int64_t cache_k_stride,
+                  int64_t cache_v_stride, float* bias_cache, const int32_t* start, void* stream) {
+  const int eb = elem_bytes(dtype);
+  if (!eb) return TG_ERR_DTYPE;
+  if (B < 0 || Kt < 0 || Hkv <= 0 || d <= 0 || k_tok_stride < (int64_t)Hkv * d ||
+      v_tok_stride < (int64_t)Hkv * d || cache_k_stride < (int64_t)Hkv * d ||
+      cache_v_stride < (int64_t)Hkv * d)
+    return TG_ERR_SHAPE;
+  if (Kt > 0 && B == 0) return TG_ERR_SHAPE;
+  if (B == 0 || Kt == 0) return TG_OK;
+  if (!k || !v || !cu_kept || !k_cache || !v_cache || !bias_cache || !start) return TG_ERR_NULL;
+  return from_hip(tg::launch_kv_scatter(k, v, k_tok_stride, v_tok_stride, bias_s, cu_kept, B, Kt, Hkv,
+                                        d, eb, k_cache, v_cache, cache_k_stride, cache_v_stride,
+                                        bias_cache, start, as_stream(stream)));
+}
+
+int tg_kv_append(const void* k_new, const void* v_new, int B, int Hkv, int d, int dtype,
+                 void* k_cache, void* v_cache, int64_t cache_k_stride, int64_t cache_v_stride,
+                 float* bias_cache, const int32_t* start, const int32_t* pos, void* stream) {
+  const int eb = elem_bytes(dtype);
+  if (!eb) return TG_ERR_DTYPE;
+  if (B < 0 || Hkv <= 0 || d <= 0 || cache_k_stride < (int64_t)Hkv * d ||
+      cache_v_stride < (int64_t)Hkv * d)
+    return TG_ERR_SHAPE;
+  if (B == 0) return TG_OK;
+  if (!k_new || !v_new || !k_cache || !v_cache || !bias_cache || !start || !pos) return TG_ERR_NULL;
+  return from_hip(tg::launch_kv_append(k_new, v_new, B, Hkv, d, eb, k_cache, v_cache, cache_k_stride,
+                                       cache_v_stride, bias_cache, start, pos, as_stream(stream)));
+}
+
+int tg_decode_attn_workspace(int B, int Hq, int d, int max_len, size_t* bytes) {
+  if (!bytes) return TG_ERR_NULL;
+  if (B < 0 || Hq <= 0 || d <= 0 || max_len < 0) return TG_ERR_SHAPE;
+  *bytes = tg::decode_workspace_bytes(B, Hq, d, max_len);
+  return TG_OK;
+}
+
+int tg_decode_attn(const void* q, const void* k_cache, const void* v_cache, int64_t cache_k_stride,
+                   int64_t cache_v_stride, const float* bias_cache, const float* gain, float tau,
+                   const int32_t* start, const int32_t* lens, int B, int max_len, int Hq, int Hkv,
+                   int d, int dtype, void* out, float* lse, void* workspace,
+                   size_t workspace_bytes, void* stream) {
+  const int eb = elem_bytes(dtype);
+  if (!eb) return TG_ERR_DTYPE;
+  if (B < 0 || max_len < 0 || Hq <= 0 || Hkv <= 0 || d <= 0 || Hq % Hkv != 0 ||
+      cache_k_stride < (int64_t)Hkv * d || cache_v_stride < (int64_t)Hkv * d)
+    return TG_ERR_SHAPE;
+  if (!isfinite(tau) || !(tau > 0.0f)) return TG_ERR_RANGE;
+  if (d != 64 && d != 128) return TG_ERR_UNSUPPORTED;
+  if (Hq / Hkv > 8) return TG_ERR_UNSUPPORTED;  // query heads per KV head held in registers
+  if ((int64_t)B * Hkv > INT32_MAX || (max_len + 127) / 128 > kMaxGridYZ) return TG_ERR_UNSUPPORTED;
+  if (B == 0) return TG_OK;
+  if (!q || !k_cache || !v_cache || !start || !lens || !out) return TG_ERR_NULL;
+  if (gain && !bias_cache) return TG_ERR_NULL;
+  const size_t need = tg::decode_workspace_bytes(B, Hq, d, max_len);
+  if (!workspace || workspace_bytes < need) return TG_ERR_WORKSPACE;
+  if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache) || !aligned16(workspace) ||
+      (cache_k_stride * eb) % 16 != 0 || (cache_v_stride * eb) % 16 != 0)
+    return TG_ERR_ALIGN;
+  return from_hip(tg::launch_decode_attn(q, k_cache, v_cache, cache_k_stride, cache_v_stride,
+                                         bias_cache, gain, tau, start, lens, B, max_len, Hq, Hkv, d,
+                                         eb, out, lse, workspace, as_stream(stream)));
+}
+
 }  // extern "C"

@@ -94,6 +94,16 @@ hipError_t launch_gate_bwd(const void* h, int64_t ld, int64_t Kt, int D, const v
                            const int32_t* cu, const int32_t* db, const int32_t* de, int B, int elem_bytes,
                            void* dh, float* dW1, float* db1, float* dw2, float* db2, void* ws,
                            hipStream_t s);
+size_t decode_workspace_bytes(int B, int Hq, int d, int max_len);
+hipError_t launch_kv_scatter(const void* k, const void* v, int64_t sks, int64_t svs, const float* bias,
+                             const int32_t* cu, int B, int64_t Kt, int Hkv, int d, int elem_bytes, void* kc,
+                             void* vc, int64_t ks, int64_t vs, float* bc, const int32_t* start, hipStream_t s);
+hipError_t launch_kv_append(const void* kn, const void* vn, int B, int Hkv, int d, int elem_bytes, void* kc, void* vc,
+                            int64_t ks, int64_t vs, float* bc, const int32_t* start, const int32_t* pos, hipStream_t s);
+hipError_t launch_decode_attn(const void* q, const void* kc, const void* vc, int64_t ks, int64_t vs, const float* bc,
+                              const float* gain, float tau, const int32_t* start, const int32_t* lens, int B,
+                              int max_len, int Hq, int Hkv, int d, int elem_bytes, void* out, float* lse, void* ws,
+                              hipStream_t s);
 hipError_t launch_rms_norm(const void* x, int64_t ld, int64_t n, int D, const float* w, float eps,
                            int elem_bytes, void* out, int64_t ld_out, hipStream_t s);
 hipError_t launch_linear_residual(const void* a, int64_t ld, int64_t n, int K, const void* W, int N,

@@ -34,7 +34,7 @@ def _declared():
 def test_every_declared_symbol_is_exported_and_typed():
     lib = tg.load_library()
     names = _declared()
-    assert "tg_gate_bwd" in names and "tg_swiglu" in names and len(names) == 18
+    assert "tg_decode_attn" in names and "tg_swiglu" in names and len(names) == 22
     for n in names:
         assert hasattr(lib, n), n
     assert set(names) == set(tg.SIGNATURES)

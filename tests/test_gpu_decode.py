@@ -1,0 +1,162 @@
+"""GPU parity of decode over the kept-only KV cache through the C ABI
+against the CPU fp64 oracle: the cache copies (bit-exact) and the decode
+attention step.
+
+Decode bar per element (the kernel works in fp32 throughout: an exp2 of an
+fp32 logit and fp32 sums, good to about 2^-17 of sum_j P_j |v_j|; the output
+is then rounded once):
+  out:  |Δ| <= 2^-16 sum_j P_j |v_j| + r |ref|   (r = 2^-8 (1 + 2^-6) bf16, 2^-22 fp32)
+  lse:  |Δ| <= 2^-16 max(1, |lse|)
+"""
+
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import learned_token_pruning_score_amd as tg
+import oracle
+import synth
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda"
+
+
+def _note(msg):
+    print(msg, flush=True)
+
+
+def _f64(t):
+    return t.detach().to("cpu").to(torch.float64).numpy()
+
+
+def _check_decode(out, lse, q, kc, vc, bc, start, lens, gain, tau, dtype):
+    o_ref, lse_ref = oracle.decode_attention(_f64(q), _f64(kc), _f64(vc), _f64(bc), start, lens,
+                                             None if gain is None else _f64(gain), tau)
+    Q, K, V, S = _f64(q), _f64(kc), _f64(vc), _f64(bc)
+    B, Hq, d = Q.shape
+    grp = Hq // K.shape[1]
+    g = np.zeros(Hq) if gain is None else _f64(gain)
+    r = 2.0 ** -8 * (1 + 2.0 ** -6) if dtype == torch.bfloat16 else 2.0 ** -22
+    got, gl = _f64(out), _f64(lse)
+    worst = 0.0
+    for b in range(B):
+        lo, n = int(start[b]), int(lens[b])
+        for h in range(Hq):
+            x = tau / math.sqrt(d) * (K[lo:lo + n, h // grp] @ Q[b, h]) + g[h] * S[lo:lo + n]
+            P = np.exp(x - x.max())
+            P /= P.sum()
+            tol = 2.0 ** -16 * (P @ np.abs(V[lo:lo + n, h // grp])) + r * np.abs(o_ref[b, h])
+            err = np.abs(got[b, h] - o_ref[b, h])
+            assert np.all(err <= tol), f"out[{b},{h}]: max err {err.max()}, bar {tol[np.argmax(err)]}"
+            worst = max(worst, float(np.max(err / tol)))
+            assert abs(gl[b, h] - lse_ref[b, h]) <= 2.0 ** -16 * max(1.0, abs(lse_ref[b, h])), (b, h)
+    return worst
+
+
+def _cache(rows, Hkv, d, dtype, g):
+    kc = torch.randn((rows, Hkv, d), generator=g).to(dtype)
+    vc = torch.randn((rows, Hkv, d), generator=g).to(dtype)
+    bc = torch.randn(rows, generator=g)
+    bc[::5] = 0.0
+    return kc, vc, bc
+
+
+# (sequence lengths, Hq, Hkv, d, dtype): ragged with a one-key sequence and
+# split boundaries (256 keys); GQA groups 1, 2, 3, 8; d 128 and 64; fp32
+CASES = [
+    ([700, 1, 300], 16, 8, 128, torch.bfloat16, True),
+    ([257, 1024], 6, 2, 64, torch.bfloat16, True),
+    ([5000], 8, 1, 128, torch.bfloat16, False),
+    ([33, 260], 4, 4, 64, torch.float32, True),
+]
+
+
+@pytest.mark.parametrize("lens,Hq,Hkv,d,dtype,with_bias", CASES)
+def test_decode_attn_parity(lens, Hq, Hkv, d, dtype, with_bias):
+    _note(f"[decode] lens={lens} Hq={Hq} Hkv={Hkv} d={d} {dtype}")
+    g = torch.Generator().manual_seed(sum(lens) + Hq)
+    gap = 37
+    start = np.cumsum([0] + [n + gap for n in lens[:-1]]).astype(np.int32)
+    rows = int(start[-1] + lens[-1] + gap)
+    kc, vc, bc = _cache(rows, Hkv, d, dtype, g)
+    q = torch.randn((len(lens), Hq, d), generator=g).to(dtype)
+    gain = torch.rand(Hq, generator=g) * 1.5 + 0.5 if with_bias else None
+    tau = 1.15
+    out, lse = tg.tg_decode_attn(q.to(DEV), kc.to(DEV), vc.to(DEV), bc.to(DEV),
+                                 None if gain is None else gain.to(DEV), tau,
+                                 torch.from_numpy(start).to(DEV), torch.tensor(lens, dtype=torch.int32, device=DEV),
+                                 max(lens), lse=torch.empty((len(lens), Hq), device=DEV))
+    torch.cuda.synchronize()
+    w = _check_decode(out, lse, q, kc, vc, bc if with_bias else torch.zeros_like(bc), start, lens, gain, tau, dtype)
+    _note(f"  worst error / bar {w:.3f}")
+
+
+def test_decode_steps_from_prefill_cache():
+    """The ragged workload's kept layout: the prefill's kept k, v and bias
+    scattered into a cache with room per sequence, then 5 decode steps each
+    appending a token (bias 0) and attending over the whole cache."""
+    name = "ragged_small_bf16"
+    _note(f"[decode steps] {name}")
+    w = synth.make_workload(name, seed=4, with_hidden=False)
+    s = w.spec
+    cu_kept, _ = oracle.plan(w.cu_seqlens, w.doc_begin, w.doc_end, w.budget)
+    cu = np.asarray(cu_kept, dtype=np.int64)
+    B, Kt = len(cu) - 1, int(cu[-1])
+    q0, k0, v0, gain = synth.attention_inputs(s, 0, Kt, seed=4)
+    g = torch.Generator().manual_seed(4)
+    bias0 = torch.randn(Kt, generator=g)
+    steps = 5
+    start = (cu[:-1] + np.arange(B) * steps).astype(np.int32)
+    rows = Kt + B * steps
+    kc = torch.zeros((rows, s.Hkv, s.d), dtype=k0.dtype, device=DEV)
+    vc = torch.zeros_like(kc)
+    bc = torch.full((rows,), 9.0, device=DEV)
+    startd = torch.from_numpy(start).to(DEV)
+    tg.tg_kv_scatter(k0.to(DEV), v0.to(DEV), bias0.to(DEV), torch.from_numpy(cu.astype(np.int32)).to(DEV),
+                     kc, vc, bc, startd)
+    # the same cache built on the host
+    Kh = torch.zeros((rows, s.Hkv, s.d), dtype=k0.dtype)
+    Vh = torch.zeros_like(Kh)
+    Bh = torch.full((rows,), 9.0)
+    for b in range(B):
+        n = int(cu[b + 1] - cu[b])
+        Kh[start[b]:start[b] + n] = k0[cu[b]:cu[b + 1]]
+        Vh[start[b]:start[b] + n] = v0[cu[b]:cu[b + 1]]
+        Bh[start[b]:start[b] + n] = bias0[cu[b]:cu[b + 1]]
+    lens = np.diff(cu).astype(np.int32)
+    for step in range(steps):
+        kn = torch.randn((B, s.Hkv, s.d), generator=g).to(k0.dtype)
+        vn = torch.randn((B, s.Hkv, s.d), generator=g).to(k0.dtype)
+        qn = torch.randn((B, s.Hq, s.d), generator=g).to(k0.dtype)
+        tg.tg_kv_append(kn.to(DEV), vn.to(DEV), kc, vc, bc, startd, torch.from_numpy(lens).to(DEV))
+        for b in range(B):
+            Kh[start[b] + lens[b]] = kn[b]
+            Vh[start[b] + lens[b]] = vn[b]
+            Bh[start[b] + lens[b]] = 0.0
+        lens = lens + 1
+        out, lse = tg.tg_decode_attn(qn.to(DEV), kc, vc, bc, gain.to(DEV), s.tau, startd,
+                                     torch.from_numpy(lens).to(DEV), int(lens.max()),
+                                     lse=torch.empty((B, s.Hq), device=DEV))
+        torch.cuda.synchronize()
+        assert torch.equal(kc.cpu(), Kh) and torch.equal(vc.cpu(), Vh) and torch.equal(bc.cpu(), Bh), step
+        _check_decode(out, lse, qn, Kh, Vh, Bh, start, lens, gain, s.tau, k0.dtype)
+
+
+def test_decode_full_size_128k():
+    """One decode step over the 128k workload's 8448 kept keys, 16 heads."""
+    _note("[decode full] 8448 keys")
+    g = torch.Generator().manual_seed(8)
+    n, Hq, Hkv, d = 8448, 16, 8, 128
+    kc, vc, bc = _cache(n + 64, Hkv, d, torch.bfloat16, g)
+    q = torch.randn((1, Hq, d), generator=g).to(torch.bfloat16)
+    gain = torch.rand(Hq, generator=g) + 0.5
+    start, lens = np.array([0], dtype=np.int32), [n]
+    out, lse = tg.tg_decode_attn(q.to(DEV), kc.to(DEV), vc.to(DEV), bc.to(DEV), gain.to(DEV), 1.15,
+                                 torch.from_numpy(start).to(DEV), torch.tensor(lens, dtype=torch.int32, device=DEV),
+                                 n, lse=torch.empty((1, Hq), device=DEV))
+    torch.cuda.synchronize()
+    w = _check_decode(out, lse, q, kc, vc, bc, start, lens, gain, 1.15, torch.bfloat16)
+    _note(f"  worst error / bar {w:.3f}")
