@@ -26,9 +26,11 @@ from .tokengate import (  # noqa: F401
     plan,
     pruned_layer,
     qkv_rope,
+    random_k_keep,
     rms_norm,
     rope_inv_freq,
     round_f32,
+    sample_budgets,
     score_grad_from_bias,
     select_topk,
     swiglu,

@@ -499,3 +499,30 @@ def decode_attention(q, k_cache, v_cache, bias_cache, start, lens, gain, tau: fl
             lse[b, h] = m + math.log(e.sum())
     return o, lse
 
+
+def sample_budgets(doc_begin, doc_end, u, min_frac: float, max_frac: float) -> np.ndarray:
+    """Random document budgets for a training step's random-budget loss.
+
+    Article, "What is token-gated attention?": each training step averages a
+    full-context loss and a random-budget loss, so one gate works across
+    budgets.  Reading (the article gives no distribution): prompt b keeps the
+    fraction ``f_b = min_frac + (max_frac - min_frac) u_b`` of its document,
+    ``u_b`` in [0, 1) drawn by the caller, and its budget is
+    ``floor(f_b * doc_len_b)`` (fp64).  The full-context loss is the budget
+    ``doc_len_b`` (f = 1).
+    """
+    db, de = _i64(doc_begin), _i64(doc_end)
+    uu = _f64(u)
+    f = float(min_frac) + (float(max_frac) - float(min_frac)) * uu
+    return np.floor(f * (de - db)).astype(np.int64)
+
+
+def random_k_keep(rand_keys, cu_seqlens, doc_begin, doc_end, budget) -> np.ndarray:
+    """Random-K selection (article, "How does TokenGate perform on
+    benchmarks?": the ablation that keeps K random document tokens instead of
+    the K best-scored ones).  Reading: with i.i.d. uniform keys ``rand_keys``
+    [T] drawn by the caller, the top-K of the keys (``select_topk`` on them)
+    is a uniformly random K-subset of each document; the question is kept as
+    always.  The kept tokens' attention bias is still their gate score."""
+    return select_topk(rand_keys, cu_seqlens, doc_begin, doc_end, budget)
+

@@ -823,3 +823,38 @@ def test_decode_attention_vs_sdpa_and_empty_sequence():
             scale=tau / math.sqrt(d), enable_gqa=True)
         assert np.max(np.abs(o[b] - ref[0, :, 0].numpy())) <= 1e-12
     assert np.all(np.isnan(o[1])) and np.all(np.isnan(lse[1]))
+
+
+# ------------------------------------------------------- selection variants
+
+def test_sample_budgets_hand_values_and_range():
+    db, de = [0, 10, 0], [100, 10, 7]
+    u = [0.0, 0.5, 0.999]
+    b = oracle.sample_budgets(db, de, u, 0.25, 0.75)
+    # f = 0.25, 0.5, 0.7495: floor(25.0), floor(0 * 0.5), floor(7 * 0.7495) = 25, 0, 5
+    assert b.tolist() == [25, 0, 5]
+    rng = np.random.default_rng(51)
+    lens = rng.integers(0, 5000, 200)
+    uu = rng.random(200)
+    bb = oracle.sample_budgets(np.zeros(200), lens, uu, 0.0, 1.0)
+    assert np.all(bb >= 0) and np.all(bb <= lens)
+    assert np.array_equal(oracle.sample_budgets(np.zeros(200), lens, np.zeros(200), 1.0, 1.0), lens)
+
+
+def test_random_k_is_a_uniform_subset_of_each_document():
+    # every document token is kept with probability K / doc_len (binomial
+    # count over many seeded draws within 5 standard deviations); the
+    # question is always kept; exactly K document tokens per prompt
+    cu, db, de, bud = [0, 12, 20], [0, 2], [10, 6], [3, 1]
+    counts = np.zeros(20)
+    n = 4000
+    rng = np.random.default_rng(52)
+    for _ in range(n):
+        keep = oracle.random_k_keep(rng.random(20).astype(np.float32), cu, db, de, bud)
+        assert keep[10] and keep[11] and keep[12] and keep[13] and all(keep[18:20])
+        assert keep[0:10].sum() == 3 and keep[14:18].sum() == 1
+        counts += keep
+    for lo, hi, k in ((0, 10, 3), (14, 18, 1)):
+        p = k / (hi - lo)
+        sd = math.sqrt(n * p * (1 - p))
+        assert np.all(np.abs(counts[lo:hi] - n * p) <= 5 * sd), counts[lo:hi]
