@@ -13,6 +13,8 @@
  * phases two and three:
  *
  *   tg_plan            host-only sizes of the kept set (no device work)
+ *   tg_sample_budgets  host-only random document budgets (training's
+ *                      random-budget loss)
  *   tg_gate_score      gate MLP score of every token
  *   tg_select_topk     per-prompt top-K over the document span -> keep flags
  *   tg_compact         stable gather of kept rows, positions and biases
@@ -98,6 +100,21 @@ const char* tg_status_string(int status);
 int tg_plan(int B, const int32_t* cu_seqlens_h, const int32_t* doc_begin_h,
             const int32_t* doc_end_h, const int32_t* budget_h,
             int32_t* cu_kept_h, int32_t* max_kept_len_h);
+
+/*
+ * Random document budgets (host only; section "What is token-gated
+ * attention?": each training step averages a full-context loss and a
+ * random-budget loss).  Prompt b keeps the fraction
+ *     f_b = min_frac + (max_frac - min_frac) * u_h[b]
+ * of its document: budget_h[b] = floor(f_b * (doc_end_h[b] - doc_begin_h[b]))
+ * in double precision.  u_h [B]: the caller's uniform draws in [0, 1).
+ * 0 <= min_frac <= max_frac <= 1, else TG_ERR_RANGE.  Random-K selection
+ * (the ablation that keeps K random document tokens) needs no call of its
+ * own: tg_select_topk over i.i.d. uniform keys keeps a uniformly random
+ * K-subset of each document; the compaction still takes the gate scores.
+ */
+int tg_sample_budgets(int B, const int32_t* doc_begin_h, const int32_t* doc_end_h,
+                      const float* u_h, float min_frac, float max_frac, int32_t* budget_h);
 
 /*
  * Gate score of every token (article, "How does TokenGate learned token

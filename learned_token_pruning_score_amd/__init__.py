@@ -36,6 +36,7 @@ from ._lib import (  # noqa: F401
     tg_qkv_rope,
     tg_rms_norm,
     tg_rope_table,
+    tg_sample_budgets,
     tg_select_topk,
     tg_select_topk_workspace,
     tg_swiglu,

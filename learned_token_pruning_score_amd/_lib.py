@@ -65,6 +65,8 @@ SIGNATURES = {
     "tg_decode_attn": (_c_int, [_c_vp, _c_vp, _c_vp, _c_i64, _c_i64, _c_vp, _c_vp, _c_f32, _c_vp, _c_vp,
                                 _c_int, _c_int, _c_int, _c_int, _c_int, _c_int, _c_vp, _c_vp, _c_vp,
                                 ctypes.c_size_t, _c_vp]),
+    "tg_sample_budgets": (_c_int, [_c_int, _c_i32_p, _c_i32_p, ctypes.POINTER(ctypes.c_float), _c_f32, _c_f32,
+                                   _c_i32_p]),
     "tg_rope_table": (_c_int, [_c_vp, _c_i64, _c_int, ctypes.c_double, _c_vp, _c_vp]),
     "tg_qkv_rope": (_c_int, [_c_vp, _c_i64, _c_i64, _c_int, _c_vp, _c_vp, _c_int, _c_int, _c_int,
                              _c_int, _c_vp, _c_i64, _c_vp]),
@@ -570,4 +572,18 @@ def tg_decode_attn(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor
         _dtype_code(q), _dev(out, "out"), _dev(lse, "lse", torch.float32), _dev(workspace, "workspace"),
         workspace.numel() * workspace.element_size(), _stream(stream)))
     return out, lse
+
+
+def tg_sample_budgets(doc_begin, doc_end, u, min_frac: float, max_frac: float) -> np.ndarray:
+    """Random document budgets (host): floor((min_frac + (max_frac -
+    min_frac) u_b) * doc_len_b) for the caller's uniform draws u in [0, 1)."""
+    db = np.ascontiguousarray(doc_begin, dtype=np.int32)
+    de = np.ascontiguousarray(doc_end, dtype=np.int32)
+    uu = np.ascontiguousarray(u, dtype=np.float32)
+    out = np.empty(db.shape[0], dtype=np.int32)
+    p = lambda a, t: a.ctypes.data_as(ctypes.POINTER(t))  # noqa: E731
+    _check("tg_sample_budgets", load_library().tg_sample_budgets(
+        int(db.shape[0]), p(db, ctypes.c_int32), p(de, ctypes.c_int32), p(uu, ctypes.c_float),
+        float(min_frac), float(max_frac), p(out, ctypes.c_int32)))
+    return out
 

@@ -78,6 +78,24 @@ int tg_plan(int B, const int32_t* cu_seqlens_h, const int32_t* doc_begin_h,
   return TG_OK;
 }
 
+int tg_sample_budgets(int B, const int32_t* doc_begin_h, const int32_t* doc_end_h,
+                      const float* u_h, float min_frac, float max_frac, int32_t* budget_h) {
+  if (B < 0) return TG_ERR_SHAPE;
+  if (B > 0 && (!doc_begin_h || !doc_end_h || !u_h || !budget_h)) return TG_ERR_NULL;
+  if (!isfinite(min_frac) || !isfinite(max_frac) || !(min_frac >= 0.0f) || !(max_frac <= 1.0f) ||
+      min_frac > max_frac)
+    return TG_ERR_RANGE;
+  for (int b = 0; b < B; ++b) {
+    if (doc_end_h[b] < doc_begin_h[b] || doc_begin_h[b] < 0) return TG_ERR_SHAPE;
+    if (!(u_h[b] >= 0.0f && u_h[b] < 1.0f)) return TG_ERR_RANGE;
+  }
+  for (int b = 0; b < B; ++b) {
+    const double f = (double)min_frac + ((double)max_frac - (double)min_frac) * (double)u_h[b];
+    budget_h[b] = (int32_t)floor(f * (double)(doc_end_h[b] - doc_begin_h[b]));
+  }
+  return TG_OK;
+}
+
 int tg_gate_score(const void* hidden, int64_t ld_hidden, int64_t T, int D, const void* W1,
                   const float* b1, const float* w2, float b2, int F, int dtype, float* scores,
                   void* stream) {

@@ -59,10 +59,15 @@ class GatedPrefill:
 
     def gate_and_select(self, hidden: torch.Tensor, W1: torch.Tensor, b1: Optional[torch.Tensor],
                         w2: torch.Tensor, b2: float, pos: Optional[torch.Tensor] = None,
-                        stream=None) -> None:
-        """Score every token, pick the kept set, compact rows/positions/biases."""
+                        rand_keys: Optional[torch.Tensor] = None, stream=None) -> None:
+        """Score every token, pick the kept set, compact rows/positions/biases.
+
+        With ``rand_keys`` [T] (i.i.d. uniform draws, fp32) the kept set is
+        random-K: the top-K of the random keys instead of the scores; the
+        kept tokens' bias is still their score."""
         _lib.tg_gate_score(hidden, W1, b1, w2, b2, scores=self.scores, stream=stream)
-        _lib.tg_select_topk(self.scores, self.cu_seqlens, self.doc_begin, self.doc_end,
+        keys = self.scores if rand_keys is None else rand_keys
+        _lib.tg_select_topk(keys, self.cu_seqlens, self.doc_begin, self.doc_end,
                             self.budget, keep=self.keep, workspace=self.ws_select, stream=stream)
         _lib.tg_compact(hidden, pos, self.scores, self.keep, self.cu_seqlens, self.doc_begin,
                         self.doc_end, self.Kt,

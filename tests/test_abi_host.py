@@ -34,7 +34,7 @@ def _declared():
 def test_every_declared_symbol_is_exported_and_typed():
     lib = tg.load_library()
     names = _declared()
-    assert "tg_decode_attn" in names and "tg_swiglu" in names and len(names) == 22
+    assert "tg_sample_budgets" in names and "tg_swiglu" in names and len(names) == 23
     for n in names:
         assert hasattr(lib, n), n
     assert set(names) == set(tg.SIGNATURES)
@@ -259,3 +259,27 @@ def test_layer_argument_checks():
     assert sw(FAKE, 2048, 10, 2048, FAKE, FAKE + 8, 6144, 1, FAKE, 6144, None) == TG_ERR_ALIGN
     assert sw(None, 2048, 0, 2048, None, None, 6144, 1, None, 6144, None) == TG_OK
 
+
+
+def test_sample_budgets_matches_oracle_and_rejects():
+    rng = np.random.default_rng(61)
+    B = 300
+    db = rng.integers(0, 100, B).astype(np.int32)
+    de = (db + rng.integers(0, 40000, B)).astype(np.int32)
+    u = rng.random(B).astype(np.float32)
+    for lo, hi in ((0.0, 1.0), (0.05, 0.3), (1.0, 1.0), (0.5, 0.5)):
+        got = tg.tg_sample_budgets(db, de, u, lo, hi)
+        exp = oracle.sample_budgets(db, de, u.astype(np.float64), np.float32(lo), np.float32(hi))
+        assert np.array_equal(got, exp), (lo, hi)
+    lib = tg.load_library()
+    f = lib.tg_sample_budgets
+    one = (ctypes.c_int32 * 1)(0)
+    ten = (ctypes.c_int32 * 1)(10)
+    uu = (ctypes.c_float * 1)(0.5)
+    out = (ctypes.c_int32 * 1)(-7)
+    assert f(1, one, ten, uu, 0.6, 0.4, out) == TG_ERR_RANGE and out[0] == -7
+    assert f(1, one, ten, uu, -0.1, 0.4, out) == TG_ERR_RANGE
+    assert f(1, one, ten, (ctypes.c_float * 1)(1.0), 0.1, 0.4, out) == TG_ERR_RANGE
+    assert f(1, ten, one, uu, 0.1, 0.4, out) == TG_ERR_SHAPE
+    assert f(1, None, ten, uu, 0.1, 0.4, out) == TG_ERR_NULL
+    assert f(0, None, None, None, 0.1, 0.4, None) == TG_OK
