@@ -198,7 +198,8 @@ def reference_points(tg, w, gp, layers, outs, hidden, W1, b1, w2, stream, dev):
     lse0 = torch.empty((s.Hq, Kt), dtype=torch.float32, device=dev)
     out0, _ = tg.tg_gated_attn_fwd(q, k, v, gp.bias_s, gain, s.tau, gp.cu_kept, gp.max_kept_len, lse=lse0)
     dout = torch.randn(out0.shape, device=dev).to(out0.dtype)
-    wsb = torch.empty(max(16, tg.tg_gated_attn_bwd_workspace(gp.B, Kt, s.Hq, gp.max_kept_len)),
+    wsb = torch.empty(max(16, tg.tg_gated_attn_bwd_workspace(gp.B, Kt, s.Hq, s.Hkv, s.d, q.dtype,
+                                                             gp.max_kept_len)),
                       dtype=torch.uint8, device=dev)
     grads = (torch.empty_like(q), torch.empty_like(k), torch.empty_like(v),
              torch.empty(Kt, dtype=torch.float32, device=dev), torch.empty(s.Hq, dtype=torch.float32, device=dev),

@@ -216,8 +216,10 @@ int tg_gated_attn_fwd(const void* q, const void* k, const void* v,
                       int B, int max_kept_len, int64_t Kt, int Hq, int Hkv,
                       int d, int dtype, void* out, float* lse, void* stream);
 
-/* Workspace bytes that tg_gated_attn_bwd needs. */
-int tg_gated_attn_bwd_workspace(int B, int64_t Kt, int Hq, int max_kept_len, size_t* bytes);
+/* Workspace bytes that tg_gated_attn_bwd needs for these shapes and dtype
+ * (bf16 with Hq > Hkv adds 2 Hq Kt d fp32 per-head dK and dV sums). */
+int tg_gated_attn_bwd_workspace(int B, int64_t Kt, int Hq, int Hkv, int d, int dtype,
+                                int max_kept_len, size_t* bytes);
 
 /*
  * Backward of tg_gated_attn_fwd (section "What is token-gated attention?":

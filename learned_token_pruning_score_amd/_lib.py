@@ -48,7 +48,7 @@ SIGNATURES = {
     "tg_gated_attn_fwd": (_c_int, [_c_vp, _c_vp, _c_vp, _c_i64, _c_i64, _c_i64, _c_vp, _c_vp,
                                    _c_f32, _c_vp, _c_int, _c_int, _c_i64, _c_int, _c_int, _c_int,
                                    _c_int, _c_vp, _c_vp, _c_vp]),
-    "tg_gated_attn_bwd_workspace": (_c_int, [_c_int, _c_i64, _c_int, _c_int, _c_size_p]),
+    "tg_gated_attn_bwd_workspace": (_c_int, [_c_int, _c_i64, _c_int, _c_int, _c_int, _c_int, _c_int, _c_size_p]),
     "tg_gated_attn_bwd": (_c_int, [_c_vp, _c_vp, _c_vp, _c_i64, _c_i64, _c_i64, _c_vp, _c_vp,
                                    _c_f32, _c_vp, _c_int, _c_int, _c_i64, _c_int, _c_int, _c_int,
                                    _c_int, _c_vp, _c_vp, _c_vp, _c_vp, _c_vp, _c_vp, _c_vp, _c_vp,
@@ -425,10 +425,12 @@ def tg_swiglu(h: torch.Tensor, w_gate: torch.Tensor, w_up: torch.Tensor,
     return out
 
 
-def tg_gated_attn_bwd_workspace(B: int, Kt: int, Hq: int, max_kept_len: int) -> int:
+def tg_gated_attn_bwd_workspace(B: int, Kt: int, Hq: int, Hkv: int, d: int, dtype: torch.dtype,
+                                max_kept_len: int) -> int:
     n = ctypes.c_size_t(0)
     _check("tg_gated_attn_bwd_workspace",
-           load_library().tg_gated_attn_bwd_workspace(B, Kt, Hq, max_kept_len, ctypes.byref(n)))
+           load_library().tg_gated_attn_bwd_workspace(B, Kt, Hq, Hkv, d, TG_BF16 if dtype == torch.bfloat16 else TG_F32,
+                                                      max_kept_len, ctypes.byref(n)))
     return int(n.value)
 
 
@@ -459,7 +461,7 @@ def tg_gated_attn_bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
                  torch.empty(1, dtype=torch.float32, device=dev))
     dq, dk, dv, db, dg, dt = grads
     if workspace is None:
-        workspace = torch.empty(max(16, tg_gated_attn_bwd_workspace(B, Kt, Hq, max_kept_len)),
+        workspace = torch.empty(max(16, tg_gated_attn_bwd_workspace(B, Kt, Hq, Hkv, d, q.dtype, max_kept_len)),
                                 dtype=torch.uint8, device=q.device)
     _check("tg_gated_attn_bwd", lib.tg_gated_attn_bwd(
         _dev(q, "q"), _dev(k, "k"), _dev(v, "v"), q.stride(0) if Kt else Hq * d,

@@ -23,15 +23,17 @@
 //              forward's value product); partial sums of dx q.k for dtau.
 //   bwd_dkdv   key-parallel: one workgroup of 4 waves per (KV head, prompt,
 //              128-key tile), 32 keys per wave; for each head of the group and
-//              each 64-row query tile S = Q K^T and dP = dO V^T (lane = key,
-//              queries in registers), dV^T += dO^T P and dK^T += Q^T dx with
-//              transposing reads of dO and Q; column sums c_hj of dx in fp32.
+//              each 64-row query tile S = Q K^T (lane = key, queries in
+//              registers), then in one pass dV^T += dO^T P, in a second
+//              dP = dO V^T and dK^T += Q^T dx with transposing reads of dO and
+//              Q; column sums c_hj of dx in fp32.
 //   bwd_final  ds and dg from c_hj, dtau from the partial sums.
 // fp32 path: one thread per (query, head) for dq and per (key, KV head) for
 // dk / dv, on vector ALUs.
 #include <math.h>
 
 #include <algorithm>
+#include <type_traits>
 
 #include "tg_common.h"
 
@@ -51,9 +53,23 @@ __device__ __forceinline__ uint32_t lds_addr(const void* p) {
   return (uint32_t)(uintptr_t)(__attribute__((address_space(3))) const char*)(reinterpret_cast<const char*>(p));
 }
 
-// 16-byte fragment of a row-major staged tile: row r (of 64), 16-byte unit c.
-__device__ __forceinline__ bf16x8 frag_row(uint32_t base, int row_units, int r, int c) {
-  return __builtin_bit_cast(bf16x8, *(lds_u4v*)(uintptr_t)(base + (r * row_units + c) * 16));
+// 16-byte fragment of a row-major staged tile, read from a per-lane base
+// address (row lane % 32, 16-byte unit lane / 32) plus a compile-time byte
+// offset (rows and units further on), which the LDS instruction carries as
+// its immediate: one address register per staged tile instead of one per
+// read.
+__device__ __forceinline__ bf16x8 frag_at(uint32_t lane_base, uint32_t off) {
+  return __builtin_bit_cast(bf16x8, *(lds_u4v*)(uintptr_t)(lane_base + off));
+}
+
+// A pointer every lane of the wave holds, moved to scalar registers so that
+// the buffer descriptors built from it are known to be uniform.
+template <typename T>
+__device__ __forceinline__ const T* wave_uniform(const T* p) {
+  const uint64_t u = reinterpret_cast<uint64_t>(p);
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)u);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(u >> 32));
+  return reinterpret_cast<const T*>(((uint64_t)hi << 32) | lo);
 }
 
 // Transposed fragment of a row-major staged tile with rows of ROWT 16-byte
@@ -218,8 +234,10 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(
   float rs = 0.0f;
   auto prefetch = [&](int k0) __attribute__((always_inline)) {
     const int rows = __builtin_amdgcn_readfirstlane(max(min(n - k0, kT), 0));
-    const __amdgpu_buffer_rsrc_t r1 = __builtin_amdgcn_make_buffer_rsrc((void*)(kbase + (int64_t)k0 * ks), (short)0, rows * (int)ks * 2, kBufFlagsB);
-    const __amdgpu_buffer_rsrc_t r2 = __builtin_amdgcn_make_buffer_rsrc((void*)(vbase + (int64_t)k0 * vs), (short)0, rows * (int)vs * 2, kBufFlagsB);
+    const __amdgpu_buffer_rsrc_t r1 = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)wave_uniform(kbase + (int64_t)k0 * ks), (short)0, rows * (int)ks * 2, kBufFlagsB);
+    const __amdgpu_buffer_rsrc_t r2 = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)wave_uniform(vbase + (int64_t)k0 * vs), (short)0, rows * (int)vs * 2, kBufFlagsB);
 #pragma unroll
     for (int j = 0; j < ITEMS; ++j) {
       rk[j] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r1, offk[j], 0, 0));
@@ -237,9 +255,9 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(
     }
     if (tid < kT) sS[tid] = rs;
   };
-  const uint32_t kb_n = lds_addr(sK), vb_n = lds_addr(sV);
+  uint32_t kl = lds_addr(sK) + ((lane & 31) * ROWN + G) * 16, vl = lds_addr(sV) + ((lane & 31) * ROWN + G) * 16;
   uint32_t ktb = tr_lane_base<ROWT>(sKT, lane);
-  asm volatile("" : "+v"(ktb));
+  asm volatile("" : "+v"(ktb), "+v"(kl), "+v"(vl));
 
   // Two workgroups share a CU: while one stages a tile (global loads, then
   // LDS writes, between two barriers), the other computes.
@@ -261,8 +279,8 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(
     for (int st = 0; st < NKS; ++st)
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb) {
-        sa[kb] = mfma32x32x16(frag_row(kb_n, ROWN, 32 * kb + (lane & 31), 2 * st + G), qf[st], sa[kb]);
-        sb[kb] = mfma32x32x16(frag_row(vb_n, ROWN, 32 * kb + (lane & 31), 2 * st + G), gf[st], sb[kb]);
+        sa[kb] = mfma32x32x16(frag_at(kl, (32 * kb * ROWN + 2 * st) * 16), qf[st], sa[kb]);
+        sb[kb] = mfma32x32x16(frag_at(vl, (32 * kb * ROWN + 2 * st) * 16), gf[st], sb[kb]);
       }
     bf16x8 pb[2][2];
 #pragma unroll
@@ -291,20 +309,36 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(
 }
 
 // ----------------------------------------------------------------- dk, dv
-template <int HD>
-__global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(
+// Two passes over the same query tiles, each light enough for two workgroups
+// per CU: DK = false accumulates dV^T += dO^T P (it needs only S); DK = true
+// accumulates dK^T += Q^T dx and the column sums of dx (it needs S and dP).
+// Recomputing S in both costs one product in five and halves the registers
+// each pass holds.  One workgroup per query head: a key tile's longest chain
+// is then one head's query tiles, not the whole group's, and the grid has
+// Hq (not Hkv) workgroups per key tile.  With a group of several heads each
+// writes its fp32 sums to part [Hq][Kt][HD] and bwd_group_sum adds the
+// group's in head order; with one head per group the workgroup stores the
+// bf16 rows itself (part == nullptr).
+template <int HD, bool DK>
+__global__ __launch_bounds__(256, 2) void bwd_dkdv_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
     int64_t qs, int64_t ks, int64_t vs, const float* __restrict__ bias, const float* __restrict__ gain,
     float tau, const int32_t* __restrict__ cu, int Hq, int Hkv, int group, int64_t Kt,
     const uint16_t* __restrict__ dout, const float* __restrict__ lse, const float* __restrict__ Dv,
-    uint16_t* __restrict__ dk, uint16_t* __restrict__ dv, float* __restrict__ colsum) {
+    uint16_t* __restrict__ dkv, float* __restrict__ part, float* __restrict__ colsum) {
   constexpr int KCH = HD / 8, NKS = HD / 16, NDB = HD / 32;
   constexpr int ROWN = KCH + 1, ROWT = KCH + 4;
   constexpr int ITEMS = kT * KCH / 256;
-  __shared__ uint4 sQ[kT * ROWN], sQT[kT * ROWT], sO[kT * ROWN], sOT[kT * ROWT];
-  __shared__ float sL[kT], sD[kT];
+  // DK: sQ (normal), sO (normal), sQT (transposing reads); dV: sQ, sOT
+  __shared__ uint4 sm[DK ? kT * (2 * ROWN + ROWT) : kT * (ROWN + ROWT)];
+  __shared__ __align__(16) float sL[kT];
+  __shared__ __align__(16) float sD[DK ? kT : 4];
+  uint4* const sQ = sm;
+  uint4* const sX = sm + kT * ROWN;  // sO (DK) or sOT (dV)
+  uint4* const sQT = sm + 2 * kT * ROWN;
 
-  const int kvh = blockIdx.x;
+  const int h = blockIdx.x;
+  const int kvh = h / group;
   const int b = blockIdx.y;
   const int tile = blockIdx.z;  // the first key tiles see the most queries: launched first
   const int lo = cu[b];
@@ -319,27 +353,29 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(
   const bool k_ok = my_k < n;
   const float c1 = tau * rsqrtf((float)HD) * kLog2eB;
 
-  bf16x8 kf[NKS], vf[NKS];
+  bf16x8 kf[NKS], vf[DK ? NKS : 1];
   {
     const uint16_t* kp = k + (int64_t)(lo + my_k) * ks + (int64_t)kvh * HD + 8 * G;
     const uint16_t* vp = v + (int64_t)(lo + my_k) * vs + (int64_t)kvh * HD + 8 * G;
 #pragma unroll
     for (int s = 0; s < NKS; ++s) {
-      uint4 a = make_uint4(0, 0, 0, 0), c = a;
-      if (k_ok) {
-        a = *reinterpret_cast<const uint4*>(kp + 16 * s);
-        c = *reinterpret_cast<const uint4*>(vp + 16 * s);
-      }
+      uint4 a = make_uint4(0, 0, 0, 0);
+      if (k_ok) a = *reinterpret_cast<const uint4*>(kp + 16 * s);
       kf[s] = as_bf16x8(a);
-      vf[s] = as_bf16x8(c);
+      if constexpr (DK) {
+        uint4 c = make_uint4(0, 0, 0, 0);
+        if (k_ok) c = *reinterpret_cast<const uint4*>(vp + 16 * s);
+        vf[s] = as_bf16x8(c);
+      }
     }
   }
   const float sj = (bias && k_ok) ? bias[lo + my_k] : 0.0f;
-  f32x16 ak[NDB], av[NDB];
+  const float bj = (bias && gain) ? gain[h] * kLog2eB * sj : 0.0f;
+  f32x16 acc[NDB];
 #pragma unroll
   for (int db = 0; db < NDB; ++db)
 #pragma unroll
-    for (int i = 0; i < 16; ++i) ak[db][i] = av[db][i] = 0.0f;
+    for (int i = 0; i < 16; ++i) acc[db][i] = 0.0f;
 
   const int t_first = k0w / kT;
   const int n_qtl = (n + kT - 1) / kT;
@@ -355,9 +391,9 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(
   auto prefetch = [&](int h, int i0) __attribute__((always_inline)) {
     const int rows = __builtin_amdgcn_readfirstlane(max(min(n - i0, kT), 0));
     const __amdgpu_buffer_rsrc_t r1 = __builtin_amdgcn_make_buffer_rsrc(
-        (void*)(q + (int64_t)(lo + i0) * qs + (int64_t)h * HD), (short)0, rows * (int)qs * 2, kBufFlagsB);
+        (void*)wave_uniform(q + (int64_t)(lo + i0) * qs + (int64_t)h * HD), (short)0, rows * (int)qs * 2, kBufFlagsB);
     const __amdgpu_buffer_rsrc_t r2 = __builtin_amdgcn_make_buffer_rsrc(
-        (void*)(dout + ((int64_t)(lo + i0) * Hq + h) * HD), (short)0, rows * Hq * HD * 2, kBufFlagsB);
+        (void*)wave_uniform(dout + ((int64_t)(lo + i0) * Hq + h) * HD), (short)0, rows * Hq * HD * 2, kBufFlagsB);
 #pragma unroll
     for (int j = 0; j < ITEMS; ++j) {
       rq[j] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r1, offq[j], 0, 0));
@@ -366,7 +402,7 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(
     if (tid < kT) {
       const bool ok = i0 + tid < n;
       rl = ok ? lse[(int64_t)h * Kt + lo + i0 + tid] * kLog2eB : 0.0f;
-      rd = ok ? Dv[(int64_t)h * Kt + lo + i0 + tid] : 0.0f;
+      if constexpr (DK) rd = ok ? Dv[(int64_t)h * Kt + lo + i0 + tid] : 0.0f;
     }
   };
   auto stage = [&]() __attribute__((always_inline)) {
@@ -374,98 +410,138 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(
     for (int j = 0; j < ITEMS; ++j) {
       const int id = tid + 256 * j;
       sQ[(id / KCH) * ROWN + id % KCH] = rq[j];
-      sQT[(id / KCH) * ROWT + id % KCH] = rq[j];
-      sO[(id / KCH) * ROWN + id % KCH] = ro[j];
-      sOT[(id / KCH) * ROWT + id % KCH] = ro[j];
+      if constexpr (DK) {
+        sQT[(id / KCH) * ROWT + id % KCH] = rq[j];
+        sX[(id / KCH) * ROWN + id % KCH] = ro[j];
+      } else {
+        sX[(id / KCH) * ROWT + id % KCH] = ro[j];
+      }
     }
     if (tid < kT) {
       sL[tid] = rl;
-      sD[tid] = rd;
+      if constexpr (DK) sD[tid] = rd;
     }
   };
-  const uint32_t qb_n = lds_addr(sQ), ob_n = lds_addr(sO);
-  uint32_t qtb = tr_lane_base<ROWT>(sQT, lane), otb = tr_lane_base<ROWT>(sOT, lane);
-  asm volatile("" : "+v"(qtb), "+v"(otb));
+  uint32_t ql = lds_addr(sQ) + ((lane & 31) * ROWN + G) * 16, ol = lds_addr(sX) + ((lane & 31) * ROWN + G) * 16;
+  // transposing reads: of Q for dK, of dO for dV
+  uint32_t trb = DK ? tr_lane_base<ROWT>(sQT, lane) : tr_lane_base<ROWT>(sX, lane);
+  asm volatile("" : "+v"(trb), "+v"(ql));
+  if constexpr (DK) asm volatile("" : "+v"(ol));
 
-  const int n_steps = group * (n_qtl - t_first);  // (head, query tile) pairs, head-major
-  prefetch(kvh * group, t_first * kT);
   float csum = 0.0f;
-  for (int st_i = 0; st_i < n_steps; ++st_i) {
-    const int hh = st_i / (n_qtl - t_first);
-    const int h = kvh * group + hh;
-    const int t = t_first + st_i % (n_qtl - t_first);
-    __syncthreads();
-    stage();
-    if (st_i + 1 < n_steps) {
-      const int hn = kvh * group + (st_i + 1) / (n_qtl - t_first);
-      const int tn = t_first + (st_i + 1) % (n_qtl - t_first);
-      prefetch(hn, tn * kT);
-    }
-    __syncthreads();
+  // last query tile first: every workgroup starts on the same tiles at the
+  // same time and walks down in near lockstep, so each staged Q / dO tile
+  // is fetched from memory once per L2 and reused by the others
+  for (int t = n_qtl - 1; t >= t_first; --t) {
     const int i0 = t * kT;
+    prefetch(h, i0);
+    __syncthreads();  // every wave is done with the previous tile
+    stage();
+    __syncthreads();
     const bool active = (kw < n) && (i0 + kT - 1 >= kw);  // some query of the tile sees a key of the wave
+    // every query of the tile sees every key of the wave, all of them valid
+    const bool full = (i0 >= kw + 31) && (i0 + kT <= n) && (kw + 32 <= n);
     if (active) {
-      const float gb = (bias && gain) ? gain[h] * kLog2eB : 0.0f;
-      const float bj = gb * sj;
-      float pr[2][16], dxr[2][16];
-      {
-        f32x16 a0, a1, b0, b1;
+      // the tile's two 32-query halves one after the other (one S / dP
+      // accumulator pair live at a time): P (dV) or dx (DK) of half qb is
+      // the B operand of the 16-row steps 2 qb, 2 qb + 1
 #pragma unroll
-        for (int i = 0; i < 16; ++i) a0[i] = a1[i] = b0[i] = b1[i] = 0.0f;
+      for (int qb = 0; qb < 2; ++qb) {
+        f32x16 sa, sb;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) sa[i] = sb[i] = 0.0f;
 #pragma unroll
         for (int st = 0; st < NKS; ++st) {
-          const bf16x8 q0f = frag_row(qb_n, ROWN, lane & 31, 2 * st + G);
-          const bf16x8 q1f = frag_row(qb_n, ROWN, 32 + (lane & 31), 2 * st + G);
-          const bf16x8 o0f = frag_row(ob_n, ROWN, lane & 31, 2 * st + G);
-          const bf16x8 o1f = frag_row(ob_n, ROWN, 32 + (lane & 31), 2 * st + G);
-          a0 = mfma32x32x16(q0f, kf[st], a0);
-          a1 = mfma32x32x16(q1f, kf[st], a1);
-          b0 = mfma32x32x16(o0f, vf[st], b0);
-          b1 = mfma32x32x16(o1f, vf[st], b1);
+          sa = mfma32x32x16(frag_at(ql, (32 * qb * ROWN + 2 * st) * 16), kf[st], sa);
+          if constexpr (DK) sb = mfma32x32x16(frag_at(ol, (32 * qb * ROWN + 2 * st) * 16), vf[st], sb);
         }
+        // registers 4 r4 .. 4 r4 + 3 hold rows qr0 .. qr0 + 3: their lse
+        // (and D) in one 16-byte LDS read; the exponent is evaluated for
+        // every element and masked by a select (no branch around the read)
+        bf16x8 xb[2];
+        auto elems = [&](auto masked) __attribute__((always_inline)) {
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const int r0 = acc_row(i, lane);
+          for (int r4 = 0; r4 < 4; ++r4) {
+            const int qr0 = qb * 32 + acc_row(4 * r4, lane);
+            const float4 L4 = *reinterpret_cast<const float4*>(sL + qr0);
+            float4 D4 = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+            if constexpr (DK) D4 = *reinterpret_cast<const float4*>(sD + qr0);
+            const float Lr[4] = {L4.x, L4.y, L4.z, L4.w}, Dr[4] = {D4.x, D4.y, D4.z, D4.w};
 #pragma unroll
-          for (int qb = 0; qb < 2; ++qb) {
-            const int qr = qb * 32 + r0;
-            const float sv = qb ? a1[i] : a0[i];
-            const float dpv = qb ? b1[i] : b0[i];
-            const bool ok = k_ok && (i0 + qr >= my_k) && (i0 + qr < n);
-            const float p = ok ? __builtin_amdgcn_exp2f(fmaf(sv, c1, bj) - sL[qr]) : 0.0f;
-            pr[qb][i] = p;
-            dxr[qb][i] = p * (dpv - sD[qr]);
-            csum += dxr[qb][i];
+            for (int j = 0; j < 4; ++j) {
+              const int i = 4 * r4 + j;
+              float p = __builtin_amdgcn_exp2f(fmaf(sa[i], c1, bj) - Lr[j]);
+              if constexpr (decltype(masked)::value) {
+                const int qi = i0 + qr0 + j;
+                p = (k_ok & (qi >= my_k) & (qi < n)) ? p : 0.0f;
+              }
+              float x = p;
+              if constexpr (DK) {
+                x = p * (sb[i] - Dr[j]);
+                csum += x;
+              }
+              xb[i >> 3][i & 7] = (__bf16)x;
+            }
           }
-        }
+        };
+        if (full)
+          elems(std::false_type{});
+        else
+          elems(std::true_type{});
+#pragma unroll
+        for (int r16 = 0; r16 < 2; ++r16)
+#pragma unroll
+          for (int db = 0; db < NDB; ++db)
+            acc[db] = mfma32x32x16(frag_tr<ROWT>(trb, 2 * qb + r16, db), xb[r16], acc[db]);
       }
-      bf16x8 pb[2][2], xb[2][2];
-      to_b_operand(pr, pb);
-      to_b_operand(dxr, xb);
-#pragma unroll
-      for (int kh = 0; kh < 4; ++kh)
-#pragma unroll
-        for (int db = 0; db < NDB; ++db) {
-          av[db] = mfma32x32x16(frag_tr<ROWT>(otb, kh, db), pb[kh >> 1][kh & 1], av[db]);
-          ak[db] = mfma32x32x16(frag_tr<ROWT>(qtb, kh, db), xb[kh >> 1][kh & 1], ak[db]);
-        }
     }
-    if (t == n_qtl - 1) {  // last query tile of head h: its column sums are complete
-      const float c = pair_sum(csum);
-      if (k_ok && G == 0) colsum[(int64_t)h * Kt + lo + my_k] = c;
-      csum = 0.0f;
-    }
+  }
+  if constexpr (DK) {
+    const float c = pair_sum(csum);
+    if (k_ok && G == 0) colsum[(int64_t)h * Kt + lo + my_k] = c;
   }
   if (!k_ok) return;
-  const float scale = tau * rsqrtf((float)HD);
-  uint16_t* kp = dk + ((int64_t)(lo + my_k) * Hkv + kvh) * HD;
-  uint16_t* vp = dv + ((int64_t)(lo + my_k) * Hkv + kvh) * HD;
+  if (part) {
+    float* pp = part + ((int64_t)h * Kt + lo + my_k) * HD;
 #pragma unroll
-  for (int db = 0; db < NDB; ++db) {
-    store_bf16_rows(kp + 32 * db, ak[db], scale, G);
-    store_bf16_rows(vp + 32 * db, av[db], 1.0f, G);
+    for (int db = 0; db < NDB; ++db)
+#pragma unroll
+      for (int g4 = 0; g4 < 4; ++g4)
+        *reinterpret_cast<float4*>(pp + 32 * db + 8 * g4 + 4 * G) =
+            make_float4(acc[db][4 * g4], acc[db][4 * g4 + 1], acc[db][4 * g4 + 2], acc[db][4 * g4 + 3]);
+    return;
   }
+  const float scale = DK ? tau * rsqrtf((float)HD) : 1.0f;
+  uint16_t* op = dkv + ((int64_t)(lo + my_k) * Hkv + kvh) * HD;
+#pragma unroll
+  for (int db = 0; db < NDB; ++db) store_bf16_rows(op + 32 * db, acc[db], scale, G);
 }
+
+// out[r][kvh][e] = bf16(mul * sum_(hh < group) part[kvh group + hh][r][e]),
+// heads in order; 4 elements per thread.
+__global__ __launch_bounds__(256) void bwd_group_sum_kernel(const float* __restrict__ part, int64_t Kt, int Hkv,
+                                                            int group, int d, float mul, uint16_t* __restrict__ out) {
+  const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;  // (row, kvh, 4-element chunk)
+  const int nc = d / 4;
+  if (idx >= Kt * Hkv * nc) return;
+  const int64_t r = idx / ((int64_t)Hkv * nc);
+  const int rem = (int)(idx - r * Hkv * nc);
+  const int kvh = rem / nc, c = rem % nc;
+  float4 a = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+  for (int hh = 0; hh < group; ++hh) {
+    const float4 x = *reinterpret_cast<const float4*>(part + ((int64_t)(kvh * group + hh) * Kt + r) * d + 4 * c);
+    a.x += x.x;
+    a.y += x.y;
+    a.z += x.z;
+    a.w += x.w;
+  }
+  const unsigned w0 = (unsigned)__builtin_bit_cast(uint16_t, (__bf16)(a.x * mul)) |
+                      ((unsigned)__builtin_bit_cast(uint16_t, (__bf16)(a.y * mul)) << 16);
+  const unsigned w1 = (unsigned)__builtin_bit_cast(uint16_t, (__bf16)(a.z * mul)) |
+                      ((unsigned)__builtin_bit_cast(uint16_t, (__bf16)(a.w * mul)) << 16);
+  *reinterpret_cast<uint2*>(out + ((r * Hkv + kvh) * d + 4 * c)) = make_uint2(w0, w1);
+}
+
 
 // ------------------------------------------------------------- fp32 paths
 __global__ __launch_bounds__(256) void bwd_dq_f32_kernel(
@@ -606,10 +682,14 @@ size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 }  // namespace
 
-size_t attn_bwd_workspace_bytes(int B, int64_t Kt, int Hq, int max_len) {
+// D, column sums, dtau partials; bf16 with several heads per KV head: the
+// per-head fp32 dK and dV sums
+size_t attn_bwd_workspace_bytes(int B, int64_t Kt, int Hq, int Hkv, int d, int elem_bytes, int max_len) {
   const int64_t n_qt = ((int64_t)max_len + 127) / 128;
   const int64_t n_part = std::max<int64_t>((int64_t)Hq * B * n_qt * 4, Kt * Hq);
-  return 2 * align256((size_t)Hq * Kt * 4) + align256((size_t)n_part * 4);
+  size_t bytes = 2 * align256((size_t)Hq * Kt * 4) + align256((size_t)n_part * 4);
+  if (elem_bytes == 2 && Hq != Hkv) bytes += 2 * align256((size_t)Hq * Kt * d * 4);
+  return bytes;
 }
 
 hipError_t launch_attn_bwd(const void* q, const void* k, const void* v, int64_t qs, int64_t ks, int64_t vs,
@@ -622,6 +702,10 @@ hipError_t launch_attn_bwd(const void* q, const void* k, const void* v, int64_t 
   float* colsum = reinterpret_cast<float*>(w + align256((size_t)Hq * Kt * 4));
   float* tpart = reinterpret_cast<float*>(w + 2 * align256((size_t)Hq * Kt * 4));
   const int group = Hq / Hkv;
+  const size_t head_off = 2 * align256((size_t)Hq * Kt * 4) +
+                          align256((size_t)std::max<int64_t>((int64_t)Hq * B * ((max_len + 127) / 128) * 4, Kt * Hq) * 4);
+  float* part_k = group > 1 ? reinterpret_cast<float*>(w + head_off) : nullptr;
+  float* part_v = group > 1 ? reinterpret_cast<float*>(w + head_off + align256((size_t)Hq * Kt * d * 4)) : nullptr;
   const int64_t rows = Kt * Hq;
   const bool has_bias = bias && gain;
   if (elem_bytes == 2)
@@ -641,17 +725,28 @@ hipError_t launch_attn_bwd(const void* q, const void* k, const void* v, int64_t 
     const auto* vp = static_cast<const uint16_t*>(v);
     const auto* gp = static_cast<const uint16_t*>(dout);
     const dim3 gq((unsigned)Hq, (unsigned)B, (unsigned)n_qt);
-    const dim3 gk((unsigned)Hkv, (unsigned)B, (unsigned)n_qt);
+    const dim3 gk((unsigned)Hq, (unsigned)B, (unsigned)n_qt);
     if (d == 128) {
       hipLaunchKernelGGL(bwd_dq_kernel<128>, gq, dim3(256), 0, s, qp, kp, vp, qs, ks, vs, bias, gain, tau, cu, Hq,
                          group, n_qt, Kt, gp, lse, Dv, static_cast<uint16_t*>(dq), tpart);
-      hipLaunchKernelGGL(bwd_dkdv_kernel<128>, gk, dim3(256), 0, s, qp, kp, vp, qs, ks, vs, bias, gain, tau, cu, Hq,
-                         Hkv, group, Kt, gp, lse, Dv, static_cast<uint16_t*>(dk), static_cast<uint16_t*>(dv), colsum);
+      hipLaunchKernelGGL((bwd_dkdv_kernel<128, false>), gk, dim3(256), 0, s, qp, kp, vp, qs, ks, vs, bias, gain, tau,
+                         cu, Hq, Hkv, group, Kt, gp, lse, Dv, static_cast<uint16_t*>(dv), part_v, colsum);
+      hipLaunchKernelGGL((bwd_dkdv_kernel<128, true>), gk, dim3(256), 0, s, qp, kp, vp, qs, ks, vs, bias, gain, tau,
+                         cu, Hq, Hkv, group, Kt, gp, lse, Dv, static_cast<uint16_t*>(dk), part_k, colsum);
     } else {
       hipLaunchKernelGGL(bwd_dq_kernel<64>, gq, dim3(256), 0, s, qp, kp, vp, qs, ks, vs, bias, gain, tau, cu, Hq,
                          group, n_qt, Kt, gp, lse, Dv, static_cast<uint16_t*>(dq), tpart);
-      hipLaunchKernelGGL(bwd_dkdv_kernel<64>, gk, dim3(256), 0, s, qp, kp, vp, qs, ks, vs, bias, gain, tau, cu, Hq,
-                         Hkv, group, Kt, gp, lse, Dv, static_cast<uint16_t*>(dk), static_cast<uint16_t*>(dv), colsum);
+      hipLaunchKernelGGL((bwd_dkdv_kernel<64, false>), gk, dim3(256), 0, s, qp, kp, vp, qs, ks, vs, bias, gain, tau,
+                         cu, Hq, Hkv, group, Kt, gp, lse, Dv, static_cast<uint16_t*>(dv), part_v, colsum);
+      hipLaunchKernelGGL((bwd_dkdv_kernel<64, true>), gk, dim3(256), 0, s, qp, kp, vp, qs, ks, vs, bias, gain, tau,
+                         cu, Hq, Hkv, group, Kt, gp, lse, Dv, static_cast<uint16_t*>(dk), part_k, colsum);
+    }
+    if (group > 1) {
+      const unsigned nb = (unsigned)((Kt * Hkv * (d / 4) + 255) / 256);
+      hipLaunchKernelGGL(bwd_group_sum_kernel, dim3(nb), dim3(256), 0, s, part_v, Kt, Hkv, group, d, 1.0f,
+                         static_cast<uint16_t*>(dv));
+      hipLaunchKernelGGL(bwd_group_sum_kernel, dim3(nb), dim3(256), 0, s, part_k, Kt, Hkv, group, d,
+                         tau / sqrtf((float)d), static_cast<uint16_t*>(dk));
     }
   } else {
     n_part = rows;

@@ -336,10 +336,13 @@ int tg_swiglu(const void* h, int64_t ld_h, int64_t n, int D, const void* w_gate,
                                     as_stream(stream)));
 }
 
-int tg_gated_attn_bwd_workspace(int B, int64_t Kt, int Hq, int max_kept_len, size_t* bytes) {
+int tg_gated_attn_bwd_workspace(int B, int64_t Kt, int Hq, int Hkv, int d, int dtype, int max_kept_len,
+                                size_t* bytes) {
   if (!bytes) return TG_ERR_NULL;
-  if (B < 0 || Kt < 0 || Hq <= 0 || max_kept_len < 0) return TG_ERR_SHAPE;
-  *bytes = tg::attn_bwd_workspace_bytes(B, Kt, Hq, max_kept_len);
+  const int eb = elem_bytes(dtype);
+  if (!eb) return TG_ERR_DTYPE;
+  if (B < 0 || Kt < 0 || Hq <= 0 || Hkv <= 0 || Hq % Hkv != 0 || d <= 0 || max_kept_len < 0) return TG_ERR_SHAPE;
+  *bytes = tg::attn_bwd_workspace_bytes(B, Kt, Hq, Hkv, d, eb, max_kept_len);
   return TG_OK;
 }
 
@@ -371,7 +374,7 @@ int tg_gated_attn_bwd(const void* q, const void* k, const void* v, int64_t q_tok
   if (B == 0 || Kt == 0) return TG_OK;
   if (!q || !k || !v || !cu_kept || !out || !lse || !dout || !dq || !dk || !dv) return TG_ERR_NULL;
   if (gain && !bias_s) return TG_ERR_NULL;
-  const size_t need = tg::attn_bwd_workspace_bytes(B, Kt, Hq, max_kept_len);
+  const size_t need = tg::attn_bwd_workspace_bytes(B, Kt, Hq, Hkv, d, eb, max_kept_len);
   if (!workspace || workspace_bytes < need) return TG_ERR_WORKSPACE;
   if (!aligned16(workspace)) return TG_ERR_ALIGN;
   if (dtype == TG_BF16) {

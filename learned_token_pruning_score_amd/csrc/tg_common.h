@@ -77,7 +77,7 @@ hipError_t launch_rope_table(const int32_t* pos, int64_t n, int d, double theta,
 hipError_t launch_qkv_rope_bf16(const void* x, int64_t ld, int64_t Kt, int D, const void* W,
                                 const float* rope, int Hq, int Hkv, int d, void* out,
                                 int64_t ld_out, hipStream_t s);
-size_t attn_bwd_workspace_bytes(int B, int64_t Kt, int Hq, int max_len);
+size_t attn_bwd_workspace_bytes(int B, int64_t Kt, int Hq, int Hkv, int d, int elem_bytes, int max_len);
 hipError_t launch_attn_bwd(const void* q, const void* k, const void* v, int64_t qs, int64_t ks, int64_t vs,
                            const float* bias, const float* gain, float tau, const int32_t* cu, int B,
                            int max_len, int64_t Kt, int Hq, int Hkv, int d, int elem_bytes, const void* out,
