@@ -129,7 +129,8 @@ __device__ __forceinline__ float wave_sum(float x) {
   return x;
 }
 
-// D[h][i] = dout_i . o_i (fp32), one thread per (row, head).
+// D[h][i] = dout_i . o_i (fp32 accumulation), one thread per (row, head):
+// the fp32 path.
 template <typename T>
 __global__ __launch_bounds__(256) void bwd_prep_kernel(const T* __restrict__ o, const T* __restrict__ dout,
                                                        int64_t Kt, int Hq, int d, float* __restrict__ D) {
@@ -157,6 +158,36 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(const T* __restrict__ o, 
   D[(int64_t)h * Kt + i] = acc;
 }
 
+// D[h][i] in bf16: TPR = d / 8 consecutive lanes per (row, head), one
+// 16-byte chunk of out and dout each (coalesced), then a fixed-order
+// butterfly over the TPR lanes.
+template <int TPR>
+__global__ __launch_bounds__(256) void bwd_prep_bf16_kernel(const uint16_t* __restrict__ o,
+                                                            const uint16_t* __restrict__ dout, int64_t Kt,
+                                                            int Hq, float* __restrict__ D) {
+  const int64_t gid = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const int64_t idx = gid / TPR;  // (row, head)
+  const int part = (int)(gid % TPR);
+  const bool ok = idx < Kt * Hq;
+  float acc = 0.0f;
+  if (ok) {
+    const uint4 a = *reinterpret_cast<const uint4*>(o + idx * (8 * TPR) + 8 * part);
+    const uint4 b = *reinterpret_cast<const uint4*>(dout + idx * (8 * TPR) + 8 * part);
+    const uint32_t av[4] = {a.x, a.y, a.z, a.w}, bv[4] = {b.x, b.y, b.z, b.w};
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      acc = fmaf(__uint_as_float(av[j] << 16), __uint_as_float(bv[j] << 16), acc);
+      acc = fmaf(__uint_as_float(av[j] & 0xffff0000u), __uint_as_float(bv[j] & 0xffff0000u), acc);
+    }
+  }
+#pragma unroll
+  for (int off = TPR / 2; off >= 1; off >>= 1) acc += __shfl_xor(acc, off);
+  if (ok && part == 0) {
+    const int64_t i = idx / Hq;
+    D[(int64_t)(idx - i * Hq) * Kt + i] = acc;
+  }
+}
+
 // ------------------------------------------------------------------- dq
 template <int HD>
 __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(
@@ -169,7 +200,7 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(
   constexpr int ROWN = KCH + 1, ROWT = KCH + 4;
   constexpr int ITEMS = kT * KCH / 256;  // 16-byte chunks per thread per tile (K, V each)
   __shared__ uint4 sK[kT * ROWN], sKT[kT * ROWT], sV[kT * ROWN];
-  __shared__ float sS[kT];
+  __shared__ __align__(16) float sS[kT];  // g_h log2(e) s_j of the tile's keys
 
   const int h = blockIdx.x;
   const int b = blockIdx.y;
@@ -243,7 +274,7 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(
       rk[j] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r1, offk[j], 0, 0));
       rv[j] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r2, offv[j], 0, 0));
     }
-    if (tid < kT) rs = (bias && k0 + tid < n) ? bias[lo + k0 + tid] : 0.0f;
+    if (tid < kT) rs = (bias && k0 + tid < n) ? gb * bias[lo + k0 + tid] : 0.0f;
   };
   auto stage = [&]() __attribute__((always_inline)) {
 #pragma unroll
@@ -268,36 +299,48 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(
     __syncthreads();
     const int k0 = t * kT;
     if (k0 > qw + 31 || qw >= n) continue;  // the tile lies past every row of this wave
-    // S^T (sa) and dP^T (sb) of the two 32-key blocks, then dx^T straight
-    // into the bf16 B operand of dQ^T += K^T dx^T
-    f32x16 sa[2], sb[2];
+    // the tile's two 32-key blocks one after the other (one S^T / dP^T
+    // accumulator pair live at a time); dx^T of block kb goes straight into
+    // the bf16 B operand of the 16-key steps 2 kb, 2 kb + 1 of dQ^T += K^T dx^T
+    const bool full = (k0 + kT - 1 <= qw) && (qw + 32 <= n);  // no mask in this tile
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
+    for (int kb = 0; kb < 2; ++kb) {
+      f32x16 sa, sb;
 #pragma unroll
-      for (int i = 0; i < 16; ++i) sa[kb][i] = sb[kb][i] = 0.0f;
+      for (int i = 0; i < 16; ++i) sa[i] = sb[i] = 0.0f;
 #pragma unroll
-    for (int st = 0; st < NKS; ++st)
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
-        sa[kb] = mfma32x32x16(frag_at(kl, (32 * kb * ROWN + 2 * st) * 16), qf[st], sa[kb]);
-        sb[kb] = mfma32x32x16(frag_at(vl, (32 * kb * ROWN + 2 * st) * 16), gf[st], sb[kb]);
+      for (int st = 0; st < NKS; ++st) {
+        sa = mfma32x32x16(frag_at(kl, (32 * kb * ROWN + 2 * st) * 16), qf[st], sa);
+        sb = mfma32x32x16(frag_at(vl, (32 * kb * ROWN + 2 * st) * 16), gf[st], sb);
       }
-    bf16x8 pb[2][2];
+      bf16x8 pb[2];
+      auto elems = [&](auto masked) __attribute__((always_inline)) {
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
+        for (int r4 = 0; r4 < 4; ++r4) {
+          const int key0 = kb * 32 + acc_row(4 * r4, lane);  // registers 4 r4 .. +3: keys key0 .. key0 + 3
+          const float4 B4 = *reinterpret_cast<const float4*>(sS + key0);
+          const float Br[4] = {B4.x, B4.y, B4.z, B4.w};
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const int key = kb * 32 + acc_row(i, lane);
-        const float x2 = fmaf(sa[kb][i], c1, gb * sS[key]);
-        const float p = (q_ok && k0 + key <= my_q) ? __builtin_amdgcn_exp2f(x2 - lse2) : 0.0f;
-        const float dxv = p * (sb[kb][i] - Di);
-        tsum = fmaf(dxv, sa[kb][i], tsum);
-        pb[kb][i >> 3][i & 7] = (__bf16)dxv;
-      }
+          for (int j = 0; j < 4; ++j) {
+            const int i = 4 * r4 + j;
+            float p = __builtin_amdgcn_exp2f(fmaf(sa[i], c1, Br[j]) - lse2);
+            if constexpr (decltype(masked)::value) p = (q_ok & (k0 + key0 + j <= my_q)) ? p : 0.0f;
+            const float dxv = p * (sb[i] - Di);
+            tsum = fmaf(dxv, sa[i], tsum);
+            pb[i >> 3][i & 7] = (__bf16)dxv;
+          }
+        }
+      };
+      if (full)
+        elems(std::false_type{});
+      else
+        elems(std::true_type{});
 #pragma unroll
-    for (int kh = 0; kh < 4; ++kh)
+      for (int r16 = 0; r16 < 2; ++r16)
 #pragma unroll
-      for (int db = 0; db < NDB; ++db) acc[db] = mfma32x32x16(frag_tr<ROWT>(ktb, kh, db), pb[kh >> 1][kh & 1], acc[db]);
+        for (int db = 0; db < NDB; ++db)
+          acc[db] = mfma32x32x16(frag_tr<ROWT>(ktb, 2 * kb + r16, db), pb[r16], acc[db]);
+    }
   }
   const float tw = wave_sum(tsum);
   if (lane == 0) tp[wave] = tw;
@@ -708,9 +751,12 @@ hipError_t launch_attn_bwd(const void* q, const void* k, const void* v, int64_t 
   float* part_v = group > 1 ? reinterpret_cast<float*>(w + head_off + align256((size_t)Hq * Kt * d * 4)) : nullptr;
   const int64_t rows = Kt * Hq;
   const bool has_bias = bias && gain;
-  if (elem_bytes == 2)
-    hipLaunchKernelGGL(bwd_prep_kernel<uint16_t>, dim3((unsigned)((rows + 255) / 256)), dim3(256), 0, s,
-                       static_cast<const uint16_t*>(out), static_cast<const uint16_t*>(dout), Kt, Hq, d, Dv);
+  if (elem_bytes == 2 && d == 128)
+    hipLaunchKernelGGL(bwd_prep_bf16_kernel<16>, dim3((unsigned)((rows * 16 + 255) / 256)), dim3(256), 0, s,
+                       static_cast<const uint16_t*>(out), static_cast<const uint16_t*>(dout), Kt, Hq, Dv);
+  else if (elem_bytes == 2)
+    hipLaunchKernelGGL(bwd_prep_bf16_kernel<8>, dim3((unsigned)((rows * 8 + 255) / 256)), dim3(256), 0, s,
+                       static_cast<const uint16_t*>(out), static_cast<const uint16_t*>(dout), Kt, Hq, Dv);
   else
     hipLaunchKernelGGL(bwd_prep_kernel<float>, dim3((unsigned)((rows + 255) / 256)), dim3(256), 0, s,
                        static_cast<const float*>(out), static_cast<const float*>(dout), Kt, Hq, d, Dv);
