@@ -115,12 +115,16 @@ def _check(fn: str, status: int) -> None:
         raise TokenGateError(fn, status)
 
 
-def _dtype_code(t: torch.Tensor) -> int:
-    if t.dtype == torch.bfloat16:
+def _dtype_code_of(dtype: torch.dtype) -> int:
+    if dtype == torch.bfloat16:
         return TG_BF16
-    if t.dtype == torch.float32:
+    if dtype == torch.float32:
         return TG_F32
-    raise TypeError(f"unsupported dtype {t.dtype}")
+    raise TypeError(f"unsupported dtype {dtype}")
+
+
+def _dtype_code(t: torch.Tensor) -> int:
+    return _dtype_code_of(t.dtype)
 
 
 def _dev(t: Optional[torch.Tensor], name: str, dtype=None) -> int:
@@ -429,8 +433,8 @@ def tg_gated_attn_bwd_workspace(B: int, Kt: int, Hq: int, Hkv: int, d: int, dtyp
                                 max_kept_len: int) -> int:
     n = ctypes.c_size_t(0)
     _check("tg_gated_attn_bwd_workspace",
-           load_library().tg_gated_attn_bwd_workspace(B, Kt, Hq, Hkv, d, TG_BF16 if dtype == torch.bfloat16 else TG_F32,
-                                                      max_kept_len, ctypes.byref(n)))
+           load_library().tg_gated_attn_bwd_workspace(B, Kt, Hq, Hkv, d, _dtype_code_of(dtype), max_kept_len,
+                                                      ctypes.byref(n)))
     return int(n.value)
 
 
@@ -477,8 +481,7 @@ def tg_gated_attn_bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
 
 def tg_gate_bwd_workspace(Kt: int, D: int, F: int, dtype: torch.dtype) -> int:
     n = ctypes.c_size_t(0)
-    code = TG_BF16 if dtype == torch.bfloat16 else TG_F32
-    _check("tg_gate_bwd_workspace", load_library().tg_gate_bwd_workspace(Kt, D, F, code, ctypes.byref(n)))
+    _check("tg_gate_bwd_workspace", load_library().tg_gate_bwd_workspace(Kt, D, F, _dtype_code_of(dtype), ctypes.byref(n)))
     return int(n.value)
 
 

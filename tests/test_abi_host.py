@@ -283,3 +283,126 @@ def test_sample_budgets_matches_oracle_and_rejects():
     assert f(1, ten, one, uu, 0.1, 0.4, out) == TG_ERR_SHAPE
     assert f(1, None, ten, uu, 0.1, 0.4, out) == TG_ERR_NULL
     assert f(0, None, None, None, 0.1, 0.4, None) == TG_OK
+
+
+def test_attention_backward_workspace_and_argument_checks():
+    import torch
+    lib = tg.load_library()
+    # bf16 with several query heads per KV head adds the per-head fp32 dK and
+    # dV sums (2 Hq Kt d floats); one head per group and fp32 need none
+    w_g2 = tg.tg_gated_attn_bwd_workspace(1, 1000, 4, 2, 128, torch.bfloat16, 1000)
+    w_g1 = tg.tg_gated_attn_bwd_workspace(1, 1000, 4, 4, 128, torch.bfloat16, 1000)
+    w_f32 = tg.tg_gated_attn_bwd_workspace(1, 1000, 4, 2, 128, torch.float32, 1000)
+    assert w_g2 - w_g1 == 2 * 4 * 1000 * 128 * 4
+    assert w_f32 == w_g1
+    with pytest.raises(tg.TokenGateError):
+        tg.tg_gated_attn_bwd_workspace(1, 1000, 4, 3, 128, torch.bfloat16, 1000)
+    with pytest.raises(TypeError):
+        tg.tg_gated_attn_bwd_workspace(1, 1000, 4, 2, 128, torch.float16, 1000)
+    n = ctypes.c_size_t(0)
+    assert lib.tg_gated_attn_bwd_workspace(1, 1000, 4, 2, 128, 7, 1000, ctypes.byref(n)) == TG_ERR_DTYPE
+    assert lib.tg_gated_attn_bwd_workspace(1, 1000, 4, 2, 128, 1, 1000, None) == TG_ERR_NULL
+
+    need = tg.tg_gated_attn_bwd_workspace(1, 100, 16, 8, 128, torch.bfloat16, 100)
+    f = lib.tg_gated_attn_bwd
+    names = ["q", "k", "v", "qs", "ks", "vs", "bias", "gain", "tau", "cu", "B", "maxlen", "Kt", "Hq", "Hkv",
+             "d", "dtype", "out", "lse", "dout", "dq", "dk", "dv", "dbias", "dgain", "dtau", "ws", "wsb",
+             "stream"]
+    base = [FAKE, FAKE, FAKE, 2048, 1024, 1024, FAKE, FAKE, 1.15, FAKE, 1, 100, 100, 16, 8, 128, 1, FAKE,
+            FAKE, FAKE, FAKE, FAKE, FAKE, None, None, None, FAKE, need, None]
+
+    def call(**kw):
+        x = list(base)
+        for k, v in kw.items():
+            x[names.index(k)] = v
+        return f(*x)
+
+    assert call(dtype=9) == TG_ERR_DTYPE
+    assert call(Hkv=6) == TG_ERR_SHAPE
+    assert call(qs=2000) == TG_ERR_SHAPE
+    assert call(maxlen=101) == TG_ERR_SHAPE
+    assert call(tau=float("nan")) == TG_ERR_RANGE and call(tau=0.0) == TG_ERR_RANGE
+    assert call(d=96, qs=96 * 16, ks=96 * 8, vs=96 * 8) == TG_ERR_UNSUPPORTED
+    assert call(B=0) == TG_OK and call(Kt=0, maxlen=0) == TG_OK  # valid no-ops
+    assert call(dout=None) == TG_ERR_NULL
+    assert call(bias=None) == TG_ERR_NULL  # gain given without bias
+    assert call(wsb=need - 1) == TG_ERR_WORKSPACE and call(ws=None) == TG_ERR_WORKSPACE
+    assert call(ws=FAKE + 8) == TG_ERR_ALIGN
+    assert call(dk=FAKE + 2) == TG_ERR_ALIGN
+    assert call(ks=1028) == TG_ERR_ALIGN
+
+
+def test_gate_backward_argument_checks():
+    import torch
+    lib = tg.load_library()
+    need = tg.tg_gate_bwd_workspace(500, 2048, 256, torch.bfloat16)
+    assert need > 0
+    with pytest.raises(TypeError):
+        tg.tg_gate_bwd_workspace(500, 2048, 256, torch.float16)
+    f = lib.tg_gate_bwd
+    names = ["h", "ld", "Kt", "D", "W1", "b1", "w2", "F", "dbias", "kidx", "cu", "db", "de", "B", "dtype",
+             "dh", "dW1", "db1", "dw2", "db2", "ws", "wsb", "stream"]
+    base = [FAKE, 2048, 500, 2048, FAKE, FAKE, FAKE, 256, FAKE, FAKE, FAKE, FAKE, FAKE, 1, 1, FAKE, FAKE,
+            FAKE, FAKE, FAKE, FAKE, need, None]
+
+    def call(**kw):
+        x = list(base)
+        for k, v in kw.items():
+            x[names.index(k)] = v
+        return f(*x)
+
+    assert call(dtype=9) == TG_ERR_DTYPE
+    assert call(ld=1000) == TG_ERR_SHAPE
+    assert call(B=0) == TG_ERR_SHAPE  # rows but no prompts
+    assert call(F=100) == TG_ERR_UNSUPPORTED
+    assert call(D=100, ld=100) == TG_ERR_UNSUPPORTED  # bf16 needs D % 64 == 0
+    assert call(W1=None) == TG_ERR_NULL and call(db2=None) == TG_ERR_NULL
+    assert call(wsb=need - 1) == TG_ERR_WORKSPACE
+    assert call(kidx=None) == TG_ERR_NULL
+    assert call(w2=FAKE + 4) == TG_ERR_ALIGN
+    assert call(h=FAKE + 2) == TG_ERR_ALIGN and call(ld=2052) == TG_ERR_ALIGN
+
+
+def test_decode_argument_checks():
+    lib = tg.load_library()
+    sc = lib.tg_kv_scatter
+    # (k, v, ks, vs, bias, cu, B, Kt, Hkv, d, dtype, kc, vc, cks, cvs, bc, start, stream)
+    assert sc(FAKE, FAKE, 1024, 1024, None, FAKE, 1, 10, 8, 128, 9, FAKE, FAKE, 1024, 1024, FAKE, FAKE, None) \
+        == TG_ERR_DTYPE
+    assert sc(FAKE, FAKE, 1000, 1024, None, FAKE, 1, 10, 8, 128, 1, FAKE, FAKE, 1024, 1024, FAKE, FAKE, None) \
+        == TG_ERR_SHAPE
+    assert sc(FAKE, FAKE, 1024, 1024, None, FAKE, 0, 10, 8, 128, 1, FAKE, FAKE, 1024, 1024, FAKE, FAKE, None) \
+        == TG_ERR_SHAPE
+    assert sc(FAKE, FAKE, 1024, 1024, None, FAKE, 1, 0, 8, 128, 1, FAKE, FAKE, 1024, 1024, FAKE, FAKE, None) \
+        == TG_OK
+    assert sc(FAKE, FAKE, 1024, 1024, None, FAKE, 1, 10, 8, 128, 1, FAKE, FAKE, 1024, 1024, None, FAKE, None) \
+        == TG_ERR_NULL
+    ap = lib.tg_kv_append
+    # (k_new, v_new, B, Hkv, d, dtype, kc, vc, cks, cvs, bc, start, pos, stream)
+    assert ap(FAKE, FAKE, 2, 8, 128, 9, FAKE, FAKE, 1024, 1024, FAKE, FAKE, FAKE, None) == TG_ERR_DTYPE
+    assert ap(FAKE, FAKE, 2, 8, 128, 1, FAKE, FAKE, 1000, 1024, FAKE, FAKE, FAKE, None) == TG_ERR_SHAPE
+    assert ap(FAKE, FAKE, 0, 8, 128, 1, FAKE, FAKE, 1024, 1024, FAKE, FAKE, FAKE, None) == TG_OK
+    assert ap(FAKE, FAKE, 2, 8, 128, 1, FAKE, FAKE, 1024, 1024, FAKE, FAKE, None, None) == TG_ERR_NULL
+    need = tg.tg_decode_attn_workspace(2, 16, 128, 5000)
+    assert need > 0
+    de = lib.tg_decode_attn
+    names = ["q", "kc", "vc", "cks", "cvs", "bc", "gain", "tau", "start", "lens", "B", "maxlen", "Hq", "Hkv",
+             "d", "dtype", "out", "lse", "ws", "wsb", "stream"]
+    base = [FAKE, FAKE, FAKE, 1024, 1024, FAKE, FAKE, 1.15, FAKE, FAKE, 2, 5000, 16, 8, 128, 1, FAKE, None,
+            FAKE, need, None]
+
+    def call(**kw):
+        x = list(base)
+        for k, v in kw.items():
+            x[names.index(k)] = v
+        return de(*x)
+
+    assert call(dtype=9) == TG_ERR_DTYPE
+    assert call(Hkv=6) == TG_ERR_SHAPE and call(cks=1000) == TG_ERR_SHAPE
+    assert call(tau=0.0) == TG_ERR_RANGE
+    assert call(d=96, cks=768, cvs=768) == TG_ERR_UNSUPPORTED
+    assert call(Hq=32, Hkv=2, cks=256, cvs=256) == TG_ERR_UNSUPPORTED  # 16 query heads per KV head
+    assert call(B=0) == TG_OK
+    assert call(q=None) == TG_ERR_NULL and call(bc=None) == TG_ERR_NULL  # gain without bias
+    assert call(wsb=need - 1) == TG_ERR_WORKSPACE
+    assert call(q=FAKE + 2) == TG_ERR_ALIGN and call(cks=1028) == TG_ERR_ALIGN
