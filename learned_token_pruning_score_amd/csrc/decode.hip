@@ -19,8 +19,9 @@
 //                over its keys; the groups of a wave and the waves of the
 //                workgroup merge in a fixed order into one (max, sum, o)
 //                partial per query head.
-//   decode_merge the splits' partials merged in split order per (sequence,
-//                head): bit-reproducible, no atomics.
+//   decode_merge the splits' partials merged per (sequence, head): one wave
+//                per 4 output elements, lanes over the splits, fixed-order
+//                butterflies: bit-reproducible, no atomics.
 #include <math.h>
 
 #include <algorithm>
@@ -147,8 +148,11 @@ __global__ __launch_bounds__(256) void decode_split_kernel(
     for (int j = 0; j < 8; ++j) o[g][j] = 0.0f;
   }
   // keys in batches of NB per lane group: the loads of a batch are all
-  // issued before any of its keys is used
-  constexpr int NB = sizeof(T) == 2 ? 4 : 2;
+  // issued before any of its keys is used; a batch never reaches past the
+  // wave's KW keys
+  constexpr int NB0 = sizeof(T) == 2 ? 4 : 2;
+  constexpr int NB = KW / KPW < NB0 ? KW / KPW : NB0;
+  static_assert(NB >= 1 && KW % (KPW * NB) == 0, "a wave's keys split into whole batches");
   const int k_lo = split * kSplit + wave * KW;
   for (int kk = 0; kk < KW; kk += KPW * NB) {
     float kv8[NB][8], vv8[NB][8], sb[NB];
@@ -222,33 +226,47 @@ __global__ __launch_bounds__(256) void decode_split_kernel(
   }
 }
 
-// One thread per (sequence, head, element): the splits merged in split
-// order, in two passes so that every load is independent of the arithmetic
-// before it: the overall max M, then sum_s l_s 2^(m_s - M) and
-// sum_s o_s 2^(m_s - M).
+// The splits' partials of one (sequence, head) merged in two passes, every
+// load independent of the arithmetic before it: the overall max M, then
+// sum_s l_s 2^(m_s - M) and sum_s o_s 2^(m_s - M).
 template <typename T, int HD>
 __global__ __launch_bounds__(256) void decode_merge_kernel(const float* __restrict__ part_m, const float* __restrict__ part_l,
                                                            const float* __restrict__ part_o, int64_t BH, int n_split,
                                                            T* __restrict__ out, float* __restrict__ lse) {
-  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  if (i >= BH * HD) return;
-  const int64_t bh = i / HD;
-  const int e = (int)(i - bh * HD);
+  // one wave per (sequence-head bh, 4 consecutive output elements); lane l
+  // takes the splits l, l + 64, ..., so every partial is loaded in one batch,
+  // and the max and the sums over the lanes are fixed-order butterflies
+  constexpr int NC = HD / 4;
+  const int64_t wid = ((int64_t)blockIdx.x * 256 + threadIdx.x) >> 6;  // wave-uniform
+  const int lane = threadIdx.x & 63;
+  if (wid >= BH * NC) return;
+  const int64_t bh = wid / NC;
+  const int c = (int)(wid - bh * NC);
   const float* pm = part_m + bh * n_split;
   const float* pl = part_l + bh * n_split;
-  const float* po = part_o + bh * n_split * HD + e;
+  const float* po = part_o + bh * n_split * HD + 4 * c;
   float M = -INFINITY;
-#pragma unroll 32
-  for (int s = 0; s < n_split; ++s) M = fmaxf(M, pm[s]);
-  float L = 0.0f, O = 0.0f;
-#pragma unroll 32
-  for (int s = 0; s < n_split; ++s) {
+  for (int s = lane; s < n_split; s += 64) M = fmaxf(M, pm[s]);
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) M = fmaxf(M, __shfl_xor(M, off));
+  float L = 0.0f, O[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+  for (int s = lane; s < n_split; s += 64) {
     const float w = __builtin_amdgcn_exp2f(pm[s] - M);  // empty split: 2^-inf = 0
+    const float4 o = *reinterpret_cast<const float4*>(po + (int64_t)s * HD);
     L = fmaf(pl[s], w, L);
-    O = fmaf(po[(int64_t)s * HD], w, O);
+    O[0] = fmaf(o.x, w, O[0]);
+    O[1] = fmaf(o.y, w, O[1]);
+    O[2] = fmaf(o.z, w, O[2]);
+    O[3] = fmaf(o.w, w, O[3]);
   }
-  out[bh * HD + e] = from_float<T>(O / L);  // an empty sequence gives NaN
-  if (e == 0 && lse) lse[bh] = (M + __log2f(L)) * kLn2D;
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) {
+    L += __shfl_xor(L, off);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) O[j] += __shfl_xor(O[j], off);
+  }
+  if (lane < 4) out[bh * HD + 4 * c + lane] = from_float<T>(O[lane] / L);  // an empty sequence gives NaN
+  if (lane == 0 && c == 0 && lse) lse[bh] = (M + __log2f(L)) * kLn2D;
 }
 
 size_t dalign(size_t x) { return (x + 255) & ~(size_t)255; }
@@ -345,7 +363,7 @@ hipError_t launch_decode_attn(const void* q, const void* kc, const void* vc, int
   }
   if (e != hipSuccess) return e;
   const int64_t BH = (int64_t)B * Hq;
-  const dim3 mg((unsigned)((BH * d + 255) / 256));
+  const dim3 mg((unsigned)((BH * (d / 4) * 64 + 255) / 256));  // one wave per 4 output elements
   if (elem_bytes == 2) {
     if (d == 128) hipLaunchKernelGGL((decode_merge_kernel<uint16_t, 128>), mg, dim3(256), 0, s, pm, pl, po, BH, n_split, static_cast<uint16_t*>(out), lse);
     else hipLaunchKernelGGL((decode_merge_kernel<uint16_t, 64>), mg, dim3(256), 0, s, pm, pl, po, BH, n_split, static_cast<uint16_t*>(out), lse);
