@@ -129,32 +129,17 @@ __device__ __forceinline__ float wave_sum(float x) {
   return x;
 }
 
-// D[h][i] = dout_i . o_i (fp32 accumulation), one thread per (row, head):
-// the fp32 path.
-template <typename T>
-__global__ __launch_bounds__(256) void bwd_prep_kernel(const T* __restrict__ o, const T* __restrict__ dout,
-                                                       int64_t Kt, int Hq, int d, float* __restrict__ D) {
+// D[h][i] = dout_i . o_i for fp32 inputs, one thread per (row, head).
+__global__ __launch_bounds__(256) void bwd_prep_f32_kernel(const float* __restrict__ o, const float* __restrict__ dout,
+                                                           int64_t Kt, int Hq, int d, float* __restrict__ D) {
   const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
   if (idx >= Kt * Hq) return;
   const int64_t i = idx / Hq;
   const int h = (int)(idx - i * Hq);
-  const T* op = o + idx * d;
-  const T* gp = dout + idx * d;
+  const float* op = o + idx * d;
+  const float* gp = dout + idx * d;
   float acc = 0.0f;
-  if constexpr (sizeof(T) == 2) {
-    for (int e = 0; e < d; e += 8) {
-      const uint4 a = *reinterpret_cast<const uint4*>(op + e);
-      const uint4 b = *reinterpret_cast<const uint4*>(gp + e);
-      const uint32_t av[4] = {a.x, a.y, a.z, a.w}, bv[4] = {b.x, b.y, b.z, b.w};
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        acc = fmaf(__uint_as_float(av[j] << 16), __uint_as_float(bv[j] << 16), acc);
-        acc = fmaf(__uint_as_float(av[j] & 0xffff0000u), __uint_as_float(bv[j] & 0xffff0000u), acc);
-      }
-    }
-  } else {
-    for (int e = 0; e < d; ++e) acc = fmaf(op[e], gp[e], acc);
-  }
+  for (int e = 0; e < d; ++e) acc = fmaf(op[e], gp[e], acc);
   D[(int64_t)h * Kt + i] = acc;
 }
 
@@ -758,7 +743,7 @@ hipError_t launch_attn_bwd(const void* q, const void* k, const void* v, int64_t 
     hipLaunchKernelGGL(bwd_prep_bf16_kernel<8>, dim3((unsigned)((rows * 8 + 255) / 256)), dim3(256), 0, s,
                        static_cast<const uint16_t*>(out), static_cast<const uint16_t*>(dout), Kt, Hq, Dv);
   else
-    hipLaunchKernelGGL(bwd_prep_kernel<float>, dim3((unsigned)((rows + 255) / 256)), dim3(256), 0, s,
+    hipLaunchKernelGGL(bwd_prep_f32_kernel, dim3((unsigned)((rows + 255) / 256)), dim3(256), 0, s,
                        static_cast<const float*>(out), static_cast<const float*>(dout), Kt, Hq, d, Dv);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;

@@ -12,8 +12,11 @@
 // over the kept rows only (ds is zero elsewhere).  bf16 path:
 //   gbwd_ds       ds of each kept row (its bias gradient inside the
 //                 document, 0 outside), from kept_idx and the spans.
-//   da            the projection kernel recomputes a = W1 h + b1 and writes
-//                 da (bf16) and fixed-order per-32-row column sums.
+//   gbwd_a        a = W1 h recomputed split over K (fp32 partials per chunk
+//                 of columns; at the kept rows' height a 256-row tile per CU
+//                 would leave most of the chip idle).
+//   gbwd_da_finish  a = sum of the chunks + b1, da (bf16) and fixed-order
+//                 per-32-row column sums of da and ds silu(a).
 //   dh            the projection kernel on da with W1 transposed.
 //   gbwd_dw1      dW1 = da^T h: one workgroup per (64-column slice of h, chunk
 //                 of rows), both MFMA operands through transposing LDS reads
@@ -32,6 +35,8 @@ constexpr int kGR = 64;                 // rows per stage of gbwd_dw1
 
 typedef short gs4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) gs4 lds_gs4;
+typedef unsigned gu4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) const gu4 g_lds_u4;
 
 __device__ __forceinline__ uint32_t g_lds_addr(const void* p) {
   return (uint32_t)(uintptr_t)(__attribute__((address_space(3))) const char*)(reinterpret_cast<const char*>(p));
@@ -54,6 +59,160 @@ __device__ __forceinline__ uint32_t g_tr_base(const void* tile, int lane) {
   const int gi = lane & 15, g = lane >> 4;
   return g_lds_addr(reinterpret_cast<const char*>(tile) + (4 * (g >> 1) + (gi >> 2)) * (RU * 16) +
                     (16 * (g & 1) + 4 * (gi & 3)) * 2);
+}
+
+// Pre-activation a = W1 h (without b1) of the kept rows, split over K:
+// workgroup (128-row tile, K chunk) writes its fp32 partial
+// part[chunk][row][f] for all F columns.  Both operands are K-contiguous
+// (rows of h and of W1), so MFMA fragments are plain 16-byte row reads:
+// lane l supplies row l % 32, columns 8 (l / 32) .. +7 of a 16-column step,
+// for W1 (A operand, rows f) and for h (B operand, rows = tokens); register
+// i of lane l then holds a[token l % 32][f = acc_row(i, l)].  Wave w owns the
+// 32-column blocks w, w + 4 of f and all 128 rows; a 64-column stage of
+// W1 (F rows) and h (128 rows) sits in LDS with rows padded to 9 16-byte
+// units (conflict-free reads), the next stage's loads in registers.
+template <int F>
+__global__ __launch_bounds__(256, 2) void gbwd_a_kernel(const uint16_t* __restrict__ h, int64_t ld, int64_t Kt, int D,
+                                                        const uint16_t* __restrict__ W1, int kc_cols,
+                                                        float* __restrict__ part) {
+  constexpr int RU = 9;
+  constexpr int NFB = F / 32;
+  constexpr int FBW = (NFB + 3) / 4;       // f-blocks per wave
+  constexpr int W_ITEMS = F * 8 / 256;     // 16-byte chunks per thread of a W1 stage
+  constexpr int H_ITEMS = 128 * 8 / 256;
+  __shared__ uint4 sW[F * RU], sH[128 * RU];
+  const int64_t t0 = (int64_t)blockIdx.x * 128;
+  const int chunk = blockIdx.y;
+  const int k_begin = chunk * kc_cols;
+  const int k_end = min(D, k_begin + kc_cols);
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int G = lane >> 5;
+  const int rows = __builtin_amdgcn_readfirstlane((int)min((int64_t)128, Kt - t0));
+  f32x16 acc[FBW][4];
+#pragma unroll
+  for (int a = 0; a < FBW; ++a)
+#pragma unroll
+    for (int b = 0; b < 4; ++b)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) acc[a][b][i] = 0.0f;
+  uint4 vw[W_ITEMS], vh[H_ITEMS];
+  auto prefetch = [&](int k0) __attribute__((always_inline)) {
+    const __amdgpu_buffer_rsrc_t rw =
+        __builtin_amdgcn_make_buffer_rsrc((void*)(W1 + k0), (short)0, (F - 1) * D * 2 + 128, kBufFlagsG);
+    const __amdgpu_buffer_rsrc_t rh =
+        __builtin_amdgcn_make_buffer_rsrc((void*)(h + t0 * ld + k0), (short)0, rows * (int)ld * 2, kBufFlagsG);
+#pragma unroll
+    for (int j = 0; j < W_ITEMS; ++j) {
+      const int id = tid + 256 * j;
+      vw[j] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rw, ((id / 8) * D + (id % 8) * 8) * 2, 0, 0));
+    }
+#pragma unroll
+    for (int j = 0; j < H_ITEMS; ++j) {
+      const int id = tid + 256 * j;
+      vh[j] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rh, ((id / 8) * (int)ld + (id % 8) * 8) * 2, 0, 0));
+    }
+  };
+  uint32_t wl = g_lds_addr(sW) + ((lane & 31) * RU + G) * 16, hl = g_lds_addr(sH) + ((lane & 31) * RU + G) * 16;
+  asm volatile("" : "+v"(wl), "+v"(hl));
+  prefetch(k_begin);
+  for (int k0 = k_begin; k0 < k_end; k0 += 64) {
+    __syncthreads();  // the previous stage is no longer read
+#pragma unroll
+    for (int j = 0; j < W_ITEMS; ++j) {
+      const int id = tid + 256 * j;
+      sW[(id / 8) * RU + id % 8] = vw[j];
+    }
+#pragma unroll
+    for (int j = 0; j < H_ITEMS; ++j) {
+      const int id = tid + 256 * j;
+      sH[(id / 8) * RU + id % 8] = vh[j];
+    }
+    __syncthreads();
+    if (k0 + 64 < k_end) prefetch(k0 + 64);
+#pragma unroll
+    for (int st = 0; st < 4; ++st) {
+      bf16x8 hf[4];
+#pragma unroll
+      for (int b = 0; b < 4; ++b)
+        hf[b] = __builtin_bit_cast(bf16x8, *(g_lds_u4*)(uintptr_t)(hl + ((32 * b) * RU + 2 * st) * 16));
+#pragma unroll
+      for (int a = 0; a < FBW; ++a) {
+        const int fb = wave + 4 * a;
+        if (fb < NFB) {
+          const bf16x8 wf = __builtin_bit_cast(bf16x8, *(g_lds_u4*)(uintptr_t)(wl + ((32 * fb) * RU + 2 * st) * 16));
+#pragma unroll
+          for (int b = 0; b < 4; ++b) acc[a][b] = mfma32x32x16(wf, hf[b], acc[a][b]);
+        }
+      }
+    }
+  }
+  // acc[a][b]: f = 32 (wave + 4a) + acc_row(i, lane), row t0 + 32 b + lane % 32
+  float* pc = part + (int64_t)chunk * Kt * F;
+#pragma unroll
+  for (int a = 0; a < FBW; ++a) {
+    const int fb = wave + 4 * a;
+    if (fb < NFB) {
+#pragma unroll
+      for (int b = 0; b < 4; ++b) {
+        const int64_t t = t0 + 32 * b + (lane & 31);
+        if (t < Kt) {
+#pragma unroll
+          for (int g4 = 0; g4 < 4; ++g4)
+            *reinterpret_cast<float4*>(pc + t * F + 32 * fb + 8 * g4 + 4 * G) =
+                make_float4(acc[a][b][4 * g4], acc[a][b][4 * g4 + 1], acc[a][b][4 * g4 + 2], acc[a][b][4 * g4 + 3]);
+        }
+      }
+    }
+  }
+}
+
+// da from the partials: workgroup (32-row block, 64 columns), thread
+// (quarter q, column f) takes rows 8q .. 8q + 7 of the block: a = (sum of the
+// chunks in order) + b1, da = ds w2 silu'(a) (bf16), and the column sums of
+// da and ds silu(a) over its rows in order, then over the quarters in order.
+__global__ __launch_bounds__(256) void gbwd_da_finish_kernel(const float* __restrict__ part, int n_kc, int64_t Kt,
+                                                             int F, const float* __restrict__ b1,
+                                                             const float* __restrict__ w2, const float* __restrict__ ds,
+                                                             uint16_t* __restrict__ da, float* __restrict__ p1,
+                                                             float* __restrict__ p2) {
+  __shared__ float r1[4][64], r2[4][64];
+  const int tid = threadIdx.x;
+  const int q = tid >> 6, c = tid & 63;
+  const int f = blockIdx.y * 64 + c;
+  const int64_t blk = blockIdx.x;
+  float c1 = 0.0f, c2 = 0.0f;
+  if (f < F) {
+    const float bb = b1 ? b1[f] : 0.0f, ww = w2[f];
+    const int64_t r0 = blk * 32 + 8 * q;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int64_t t = r0 + j;
+      if (t < Kt) {
+        float a = part[t * F + f];
+        for (int k = 1; k < n_kc; ++k) a += part[((int64_t)k * Kt + t) * F + f];
+        a += bb;
+        const float dsr = ds[t];
+        const float sg = 1.0f / (1.0f + expf(-a));
+        const float d = dsr * ww * sg * (1.0f + a * (1.0f - sg));
+        da[t * F + f] = __builtin_bit_cast(uint16_t, (__bf16)d);
+        c1 += d;
+        c2 += dsr * a * sg;
+      }
+    }
+  }
+  r1[q][c] = c1;
+  r2[q][c] = c2;
+  __syncthreads();
+  if (q == 0 && f < F) {
+    p1[blk * F + f] = ((r1[0][c] + r1[1][c]) + r1[2][c]) + r1[3][c];
+    p2[blk * F + f] = ((r2[0][c] + r2[1][c]) + r2[2][c]) + r2[3][c];
+  }
+}
+
+__global__ __launch_bounds__(256) void gbwd_fill_kernel(float* __restrict__ p, int64_t n) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i < n) p[i] = 0.0f;
 }
 
 // ds of each kept row: its bias gradient when the row's token lies inside
@@ -181,16 +340,21 @@ __global__ __launch_bounds__(256) void gbwd_dw1_sum_kernel(const float* __restri
   dW1[i] = acc;
 }
 
-__global__ __launch_bounds__(256) void gbwd_col_sum_kernel(const float* __restrict__ p1, const float* __restrict__ p2,
-                                                           int64_t n_blk, int F, float* __restrict__ db1,
-                                                           float* __restrict__ dw2) {
-  __shared__ float r1[4][64], r2[4][64];
+// db1 and dw2 from the per-32-row-block column sums: 64 columns per
+// workgroup, 16 groups of blocks (block b in group b % 16) per column, the
+// group sums added in group order.
+__global__ __launch_bounds__(1024) void gbwd_col_sum_kernel(const float* __restrict__ p1, const float* __restrict__ p2,
+                                                            int64_t n_blk, int F, float* __restrict__ db1,
+                                                            float* __restrict__ dw2) {
+  constexpr int NG = 16;
+  __shared__ float r1[NG][64], r2[NG][64];
   const int tid = threadIdx.x;
   const int grp = tid >> 6;
   const int f = blockIdx.x * 64 + (tid & 63);
   float a1 = 0.0f, a2 = 0.0f;
   if (f < F) {
-    for (int64_t b = grp; b < n_blk; b += 4) {
+#pragma unroll 8
+    for (int64_t b = grp; b < n_blk; b += NG) {
       a1 += p1[b * F + f];
       a2 += p2[b * F + f];
     }
@@ -199,21 +363,28 @@ __global__ __launch_bounds__(256) void gbwd_col_sum_kernel(const float* __restri
   r2[grp][tid & 63] = a2;
   __syncthreads();
   if (tid < 64 && f < F) {
-    const float s1 = ((r1[0][tid] + r1[1][tid]) + r1[2][tid]) + r1[3][tid];
-    const float s2 = ((r2[0][tid] + r2[1][tid]) + r2[2][tid]) + r2[3][tid];
+    float s1 = r1[0][tid], s2 = r2[0][tid];
+#pragma unroll
+    for (int g = 1; g < NG; ++g) {
+      s1 += r1[g][tid];
+      s2 += r2[g][tid];
+    }
     if (db1) db1[f] = s1;
     dw2[f] = s2;
   }
 }
 
-__global__ __launch_bounds__(256) void gbwd_sum_ds_kernel(const float* __restrict__ ds, int64_t Kt, float* __restrict__ db2) {
-  __shared__ float red[256];
+// db2 = sum of ds: thread i sums rows i, i + 1024, ... (loads unrolled), then
+// a fixed tree over the 1024 threads.
+__global__ __launch_bounds__(1024) void gbwd_sum_ds_kernel(const float* __restrict__ ds, int64_t Kt, float* __restrict__ db2) {
+  __shared__ float red[1024];
   const int tid = threadIdx.x;
   float acc = 0.0f;
-  for (int64_t r = tid; r < Kt; r += 256) acc += ds[r];
+#pragma unroll 8
+  for (int64_t r = tid; r < Kt; r += 1024) acc += ds[r];
   red[tid] = acc;
   __syncthreads();
-  for (int w = 128; w >= 1; w >>= 1) {
+  for (int w = 512; w >= 1; w >>= 1) {
     if (tid < w) red[tid] += red[tid + w];
     __syncthreads();
   }
@@ -279,21 +450,33 @@ __global__ __launch_bounds__(256) void gbwd_dw1_f32_kernel(const float* __restri
 size_t galign(size_t x) { return (x + 255) & ~(size_t)255; }
 
 struct GbwdLayout {
-  int64_t n_blk;       // 32-row blocks of the da column sums (tile-rounded)
+  int64_t n_blk;       // 32-row blocks of the da column sums
   int chunk_rows;      // rows per dW1 chunk
   int n_chunks;
-  size_t off_ds, off_da, off_wt, off_p1, off_p2, off_part, total;
+  int kc_cols;         // columns of h per K chunk of the pre-activation
+  int n_kc;
+  size_t off_ds, off_da, off_wt, off_p1, off_p2, off_part, off_pa, total;
 };
 
 GbwdLayout gbwd_layout(int64_t Kt, int D, int F, int eb) {
   GbwdLayout L{};
-  L.n_blk = (Kt + 255) / 256 * 8;
+  L.n_blk = (Kt + 31) / 32;
+  // K chunks of the pre-activation: enough (128-row tile, chunk) workgroups
+  // for every CU, in whole 64-column stages
+  const int64_t a_tiles = (Kt + 127) / 128;
+  const int64_t n_stage = D / 64;
+  int64_t kc = a_tiles > 0 ? (256 + a_tiles - 1) / a_tiles : 1;
+  if (kc > n_stage) kc = n_stage;
+  if (kc < 1) kc = 1;
+  L.kc_cols = (int)((n_stage + kc - 1) / kc * 64);
+  L.n_kc = (int)((D + L.kc_cols - 1) / L.kc_cols);
   const int64_t row_tiles = (Kt + kGR - 1) / kGR;
   const int n_dt = D / 64;
   int64_t want = (256 + n_dt - 1) / n_dt;
   if (want < 1) want = 1;
   if (want > row_tiles) want = row_tiles > 0 ? row_tiles : 1;
   L.chunk_rows = (int)(((row_tiles + want - 1) / want) * kGR);
+  if (L.chunk_rows < kGR) L.chunk_rows = kGR;  // no rows: one empty chunk
   L.n_chunks = (int)((Kt + L.chunk_rows - 1) / L.chunk_rows);
   if (L.n_chunks < 1) L.n_chunks = 1;
   size_t o = 0;
@@ -304,6 +487,7 @@ GbwdLayout gbwd_layout(int64_t Kt, int D, int F, int eb) {
     L.off_p1 = o; o += galign((size_t)L.n_blk * F * 4);
     L.off_p2 = o; o += galign((size_t)L.n_blk * F * 4);
     L.off_part = o; o += galign((size_t)L.n_chunks * F * D * 4);
+    L.off_pa = o; o += galign((size_t)L.n_kc * Kt * F * 4);
   } else {
     L.off_p2 = o; o += galign((size_t)Kt * F * 4);  // ds * silu(a) per element
   }
@@ -322,10 +506,18 @@ hipError_t launch_gate_bwd(const void* h, int64_t ld, int64_t Kt, int D, const v
                            const int32_t* cu, const int32_t* db, const int32_t* de, int B, int elem_bytes,
                            void* dh, float* dW1, float* db1, float* dw2, float* db2, void* ws,
                            hipStream_t s) {
+  const dim3 blk(256);
+  if (Kt == 0) {  // no kept rows: every gradient is zero
+    const int64_t FD = (int64_t)F * D;
+    hipLaunchKernelGGL(gbwd_fill_kernel, dim3((unsigned)((FD + 255) / 256)), blk, 0, s, dW1, FD);
+    if (db1) hipLaunchKernelGGL(gbwd_fill_kernel, dim3((unsigned)((F + 255) / 256)), blk, 0, s, db1, (int64_t)F);
+    hipLaunchKernelGGL(gbwd_fill_kernel, dim3((unsigned)((F + 255) / 256)), blk, 0, s, dw2, (int64_t)F);
+    hipLaunchKernelGGL(gbwd_fill_kernel, dim3(1), blk, 0, s, db2, (int64_t)1);
+    return hipGetLastError();
+  }
   const GbwdLayout L = gbwd_layout(Kt, D, F, elem_bytes);
   char* w = static_cast<char*>(ws);
   float* ds = reinterpret_cast<float*>(w + L.off_ds);
-  const dim3 blk(256);
   hipLaunchKernelGGL(gbwd_ds_kernel, dim3((unsigned)((Kt + 255) / 256)), blk, 0, s, dbias, kept_idx, cu, db, de, B,
                      Kt, ds);
   hipError_t e = hipGetLastError();
@@ -337,7 +529,16 @@ hipError_t launch_gate_bwd(const void* h, int64_t ld, int64_t Kt, int D, const v
     float* p1 = reinterpret_cast<float*>(w + L.off_p1);
     float* p2 = reinterpret_cast<float*>(w + L.off_p2);
     float* part = reinterpret_cast<float*>(w + L.off_part);
-    e = launch_gate_bwd_da(h, ld, Kt, D, W1, F, b1, w2, ds, da, p1, p2, s);
+    float* pa = reinterpret_cast<float*>(w + L.off_pa);
+    const auto* hp = static_cast<const uint16_t*>(h);
+    const auto* w1p = static_cast<const uint16_t*>(W1);
+    const dim3 ga((unsigned)((Kt + 127) / 128), (unsigned)L.n_kc);
+    if (F == 256) hipLaunchKernelGGL(gbwd_a_kernel<256>, ga, blk, 0, s, hp, ld, Kt, D, w1p, L.kc_cols, pa);
+    else if (F == 128) hipLaunchKernelGGL(gbwd_a_kernel<128>, ga, blk, 0, s, hp, ld, Kt, D, w1p, L.kc_cols, pa);
+    else hipLaunchKernelGGL(gbwd_a_kernel<64>, ga, blk, 0, s, hp, ld, Kt, D, w1p, L.kc_cols, pa);
+    hipLaunchKernelGGL(gbwd_da_finish_kernel, dim3((unsigned)L.n_blk, (unsigned)((F + 63) / 64)), blk, 0, s, pa, L.n_kc,
+                       Kt, F, b1, w2, ds, static_cast<uint16_t*>(da), p1, p2);
+    e = hipGetLastError();
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL(gbwd_transpose_kernel, dim3((unsigned)(((int64_t)F * D + 255) / 256)), blk, 0, s,
                        static_cast<const uint16_t*>(W1), F, D, wt);
@@ -347,19 +548,16 @@ hipError_t launch_gate_bwd(const void* h, int64_t ld, int64_t Kt, int D, const v
     if (e != hipSuccess) return e;
     const dim3 g((unsigned)(D / 64), (unsigned)L.n_chunks);
     const auto* dap = static_cast<const uint16_t*>(da);
-    const auto* hp = static_cast<const uint16_t*>(h);
     if (F == 256) hipLaunchKernelGGL(gbwd_dw1_kernel<256>, g, blk, 0, s, dap, hp, ld, Kt, D, L.chunk_rows, part);
     else if (F == 128) hipLaunchKernelGGL(gbwd_dw1_kernel<128>, g, blk, 0, s, dap, hp, ld, Kt, D, L.chunk_rows, part);
     else hipLaunchKernelGGL(gbwd_dw1_kernel<64>, g, blk, 0, s, dap, hp, ld, Kt, D, L.chunk_rows, part);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
-    // the 32-row blocks holding a kept row are written by the da launch
-    // (blocks past them may belong to sub-tiles that had no rows)
     const int64_t FD = (int64_t)F * D;
     hipLaunchKernelGGL(gbwd_dw1_sum_kernel, dim3((unsigned)((FD + 255) / 256)), blk, 0, s, part, L.n_chunks, FD, dW1);
-    hipLaunchKernelGGL(gbwd_col_sum_kernel, dim3((unsigned)((F + 63) / 64)), blk, 0, s, p1, p2, (Kt + 31) / 32, F, db1,
-                       dw2);
-    hipLaunchKernelGGL(gbwd_sum_ds_kernel, dim3(1), blk, 0, s, ds, Kt, db2);
+    hipLaunchKernelGGL(gbwd_col_sum_kernel, dim3((unsigned)((F + 63) / 64)), dim3(1024), 0, s, p1, p2, L.n_blk, F,
+                       db1, dw2);
+    hipLaunchKernelGGL(gbwd_sum_ds_kernel, dim3(1), dim3(1024), 0, s, ds, Kt, db2);
     return hipGetLastError();
   }
   float* da = reinterpret_cast<float*>(w + L.off_da);

@@ -12,10 +12,7 @@
 //           as projected;
 //   resid   (attention output and down projection) the residual row is added;
 //   swiglu  (gate and up projections) silu(gate) * up;
-//   store   plain product (the gate backward's dh = da . W1);
-//   gate_bwd the gate MLP's backward on its own pre-activation
-//           a = W1 x + b1: da = ds * w2 * silu'(a) and, per 32-row block, the
-//           column sums of da and of ds * silu(a).
+//   store   plain product (the gate backward's dh = da . W1).
 //
 // Kernels:
 //   rope_table   cos / sin of every (kept row, frequency) pair, evaluated in
@@ -50,7 +47,7 @@ constexpr int kBM = 256;    // rows of x per tile (8 waves x 32)
 constexpr int kNFB = 8;     // 32-row weight blocks per tile
 constexpr int kBufFlags = 0x00020000;  // raw buffer: reads past num_records give 0
 
-enum ProjEpi : int { kEpiRope = 0, kEpiResid = 1, kEpiSwiglu = 2, kEpiStore = 3, kEpiGateBwd = 4 };
+enum ProjEpi : int { kEpiRope = 0, kEpiResid = 1, kEpiSwiglu = 2, kEpiStore = 3 };
 
 // Weight rows staged per source in a tile: 256 of W, or 128 of W_gate
 // followed by the same 128 of W_up.
@@ -75,13 +72,6 @@ struct ProjArgs {
   int64_t ld_res;
   uint16_t* out;         // output rows, stride ld_out
   int64_t ld_out;
-  // gate backward (a = W1 x + b1 per row): da = ds_row * w2 * silu'(a) to
-  // out, and per 32-row block the column sums of da and of ds_row * silu(a)
-  const float* b1;       // may be null
-  const float* w2;
-  const float* ds;       // per row
-  float* part_db1;       // [rows / 32 blocks][N]
-  float* part_dw2;
 };
 
 // A staged row of weights is 64 columns = eight 16-byte chunks; logical
@@ -141,45 +131,6 @@ __device__ __forceinline__ void finish_pair(const ProjArgs& g, f32x16& a, f32x16
           const float av = a[4 * i4 + c], bv = b[4 * i4 + c];
           a[4 * i4 + c] = av * cs[c] - bv * sn[c];
           b[4 * i4 + c] = bv * cs[c] + av * sn[c];
-        }
-      }
-    }
-  }
-  if (EPI == kEpiGateBwd) {
-    // da, and the two column sums over the wave's 32 rows (the lanes with
-    // the same lane / 32) in a fixed butterfly order, four columns at a
-    // time; rows past M have ds = 0
-    const float dsr = t < g.M ? g.ds[t] : 0.0f;
-    const int64_t blk = t / 32;
-#pragma unroll
-    for (int s2 = 0; s2 < 2; ++s2) {
-      f32x16& v = s2 ? b : a;
-      const int col = (s2 ? colB : colA) + hf;
-#pragma unroll
-      for (int i4 = 0; i4 < 4; ++i4) {
-        const float4 bb = g.b1 ? *reinterpret_cast<const float4*>(g.b1 + col + 8 * i4) : make_float4(0, 0, 0, 0);
-        const float4 ww = *reinterpret_cast<const float4*>(g.w2 + col + 8 * i4);
-        const float bv[4] = {bb.x, bb.y, bb.z, bb.w}, wv[4] = {ww.x, ww.y, ww.z, ww.w};
-        float c1[4], c2[4];
-#pragma unroll
-        for (int c = 0; c < 4; ++c) {
-          const float av = v[4 * i4 + c] + bv[c];
-          const float sg = 1.0f / (1.0f + expf(-av));
-          const float da = dsr * wv[c] * sg * (1.0f + av * (1.0f - sg));
-          v[4 * i4 + c] = da;
-          c1[c] = da;
-          c2[c] = dsr * av * sg;
-        }
-#pragma unroll
-        for (int off = 1; off < 32; off <<= 1)
-#pragma unroll
-          for (int c = 0; c < 4; ++c) {
-            c1[c] += __shfl_xor(c1[c], off);
-            c2[c] += __shfl_xor(c2[c], off);
-          }
-        if ((lane & 31) == 0) {
-          *reinterpret_cast<float4*>(g.part_db1 + blk * g.N + col + 8 * i4) = make_float4(c1[0], c1[1], c1[2], c1[3]);
-          *reinterpret_cast<float4*>(g.part_dw2 + blk * g.N + col + 8 * i4) = make_float4(c2[0], c2[1], c2[2], c2[3]);
         }
       }
     }
@@ -790,18 +741,6 @@ hipError_t launch_linear_residual(const void* a, int64_t ld, int64_t n, int K, c
 hipError_t launch_proj_store(const void* x, int64_t ld, int64_t n, int K, const void* W, int N, void* out,
                              int64_t ld_out, hipStream_t s) {
   return launch_proj<kEpiStore, 128>(proj_args(x, ld, n, K, W, nullptr, N, out, ld_out), s);
-}
-
-hipError_t launch_gate_bwd_da(const void* h, int64_t ld, int64_t n, int D, const void* W1, int F,
-                              const float* b1, const float* w2, const float* ds, void* da,
-                              float* part_db1, float* part_dw2, hipStream_t s) {
-  ProjArgs g = proj_args(h, ld, n, D, W1, nullptr, F, da, F);
-  g.b1 = b1;
-  g.w2 = w2;
-  g.ds = ds;
-  g.part_db1 = part_db1;
-  g.part_dw2 = part_dw2;
-  return launch_proj<kEpiGateBwd, 128>(g, s);
 }
 
 hipError_t launch_swiglu(const void* h, int64_t ld, int64_t n, int K, const void* Wg, const void* Wu,

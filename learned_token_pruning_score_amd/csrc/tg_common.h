@@ -85,9 +85,6 @@ hipError_t launch_attn_bwd(const void* q, const void* k, const void* v, int64_t 
                            float* dg, float* dtau, void* ws, hipStream_t s);
 hipError_t launch_proj_store(const void* x, int64_t ld, int64_t n, int K, const void* W, int N, void* out,
                              int64_t ld_out, hipStream_t s);
-hipError_t launch_gate_bwd_da(const void* h, int64_t ld, int64_t n, int D, const void* W1, int F,
-                              const float* b1, const float* w2, const float* ds, void* da,
-                              float* part_db1, float* part_dw2, hipStream_t s);
 size_t gate_bwd_workspace_bytes(int64_t Kt, int D, int F, int elem_bytes);
 hipError_t launch_gate_bwd(const void* h, int64_t ld, int64_t Kt, int D, const void* W1, const float* b1,
                            const float* w2, int F, const float* dbias, const int32_t* kept_idx,

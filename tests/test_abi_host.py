@@ -337,6 +337,9 @@ def test_gate_backward_argument_checks():
     lib = tg.load_library()
     need = tg.tg_gate_bwd_workspace(500, 2048, 256, torch.bfloat16)
     assert need > 0
+    # no kept rows: a finite workspace (an earlier layout divided by a zero chunk size)
+    assert tg.tg_gate_bwd_workspace(0, 2048, 256, torch.bfloat16) >= 0
+    assert tg.tg_gate_bwd_workspace(0, 2048, 256, torch.float32) >= 0
     with pytest.raises(TypeError):
         tg.tg_gate_bwd_workspace(500, 2048, 256, torch.float16)
     f = lib.tg_gate_bwd
@@ -361,6 +364,14 @@ def test_gate_backward_argument_checks():
     assert call(kidx=None) == TG_ERR_NULL
     assert call(w2=FAKE + 4) == TG_ERR_ALIGN
     assert call(h=FAKE + 2) == TG_ERR_ALIGN and call(ld=2052) == TG_ERR_ALIGN
+
+
+def test_workspace_queries_at_zero_sizes():
+    import torch
+    assert tg.tg_select_topk_workspace(0, 0) >= 0 and tg.tg_select_topk_workspace(3, 0) >= 0
+    assert tg.tg_compact_workspace(0, 0) >= 0
+    assert tg.tg_gated_attn_bwd_workspace(0, 0, 4, 2, 128, torch.bfloat16, 0) >= 0
+    assert tg.tg_decode_attn_workspace(0, 4, 128, 0) >= 0 and tg.tg_decode_attn_workspace(2, 4, 64, 0) >= 0
 
 
 def test_decode_argument_checks():

@@ -149,3 +149,23 @@ def test_gate_bwd_full_size_128k():
     case = (cu, db, de, kept, hk, W1, b1, w2, dbias, T)
     res = _run(*case)
     _check(*case, torch.bfloat16, res)
+
+
+def test_gate_bwd_no_kept_rows():
+    """No kept rows (one empty prompt): every gradient is zero, with no
+    kernel reading the empty inputs."""
+    _note("[gate bwd] no kept rows")
+    tg_ = torch.Generator().manual_seed(3)
+    D, F = 256, 64
+    W1 = (torch.randn((F, D), generator=tg_) / D ** 0.5).to(torch.bfloat16)
+    b1 = torch.randn(F, generator=tg_) * 0.1
+    w2 = torch.randn(F, generator=tg_)
+    i32 = dict(dtype=torch.int32, device=DEV)
+    dh, dW1, db1, dw2, db2 = tg.tg_gate_bwd(
+        torch.empty((0, D), dtype=torch.bfloat16, device=DEV), W1.to(DEV), b1.to(DEV), w2.to(DEV),
+        torch.empty(0, device=DEV), torch.empty(0, **i32), torch.zeros(2, **i32), torch.zeros(1, **i32),
+        torch.zeros(1, **i32))
+    torch.cuda.synchronize()
+    assert dh.shape == (0, D)
+    for t in (dW1, db1, dw2, db2):
+        assert torch.count_nonzero(t).item() == 0
