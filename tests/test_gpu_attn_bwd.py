@@ -156,13 +156,17 @@ def _check_all(cu, q, k, v, dout, bias, gain, tau, grads, out_st, dtype):
 
 
 # prompt lengths: ragged with a 1-row and an empty prompt, several 128-key
-# and 64-row tiles per prompt; GQA groups of 2 and 3; d = 128 and 64
+# and 64-row tiles per prompt; GQA groups of 1, 2, 3 and 8; d = 128 and 64
 CASES = [
     ([300, 1, 399, 0, 300], 4, 2, 128, torch.bfloat16, True),
     ([130, 257], 3, 1, 64, torch.bfloat16, True),
     ([200, 77], 4, 4, 128, torch.bfloat16, False),
     ([20, 45], 4, 2, 64, torch.float32, True),
     ([33], 2, 1, 128, torch.float32, False),
+    # GQA group 8 (one KV head): eight per-head partial sums per key in the
+    # fixed-order group sum; a 64-row tail and a 128-key tile boundary
+    ([320, 129], 8, 1, 128, torch.bfloat16, True),
+    ([200], 8, 2, 64, torch.bfloat16, True),
 ]
 
 
