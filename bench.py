@@ -329,8 +329,8 @@ def cpu_baseline(w, q_layers, cu_kept, Kt):
 def main():
     args = parse()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py runs on exactly one GPU: the gated prefill is measured on one MI355X; "
-              "multi-GPU runs are not part of this build.", file=sys.stderr)
+        print("bench.py runs on exactly one GPU: the gated prefill is measured on one MI355X "
+              "and the library has no multi-GPU path.", file=sys.stderr)
         sys.exit(2)
 
     import torch

@@ -71,7 +71,7 @@ typedef enum {
   TG_ERR_DTYPE = -3,       /* unknown dtype code */
   TG_ERR_RANGE = -4,       /* a scalar argument is out of range (e.g. tau not finite) */
   TG_ERR_ALIGN = -5,       /* a pointer or stride breaks the 16-byte rule */
-  TG_ERR_UNSUPPORTED = -6, /* valid, but a shape this build has no kernel for */
+  TG_ERR_UNSUPPORTED = -6, /* valid, but a shape the library has no kernel for */
   TG_ERR_WORKSPACE = -7,   /* workspace NULL or smaller than the *_workspace size */
   TG_ERR_HIP = -8          /* the HIP runtime reported an error at launch */
 } tg_status;

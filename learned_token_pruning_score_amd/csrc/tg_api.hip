@@ -37,7 +37,7 @@ const char* tg_status_string(int status) {
     case TG_ERR_DTYPE: return "unknown dtype code";
     case TG_ERR_RANGE: return "a scalar argument is out of range";
     case TG_ERR_ALIGN: return "a pointer or stride is misaligned";
-    case TG_ERR_UNSUPPORTED: return "shape not supported by this build";
+    case TG_ERR_UNSUPPORTED: return "shape not supported by the library's kernels";
     case TG_ERR_WORKSPACE: return "workspace missing or too small";
     case TG_ERR_HIP: return "HIP runtime error at launch";
     default: return "unknown status";
