@@ -10,8 +10,9 @@
 // start[b] + len[b] - 1, with room after them for the tokens it generates.
 //   kv_scatter   prefill's compacted rows (ragged by cu_kept) into the cache.
 //   kv_append    each step's new k, v at row start[b] + pos[b], bias 0.
-//   decode_split one workgroup of 4 waves per (sequence, KV head, 128-key
-//                split): a decode step reads every cached key once and does
+//   decode_split one workgroup of 4 waves per (sequence, KV head, split of 128
+//                keys, 256 once the grid holds about 8 workgroups per CU): a
+//                decode step reads every cached key once and does
 //                Hq/Hkv dot products per key, so it is bound by HBM, not by the
 //                matrix cores: 16 lanes (d = 128; 8 for d = 64) share one key
 //                row (16 bytes each, one coalesced read), the group's queries
@@ -33,7 +34,8 @@ namespace {
 
 constexpr float kLog2eD = 1.4426950408889634f;
 constexpr float kLn2D = 0.6931471805599453f;
-constexpr int kSplit = 128;  // keys per split
+constexpr int kSplit = 128;      // keys per split
+constexpr int kSplitLong = 256;  // keys per split once the grid holds about 8 workgroups per CU
 
 template <typename T>
 __device__ __forceinline__ void load8(const T* p, float (&v)[8]) {
@@ -111,7 +113,7 @@ __global__ __launch_bounds__(256) void kv_append_kernel(const T* __restrict__ kn
 
 // Partial of one split.  part_m / part_l [B * Hq, n_split], part_o [B * Hq,
 // n_split, HD]; grid (B * Hkv, n_split).
-template <typename T, int HD, int G>
+template <typename T, int HD, int G, int KS>
 __global__ __launch_bounds__(256) void decode_split_kernel(
     const T* __restrict__ q, const T* __restrict__ kc, const T* __restrict__ vc, int64_t ks, int64_t vs,
     const float* __restrict__ bc, const float* __restrict__ gain, float c2, const int32_t* __restrict__ start,
@@ -119,7 +121,7 @@ __global__ __launch_bounds__(256) void decode_split_kernel(
     float* __restrict__ part_l, float* __restrict__ part_o) {
   constexpr int LPK = HD / 8;       // lanes per key
   constexpr int KPW = 64 / LPK;     // keys per wave step
-  constexpr int KW = kSplit / 4;    // keys per wave per split
+  constexpr int KW = KS / 4;        // keys per wave per split
   __shared__ float sm[4][G], sl[4][G], so[4][G][HD];
   const int b = blockIdx.x / Hkv;
   const int kvh = blockIdx.x - b * Hkv;
@@ -153,7 +155,7 @@ __global__ __launch_bounds__(256) void decode_split_kernel(
   constexpr int NB0 = sizeof(T) == 2 ? 4 : 2;
   constexpr int NB = KW / KPW < NB0 ? KW / KPW : NB0;
   static_assert(NB >= 1 && KW % (KPW * NB) == 0, "a wave's keys split into whole batches");
-  const int k_lo = split * kSplit + wave * KW;
+  const int k_lo = split * KS + wave * KW;
   for (int kk = 0; kk < KW; kk += KPW * NB) {
     float kv8[NB][8], vv8[NB][8], sb[NB];
     bool ok[NB];
@@ -272,12 +274,16 @@ __global__ __launch_bounds__(256) void decode_merge_kernel(const float* __restri
 size_t dalign(size_t x) { return (x + 255) & ~(size_t)255; }
 
 template <typename T, int HD>
-hipError_t launch_split(int G, dim3 grid, hipStream_t s, const T* q, const T* kc, const T* vc, int64_t ks, int64_t vs,
-                        const float* bc, const float* gain, float c2, const int32_t* start, const int32_t* lens, int Hq,
-                        int Hkv, int n_split, float* pm, float* pl, float* po) {
-#define TG_DEC(GG)                                                                                             \
-  hipLaunchKernelGGL((decode_split_kernel<T, HD, GG>), grid, dim3(256), 0, s, q, kc, vc, ks, vs, bc, gain, c2, \
-                     start, lens, Hq, Hkv, n_split, pm, pl, po)
+hipError_t launch_split(int G, bool long_split, dim3 grid, hipStream_t s, const T* q, const T* kc, const T* vc,
+                        int64_t ks, int64_t vs, const float* bc, const float* gain, float c2, const int32_t* start,
+                        const int32_t* lens, int Hq, int Hkv, int n_split, float* pm, float* pl, float* po) {
+#define TG_DEC(GG)                                                                                                   \
+  if (long_split)                                                                                                    \
+    hipLaunchKernelGGL((decode_split_kernel<T, HD, GG, kSplitLong>), grid, dim3(256), 0, s, q, kc, vc, ks, vs, bc,  \
+                       gain, c2, start, lens, Hq, Hkv, n_split, pm, pl, po);                                         \
+  else                                                                                                               \
+    hipLaunchKernelGGL((decode_split_kernel<T, HD, GG, kSplit>), grid, dim3(256), 0, s, q, kc, vc, ks, vs, bc, gain, \
+                       c2, start, lens, Hq, Hkv, n_split, pm, pl, po)
   switch (G) {
     case 1: TG_DEC(1); break;
     case 2: TG_DEC(2); break;
@@ -338,7 +344,11 @@ hipError_t launch_decode_attn(const void* q, const void* kc, const void* vc, int
                               const float* gain, float tau, const int32_t* start, const int32_t* lens, int B,
                               int max_len, int Hq, int Hkv, int d, int elem_bytes, void* out, float* lse, void* ws,
                               hipStream_t s) {
-  const int n_split = std::max(1, (max_len + kSplit - 1) / kSplit);
+  // longer splits once there are enough workgroups (fewer partials to write
+  // and merge); the workspace is sized for the shorter ones, the larger count
+  const bool long_split = (int64_t)B * Hkv * ((max_len + kSplitLong - 1) / kSplitLong) >= 2048;
+  const int split_keys = long_split ? kSplitLong : kSplit;
+  const int n_split = std::max(1, (max_len + split_keys - 1) / split_keys);
   const int64_t P = (int64_t)B * Hq * n_split;
   char* w = static_cast<char*>(ws);
   float* pm = reinterpret_cast<float*>(w);
@@ -352,14 +362,14 @@ hipError_t launch_decode_attn(const void* q, const void* kc, const void* vc, int
     const auto* qp = static_cast<const uint16_t*>(q);
     const auto* kp = static_cast<const uint16_t*>(kc);
     const auto* vp = static_cast<const uint16_t*>(vc);
-    e = d == 128 ? launch_split<uint16_t, 128>(G, grid, s, qp, kp, vp, ks, vs, bc, gain, c2, start, lens, Hq, Hkv, n_split, pm, pl, po)
-                 : launch_split<uint16_t, 64>(G, grid, s, qp, kp, vp, ks, vs, bc, gain, c2, start, lens, Hq, Hkv, n_split, pm, pl, po);
+    e = d == 128 ? launch_split<uint16_t, 128>(G, long_split, grid, s, qp, kp, vp, ks, vs, bc, gain, c2, start, lens, Hq, Hkv, n_split, pm, pl, po)
+                 : launch_split<uint16_t, 64>(G, long_split, grid, s, qp, kp, vp, ks, vs, bc, gain, c2, start, lens, Hq, Hkv, n_split, pm, pl, po);
   } else {
     const auto* qp = static_cast<const float*>(q);
     const auto* kp = static_cast<const float*>(kc);
     const auto* vp = static_cast<const float*>(vc);
-    e = d == 128 ? launch_split<float, 128>(G, grid, s, qp, kp, vp, ks, vs, bc, gain, c2, start, lens, Hq, Hkv, n_split, pm, pl, po)
-                 : launch_split<float, 64>(G, grid, s, qp, kp, vp, ks, vs, bc, gain, c2, start, lens, Hq, Hkv, n_split, pm, pl, po);
+    e = d == 128 ? launch_split<float, 128>(G, long_split, grid, s, qp, kp, vp, ks, vs, bc, gain, c2, start, lens, Hq, Hkv, n_split, pm, pl, po)
+                 : launch_split<float, 64>(G, long_split, grid, s, qp, kp, vp, ks, vs, bc, gain, c2, start, lens, Hq, Hkv, n_split, pm, pl, po);
   }
   if (e != hipSuccess) return e;
   const int64_t BH = (int64_t)B * Hq;

@@ -145,6 +145,26 @@ def test_decode_steps_from_prefill_cache():
         _check_decode(out, lse, qn, Kh, Vh, Bh, start, lens, gain, s.tau, k0.dtype)
 
 
+def test_decode_long_splits():
+    """32 sequences of 3000-4096 keys over 4 KV heads: enough workgroups that
+    the step takes 256-key splits (one partial per 256 keys)."""
+    _note("[decode] 32 sequences, 256-key splits")
+    g = torch.Generator().manual_seed(12)
+    lens = [4096 - 37 * i for i in range(32)]
+    Hq, Hkv, d = 8, 4, 64
+    start = np.cumsum([0] + lens[:-1]).astype(np.int32)
+    rows = int(start[-1] + lens[-1])
+    kc, vc, bc = _cache(rows, Hkv, d, torch.bfloat16, g)
+    q = torch.randn((len(lens), Hq, d), generator=g).to(torch.bfloat16)
+    gain = torch.rand(Hq, generator=g) + 0.5
+    out, lse = tg.tg_decode_attn(q.to(DEV), kc.to(DEV), vc.to(DEV), bc.to(DEV), gain.to(DEV), 1.15,
+                                 torch.from_numpy(start).to(DEV), torch.tensor(lens, dtype=torch.int32, device=DEV),
+                                 max(lens), lse=torch.empty((len(lens), Hq), device=DEV))
+    torch.cuda.synchronize()
+    w = _check_decode(out, lse, q, kc, vc, bc, start, lens, gain, 1.15, torch.bfloat16)
+    _note(f"  worst error / bar {w:.3f}")
+
+
 def test_decode_full_size_128k():
     """One decode step over the 128k workload's 8448 kept keys, 16 heads."""
     _note("[decode full] 8448 keys")
