@@ -222,7 +222,10 @@ def test_compact_invariants():
     s = rng.standard_normal(T).astype(np.float32)
     s[5] = -0.0
     hidden = rng.standard_normal((T, 6)).astype(np.float32)
-    pos = np.concatenate([np.arange(50), np.arange(1), np.arange(79)]).astype(np.int32)
+    # explicit positions that cannot be recovered from the index: each prompt
+    # holds a random permutation of distinct position ids offset by 1000 b
+    pos = np.concatenate([rng.permutation(n) + 1000 * b
+                          for b, n in enumerate(np.diff(cu))]).astype(np.int32)
     keep = oracle.select_topk(s, cu, db, de, bud)
     hk, pk, bias, idx = oracle.compact(hidden, pos, s, keep, cu, db, de)
     cu_kept, _ = oracle.plan(cu, db, de, bud)
@@ -231,8 +234,12 @@ def test_compact_invariants():
     assert np.all(np.diff(idx) > 0)
     for b in range(3):
         rows = slice(cu_kept[b], cu_kept[b + 1])
-        assert np.all(np.diff(pk[rows]) > 0)  # positions preserved, increasing
         assert np.all((idx[rows] >= cu[b]) & (idx[rows] < cu[b + 1]))
+        # positions preserved: every kept position is one of the prompt's
+        # original ids, carried by the token it belonged to
+        orig = {int(pos[t]): t for t in range(cu[b], cu[b + 1])}
+        for r in range(cu_kept[b], cu_kept[b + 1]):
+            assert int(pk[r]) in orig and orig[int(pk[r])] == idx[r]
         for t in range(cu[b], cu[b + 1]):
             in_doc = cu[b] + db[b] <= t < cu[b] + de[b]
             if not in_doc:
@@ -244,6 +251,25 @@ def test_compact_invariants():
             assert bias[r].view(np.uint32) == s[t].view(np.uint32)
         else:
             assert bias[r].view(np.uint32) == np.uint32(0)  # +0.0 exactly
+
+
+def test_compact_hand_worked():
+    g = _load("compact_hand_worked.json")
+    s = np.array(g["scores"], dtype=np.float32)
+    T = s.shape[0]
+    hidden = np.array([[10 * t, 10 * t + 1] for t in range(T)], dtype=np.int16)
+    pos = np.array(g["positions"], dtype=np.int32)
+    keep = oracle.select_topk(s, g["cu_seqlens"], g["doc_begin"], g["doc_end"], g["budget"])
+    assert keep.tolist() == g["keep"]
+    cu_kept, _ = oracle.plan(g["cu_seqlens"], g["doc_begin"], g["doc_end"], g["budget"])
+    assert cu_kept.tolist() == g["cu_kept"]
+    hk, pk, bias, idx = oracle.compact(hidden, pos, s, keep, g["cu_seqlens"], g["doc_begin"],
+                                       g["doc_end"])
+    assert idx.tolist() == g["kept_idx"]
+    assert pk.dtype == np.int32 and pk.tolist() == g["pos_k"]
+    assert bias.dtype == np.float32 and bias.tolist() == g["bias"]
+    assert np.all(np.signbit(bias) == False)  # noqa: E712  (+0.0 outside the document)
+    assert hk.tolist() == g["hidden_k"]
 
 
 # ------------------------------------------------------------------ attention
@@ -833,6 +859,12 @@ def test_sample_budgets_hand_values_and_range():
     b = oracle.sample_budgets(db, de, u, 0.25, 0.75)
     # f = 0.25, 0.5, 0.7495: floor(25.0), floor(0 * 0.5), floor(7 * 0.7495) = 25, 0, 5
     assert b.tolist() == [25, 0, 5]
+    # floor, not rounding: 7 * 0.999 = 6.993 -> 6; 10 * 0.66 = 6.6 -> 6;
+    # 9 * 0.5 = 4.5 -> 4 (round-half-up or ceil would give 5)
+    b = oracle.sample_budgets([0, 0, 0], [7, 10, 9], [0.999, 0.66, 0.5], 0.0, 1.0)
+    assert b.tolist() == [6, 6, 4]
+    # the fraction is min + (max - min) u: u = 0.5 over [0.2, 0.6] is 0.4
+    assert oracle.sample_budgets([0], [1000], [0.5], 0.2, 0.6).tolist() == [400]
     rng = np.random.default_rng(51)
     lens = rng.integers(0, 5000, 200)
     uu = rng.random(200)
