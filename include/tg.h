@@ -328,8 +328,13 @@ int tg_decode_attn_workspace(int B, int Hq, int d, int max_len, size_t* bytes);
  *     out[b, h] = softmax(x) v,   lse[b, h] = ln sum_j exp(x_j)
  * q and out packed [B, Hq, d] in dtype; lse [B, Hq] fp32 or NULL; gain
  * NULL drops the bias term.  A sequence of length 0 gives NaN.  Vector-ALU
- * kernel (a step reads each cached key once: HBM-bound), fp32 arithmetic,
- * key splits of 128 merged in a fixed order.  Supported: d in {64, 128},
+ * kernel (a step reads each cached key once: HBM-bound), fp32 arithmetic.
+ * Each sequence's keys are cut into splits merged in a fixed order: splits
+ * of 128 keys, or of 256 keys when B * Hkv * ceil(max_len / 256) >= 2048
+ * (enough workgroups to fill the chip).  The split size sets the order of
+ * the sums, so a sequence's output can differ in its last bits between
+ * calls whose B or max_len put them on different sides of that rule; calls
+ * with the same arguments give identical bits.  Supported: d in {64, 128},
  * Hq / Hkv <= 8, max_len <= 65535 * 128; q, caches and workspace 16-byte
  * aligned.
  */

@@ -5,10 +5,12 @@ The TokenGate article ("How does TokenGate learned token pruning work?")
 splits prefill into a standard forward below the gate layer, the gate module
 (score every token, keep the top-K document tokens and the whole question),
 and a pruned forward over the kept tokens whose attention carries the score
-bias ("What is token-gated attention?").  This class runs the gate module,
-the rotary table of the kept rows' original positions, a pruned layer's
-fused q/k/v projection with the rotary embedding, and its token-gated
-attention; the output projection and the MLP are not part of it.
+bias ("What is token-gated attention?").  This class runs the gate module
+(score, top-K, compaction), the rotary table of the kept rows' original
+positions, the token-gated attention, and a whole pruned layer on the kept
+rows (``pruned_layer``: RMSNorm, the fused q/k/v projection with the rotary
+embedding, the gated attention, the output projection added to the residual,
+RMSNorm and the SwiGLU MLP added to the residual).
 The kept count is known on the host from the metadata (``tg_plan``), so no
 step waits on the device.
 """
