@@ -12,9 +12,11 @@
 //  * Scores are formed transposed, S^T = K Q^T, with the 32x32x16 MFMA: lane
 //    l then holds 32 keys of query row (l & 31) per 64-key tile, so the
 //    softmax max and sum are lane-local plus one exchange with lane l ^ 32.
-//  * The bias and temperature fold into the score: the bias enters the MFMA
-//    as one more k-step and the logit is scale * acc, so p = exp2(scale *
-//    acc - scale * m) is one FMA and one exp2 per score.
+//  * The bias and temperature fold into the score: the score accumulators
+//    start at the key's bias c_j = g_h log2e s_j / scale (the MFMA's C
+//    operand, read from LDS), so the accumulator holds q.k + c_j, the logit
+//    is scale * acc, and p = exp2(scale * acc - scale * m) is one FMA and
+//    one exp2 per score.
 //  * P^T stays in registers: the accumulator layout of S^T is exactly the B
 //    operand layout of O^T += V^T P^T once keys are relabelled (within each
 //    16-key MFMA step, lane half G holds keys 4G..4G+3 and 8+4G..8+4G+3); V
@@ -71,7 +73,7 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_bf16_kernel(
   // Three LDS stages (see the schedule below).
   __shared__ uint4 sK[3][kBK * KROW];
   __shared__ uint4 sV[3][kBK * VROW];
-  __shared__ uint32_t sB[3][kBK];  // per key: bias / scale as a bf16 (hi, lo) pair
+  __shared__ __attribute__((aligned(16))) float sB[3][kBK];  // per key: g_h log2e s_j / scale
 
   const int x = blockIdx.x;
   const int h = head_swizzle ? (x % 8) * (Hq / 8) + x / 8 : x;
@@ -92,14 +94,13 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_bf16_kernel(
   const int grp = wave >> 2;  // 0: first half of the block, 1: second
   const int qw = q0 + 64 * (wave & 3) + 32 * grp;
   const int my_q = qw + (lane & 31);
-  // The key bias enters the score MFMA as one more k-step: K gains the
-  // columns (c_hi, c_lo) with c_hi + c_lo = g_h log2e s_j / scale (two bf16
-  // parts, exact to about 2^-16 of c) and Q gains the columns (1, 1), so the
-  // accumulator holds q.k + c and the logit is scale * acc.  The softmax then
-  // needs one FMA per score.  Requires scale > 0 (checked on the host).
+  // The key bias is the initial value of the score accumulators: the stage
+  // holds c_j = g_h log2e s_j / scale per key in fp32 (0 without a bias), so
+  // the accumulator holds q.k + c_j and the logit is scale * acc.  The
+  // softmax then needs one FMA per score.  Requires scale > 0 (checked on
+  // the host).
   const bool has_bias = (bias != nullptr) && (gain != nullptr);
   const float cmul = has_bias ? gain[h] * kLog2e / qk_scale : 0.0f;
-  const bf16x8 q_one = as_bf16x8(make_uint4(G == 0 ? 0x3F803F80u : 0u, 0u, 0u, 0u));
   const float rs_thr = kRescale / qk_scale;  // rescale threshold in accumulator units
 
   bf16x8 qf[NKS];
@@ -172,23 +173,16 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_bf16_kernel(
       if (grp == 0) sK[buf][(id / KCH) * KROW + (id % KCH)] = hreg[j];
       else sV[buf][(id / KCH) * VROW + (id % KCH)] = hreg[j];
     }
-    if (grp == 0 && gtid < kBK) {
-      const float c = breg * cmul;
-      const __bf16 c_hi = (__bf16)c;
-      const __bf16 c_lo = (__bf16)(c - (float)c_hi);
-      sB[buf][gtid] = (uint32_t)__builtin_bit_cast(uint16_t, c_hi) |
-                      ((uint32_t)__builtin_bit_cast(uint16_t, c_lo) << 16);
-    }
+    if (grp == 0 && gtid < kBK) sB[buf][gtid] = has_bias ? breg * cmul : 0.0f;
   };
 
-  // Scores S^T = K Q^T (+ bias column) of one tile into s, two interleaved
-  // MFMA chains; the K fragments are read KAHEAD k-steps ahead.
+  // Scores S^T = K Q^T + bias of one tile into s, two interleaved MFMA
+  // chains; the K fragments are read KAHEAD k-steps ahead.
   f32x16 s[2];
   auto qk = [&](int buf) __attribute__((always_inline)) {
     // The lane's address in the stage is made opaque once, so each
     // fragment read is that address plus an immediate offset.  kfrag: the
-    // fragments of k-step st for both key halves; st == NKS: the bias
-    // columns.
+    // fragments of k-step st for both key halves.
     typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
     typedef __attribute__((address_space(3))) const u32x4 lds_u4;
     uint32_t ka = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) const char*)
@@ -197,24 +191,31 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_bf16_kernel(
     auto kfrag = [&](int st, uint4 (&f)[2]) __attribute__((always_inline)) {
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
-        f[kb] = st < NKS ? __builtin_bit_cast(uint4, *(lds_u4*)(uintptr_t)(ka + ((kb * 32) * KROW + 2 * st) * 16))
-                         : make_uint4((has_bias && G == 0) ? sB[buf][kb * 32 + (lane & 31)] : 0u, 0u, 0u, 0u);
+        f[kb] = __builtin_bit_cast(uint4, *(lds_u4*)(uintptr_t)(ka + ((kb * 32) * KROW + 2 * st) * 16));
     };
+    // accumulators start at the key bias: register i of key half kb holds
+    // key kb * 32 + 8 (i / 4) + 4 G + i % 4 (four consecutive keys per
+    // 16-byte read, the same for a whole lane half)
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-      for (int i = 0; i < 16; ++i) s[kb][i] = 0.0f;
+      for (int a = 0; a < 4; ++a) {
+        const float4 c = *reinterpret_cast<const float4*>(&sB[buf][kb * 32 + 8 * a + 4 * G]);
+        s[kb][4 * a + 0] = c.x;
+        s[kb][4 * a + 1] = c.y;
+        s[kb][4 * a + 2] = c.z;
+        s[kb][4 * a + 3] = c.w;
+      }
     // each fragment has its own registers: no copies between steps
-    uint4 f[NKS + 1][2];
+    uint4 f[NKS][2];
 #pragma unroll
     for (int j = 0; j < KAHEAD; ++j) kfrag(j, f[j]);
 #pragma unroll
-    for (int st = 0; st <= NKS; ++st) {
-      if (st + KAHEAD <= NKS) kfrag(st + KAHEAD, f[st + KAHEAD]);
+    for (int st = 0; st < NKS; ++st) {
+      if (st + KAHEAD < NKS) kfrag(st + KAHEAD, f[st + KAHEAD]);
       __builtin_amdgcn_sched_barrier(0);
-      const bf16x8 bq = st < NKS ? qf[st < NKS ? st : 0] : q_one;
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb) s[kb] = mfma32x32x16(as_bf16x8(f[st][kb]), bq, s[kb]);
+      for (int kb = 0; kb < 2; ++kb) s[kb] = mfma32x32x16(as_bf16x8(f[st][kb]), qf[st], s[kb]);
       __builtin_amdgcn_sched_barrier(0);
     }
   };
@@ -464,7 +465,7 @@ __global__ __launch_bounds__(512, 1) void attn_bf16_ks_kernel(
   // the end-of-kernel merge reuses the same memory
   static_assert(4 * NDB * 16 * 64 + 2 * 4 * 64 <= 4 * B_OFF, "merge area");
   __shared__ uint4 smem[LDS_U4];
-  uint32_t* const sB = reinterpret_cast<uint32_t*>(smem + B_OFF);  // [2][kBK]
+  float* const sB = reinterpret_cast<float*>(smem + B_OFF);  // [2][kBK]: g_h log2e s_j / scale
 
   const int x = blockIdx.x;
   const int h = head_swizzle ? (x % 8) * (Hq / 8) + x / 8 : x;
@@ -484,7 +485,6 @@ __global__ __launch_bounds__(512, 1) void attn_bf16_ks_kernel(
   const int my_q = qw + (lane & 31);
   const bool has_bias = (bias != nullptr) && (gain != nullptr);
   const float cmul = has_bias ? gain[h] * kLog2e / qk_scale : 0.0f;
-  const bf16x8 q_one = as_bf16x8(make_uint4(G == 0 ? 0x3F803F80u : 0u, 0u, 0u, 0u));
   const float rs_thr = kRescale / qk_scale;
 
   bf16x8 qf[NKS];
@@ -561,13 +561,7 @@ __global__ __launch_bounds__(512, 1) void attn_bf16_ks_kernel(
       const int id = gtid + j * (NT / 2);
       sk[(id / KCH) * KROW + (id % KCH)] = hreg[j];
     }
-    if (gtid < kBK) {
-      const float c = breg * cmul;
-      const __bf16 c_hi = (__bf16)c;
-      const __bf16 c_lo = (__bf16)(c - (float)c_hi);
-      sB[kbuf(t) * kBK + gtid] = (uint32_t)__builtin_bit_cast(uint16_t, c_hi) |
-                                  ((uint32_t)__builtin_bit_cast(uint16_t, c_lo) << 16);
-    }
+    if (gtid < kBK) sB[kbuf(t) * kBK + gtid] = has_bias ? breg * cmul : 0.0f;
   };
   auto store_v = [&](int t) __attribute__((always_inline)) {
     uint4* sv = smem + 2 * K_STAGE + vbuf(t) * V_STAGE;
@@ -589,23 +583,28 @@ __global__ __launch_bounds__(512, 1) void attn_bf16_ks_kernel(
     auto kfrag = [&](int st, uint4 (&f)[2]) __attribute__((always_inline)) {
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
-        f[kb] = st < NKS ? __builtin_bit_cast(uint4, *(lds_u4*)(uintptr_t)(ka + ((kb * 32) * KROW + 2 * st) * 16))
-                         : make_uint4((has_bias && G == 0) ? sB[kb_ * kBK + kb * 32 + (lane & 31)] : 0u, 0u, 0u, 0u);
+        f[kb] = __builtin_bit_cast(uint4, *(lds_u4*)(uintptr_t)(ka + ((kb * 32) * KROW + 2 * st) * 16));
     };
+    // accumulators start at the key bias (see the 256-row kernel)
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-      for (int i = 0; i < 16; ++i) s[kb][i] = 0.0f;
-    uint4 f[NKS + 1][2];
+      for (int a = 0; a < 4; ++a) {
+        const float4 c = *reinterpret_cast<const float4*>(&sB[kb_ * kBK + kb * 32 + 8 * a + 4 * G]);
+        s[kb][4 * a + 0] = c.x;
+        s[kb][4 * a + 1] = c.y;
+        s[kb][4 * a + 2] = c.z;
+        s[kb][4 * a + 3] = c.w;
+      }
+    uint4 f[NKS][2];
 #pragma unroll
     for (int j = 0; j < KAHEAD; ++j) kfrag(j, f[j]);
 #pragma unroll
-    for (int st = 0; st <= NKS; ++st) {
-      if (st + KAHEAD <= NKS) kfrag(st + KAHEAD, f[st + KAHEAD]);
+    for (int st = 0; st < NKS; ++st) {
+      if (st + KAHEAD < NKS) kfrag(st + KAHEAD, f[st + KAHEAD]);
       __builtin_amdgcn_sched_barrier(0);
-      const bf16x8 bq = st < NKS ? qf[st < NKS ? st : 0] : q_one;
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb) s[kb] = mfma32x32x16(as_bf16x8(f[st][kb]), bq, s[kb]);
+      for (int kb = 0; kb < 2; ++kb) s[kb] = mfma32x32x16(as_bf16x8(f[st][kb]), qf[st], s[kb]);
       __builtin_amdgcn_sched_barrier(0);
     }
   };
