@@ -156,6 +156,26 @@ int tg_select_topk(const float* scores, const int32_t* cu_seqlens,
                    const int32_t* budget, int B, int64_t T, uint8_t* keep,
                    void* workspace, size_t workspace_bytes, void* stream);
 
+/*
+ * tg_select_topk without a workspace argument, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc).  Same arguments, results and checks as
+ * tg_select_topk; the workspace is a static device array inside the library
+ * (4 MiB, one copy per GPU, held until the process ends).  The call itself
+ * allocates nothing: on its first use on a device it only looks up that
+ * array's address.
+ * Limit: the tg_select_topk_workspace size of (B, T) must fit in 4 MiB when
+ * T > 32768 (about B <= 190 prompts at any T; T <= 32768 needs no scratch),
+ * else TG_ERR_WORKSPACE before any device work.
+ * Every call on a GPU shares that GPU's array: calls that can overlap on one
+ * GPU (other streams, other host threads) race and must be serialized by the
+ * caller.  Nothing in the array needs clearing between calls.
+ */
+int tg_select_topk_noalloc(const float* scores, const int32_t* cu_seqlens,
+                           const int32_t* doc_begin, const int32_t* doc_end,
+                           const int32_t* budget, int B, int64_t T, uint8_t* keep,
+                           void* stream);
+
 /* Workspace bytes that tg_compact needs for B prompts over T tokens. */
 int tg_compact_workspace(int B, int64_t T, size_t* bytes);
 

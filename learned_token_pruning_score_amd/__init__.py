@@ -38,6 +38,7 @@ from ._lib import (  # noqa: F401
     tg_rope_table,
     tg_sample_budgets,
     tg_select_topk,
+    tg_select_topk_noalloc,
     tg_select_topk_workspace,
     tg_swiglu,
 )

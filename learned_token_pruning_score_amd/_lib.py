@@ -41,6 +41,8 @@ SIGNATURES = {
     "tg_select_topk_workspace": (_c_int, [_c_int, _c_i64, _c_size_p]),
     "tg_select_topk": (_c_int, [_c_vp, _c_vp, _c_vp, _c_vp, _c_vp, _c_int, _c_i64, _c_vp,
                                 _c_vp, ctypes.c_size_t, _c_vp]),
+    "tg_select_topk_noalloc": (_c_int, [_c_vp, _c_vp, _c_vp, _c_vp, _c_vp, _c_int, _c_i64, _c_vp,
+                                        _c_vp]),
     "tg_compact_workspace": (_c_int, [_c_int, _c_i64, _c_size_p]),
     "tg_compact": (_c_int, [_c_vp, _c_i64, _c_int, _c_int, _c_vp, _c_vp, _c_vp, _c_vp, _c_vp,
                             _c_vp, _c_int, _c_i64, _c_i64, _c_vp, _c_vp, _c_vp, _c_vp, _c_vp,
@@ -229,6 +231,22 @@ def tg_select_topk(scores: torch.Tensor, cu_seqlens: torch.Tensor, doc_begin: to
         _dev(budget, "budget", torch.int32), B, T, _dev(keep, "keep", torch.uint8),
         _dev(workspace, "workspace"), workspace.numel() * workspace.element_size(),
         _stream(stream)))
+    return keep
+
+
+def tg_select_topk_noalloc(scores: torch.Tensor, cu_seqlens: torch.Tensor, doc_begin: torch.Tensor,
+                           doc_end: torch.Tensor, budget: torch.Tensor, keep: torch.Tensor,
+                           stream=None) -> torch.Tensor:
+    """tg_select_topk on the library's static scratch: no workspace argument and
+    no allocation (``keep`` must be given)."""
+    _require_gpu()
+    lib = load_library()
+    T = scores.shape[0]
+    B = budget.shape[0]
+    _check("tg_select_topk_noalloc", lib.tg_select_topk_noalloc(
+        _dev(scores, "scores", torch.float32), _dev(cu_seqlens, "cu_seqlens", torch.int32),
+        _dev(doc_begin, "doc_begin", torch.int32), _dev(doc_end, "doc_end", torch.int32),
+        _dev(budget, "budget", torch.int32), B, T, _dev(keep, "keep", torch.uint8), _stream(stream)))
     return keep
 
 

@@ -34,7 +34,18 @@
 // on execution order.
 #include <limits.h>
 
+#include <atomic>
+
 #include "tg_common.h"
+
+// Scratch memory of the allocation-free entry point (tg_select_topk_noalloc):
+// a file-scope device array, one copy per GPU, held until the process ends,
+// that takes the place of the caller's workspace (per-prompt states and chunk
+// histograms).  The host never uses the array's name as a device address:
+// its address on each device comes from hipGetSymbolAddress
+// (tg::select_static_scratch).
+static constexpr size_t kStaticScratchBytes = (size_t)4 << 20;
+static __device__ __align__(256) unsigned char scratch[kStaticScratchBytes];
 
 namespace tg {
 namespace {
@@ -477,6 +488,32 @@ int chunk_size(int64_t T) {
 size_t n_slots(int B, int64_t T) { return (size_t)((T + chunk_size(T) - 1) / chunk_size(T)) + (size_t)B; }
 
 }  // namespace
+
+size_t select_static_scratch_capacity() { return kStaticScratchBytes; }
+
+size_t select_scratch_bytes_needed(int B, int64_t T) {
+  // the one-workgroup path uses no workspace
+  return (B == 0 || T == 0 || T <= kSingleMaxT) ? 0 : select_workspace_bytes(B, T);
+}
+
+hipError_t select_static_scratch(void** ptr) {
+  // resolved once per device, with that device current; concurrent first
+  // calls resolve and store the same address
+  static std::atomic<void*> addr[64];
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= 64) return hipErrorInvalidDevice;
+  void* p = addr[dev].load(std::memory_order_acquire);
+  if (p == nullptr) {
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    if (p == nullptr) return hipErrorInvalidSymbol;
+    addr[dev].store(p, std::memory_order_release);
+  }
+  *ptr = p;
+  return hipSuccess;
+}
 
 size_t select_workspace_bytes(int B, int64_t T) {
   const size_t st = ((size_t)2 * B * sizeof(SelState) + 255) & ~(size_t)255;

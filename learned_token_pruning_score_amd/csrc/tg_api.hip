@@ -143,6 +143,28 @@ int tg_select_topk(const float* scores, const int32_t* cu_seqlens, const int32_t
                                     workspace, as_stream(stream)));
 }
 
+int tg_select_topk_noalloc(const float* scores, const int32_t* cu_seqlens,
+                           const int32_t* doc_begin, const int32_t* doc_end,
+                           const int32_t* budget, int B, int64_t T, uint8_t* keep,
+                           void* stream) {
+  if (B < 0 || T < 0 || T > INT32_MAX) return TG_ERR_SHAPE;
+  if (B == 0 && T != 0) return TG_ERR_SHAPE;
+  if (T == 0 && B == 0) return TG_OK;
+  if (!cu_seqlens || !doc_begin || !doc_end || !budget) return TG_ERR_NULL;
+  if (T > 0 && (!scores || !keep)) return TG_ERR_NULL;
+  if (B > kMaxGridYZ) return TG_ERR_UNSUPPORTED;
+  const size_t need = tg::select_scratch_bytes_needed(B, T);
+  if (need > tg::select_static_scratch_capacity()) return TG_ERR_WORKSPACE;
+  if (T == 0) return TG_OK;
+  void* ws = nullptr;
+  if (need > 0) {
+    const hipError_t e = tg::select_static_scratch(&ws);
+    if (e != hipSuccess) return TG_ERR_HIP;
+  }
+  return from_hip(tg::launch_select(scores, cu_seqlens, doc_begin, doc_end, budget, B, T, keep, ws,
+                                    as_stream(stream)));
+}
+
 int tg_compact_workspace(int B, int64_t T, size_t* bytes) {
   if (!bytes) return TG_ERR_NULL;
   if (B < 0 || T < 0) return TG_ERR_SHAPE;

@@ -52,6 +52,12 @@ hipError_t launch_gate_f32(const float* hidden, int64_t ld, int64_t T, int D, co
                            hipStream_t s);
 
 size_t select_workspace_bytes(int B, int64_t T);
+// Allocation-free selection: bytes of scratch a call needs (0 when the
+// one-workgroup path runs), the capacity of the static scratch array, and
+// its address on the current device.
+size_t select_scratch_bytes_needed(int B, int64_t T);
+size_t select_static_scratch_capacity();
+hipError_t select_static_scratch(void** ptr);
 hipError_t launch_select(const float* scores, const int32_t* cu, const int32_t* db,
                          const int32_t* de, const int32_t* budget, int B, int64_t T,
                          uint8_t* keep, void* ws, hipStream_t s);

@@ -34,7 +34,7 @@ def _declared():
 def test_every_declared_symbol_is_exported_and_typed():
     lib = tg.load_library()
     names = _declared()
-    assert "tg_sample_budgets" in names and "tg_swiglu" in names and len(names) == 23
+    assert "tg_sample_budgets" in names and "tg_swiglu" in names and len(names) == 24
     for n in names:
         assert hasattr(lib, n), n
     assert set(names) == set(tg.SIGNATURES)
@@ -417,3 +417,23 @@ def test_decode_argument_checks():
     assert call(q=None) == TG_ERR_NULL and call(bc=None) == TG_ERR_NULL  # gain without bias
     assert call(wsb=need - 1) == TG_ERR_WORKSPACE
     assert call(q=FAKE + 2) == TG_ERR_ALIGN and call(cks=1028) == TG_ERR_ALIGN
+
+
+def test_select_noalloc_argument_checks():
+    lib = tg.load_library()
+    f = FAKE
+    # same checks as tg_select_topk, all before any device work
+    assert lib.tg_select_topk_noalloc(f, None, f, f, f, 1, 100, f, None) == TG_ERR_NULL
+    assert lib.tg_select_topk_noalloc(None, f, f, f, f, 1, 100, f, None) == TG_ERR_NULL
+    assert lib.tg_select_topk_noalloc(f, f, f, f, f, 1, 100, None, None) == TG_ERR_NULL
+    assert lib.tg_select_topk_noalloc(f, f, f, f, f, -1, 100, f, None) == TG_ERR_SHAPE
+    assert lib.tg_select_topk_noalloc(f, f, f, f, f, 0, 100, f, None) == TG_ERR_SHAPE
+    assert lib.tg_select_topk_noalloc(f, f, f, f, f, 1, 1 << 31, f, None) == TG_ERR_SHAPE
+    assert lib.tg_select_topk_noalloc(f, f, f, f, f, 70000, 100000, f, None) == TG_ERR_UNSUPPORTED
+    assert lib.tg_select_topk_noalloc(None, None, None, None, None, 0, 0, None, None) == TG_OK
+    # the static scratch holds 4 MiB: 300 prompts over 40000 tokens need the
+    # chunked path's 4.96 MB workspace and are rejected before any launch
+    assert tg.tg_select_topk_workspace(300, 40000) > (4 << 20)
+    assert lib.tg_select_topk_noalloc(f, f, f, f, f, 300, 40000, f, None) == TG_ERR_WORKSPACE
+    # the largest single-prompt workspace (64 chunks) fits
+    assert tg.tg_select_topk_workspace(1, 1 << 30) <= (4 << 20)
