@@ -125,7 +125,7 @@ int tg_sample_budgets(int B, const int32_t* doc_begin_h, const int32_t* doc_end_
  * hidden  [T, D] row-major, row stride ld_hidden elements (>= D), dtype.
  * W1      [F, D] row-major, dtype.   b1 [F] fp32 or NULL (zero).
  * w2      [F] fp32.  b2 scalar.      scores [T] fp32 out.
- * Supported: TG_BF16 with D % 64 == 0, F in {64, 128, 256} and a row stride
+ * Supported: TG_BF16 with D % 8 == 0, F in {64, 128, 256} and a row stride
  * below 2^22 elements, or
  * TG_F32 with any D >= 1 and 1 <= F <= 1024.  bf16 needs hidden, W1 and the
  * row stride aligned to 16 bytes.  T == 0 is a no-op.

@@ -74,21 +74,34 @@ __global__ __launch_bounds__(512, 1) void gate_bf16_kernel(
   }
 
   // Stages per tile, rounded up to a multiple of four (the unroll below);
-  // stages past D load zeros and add nothing.
-  const int nk = (D / kGateBK + 3) & ~3;
+  // stages past D load zeros and add nothing.  With D % 64 != 0 the last
+  // stage that holds columns of D (stage D / 64) is partial: there the
+  // 16-byte chunks of both operands at or past column D (D % 8 == 0, so a
+  // chunk is wholly in or out) are loaded from the first offset past the
+  // buffer's range, which reads zeros, instead of from the next row.
+  const int nk = ((D + kGateBK - 1) / kGateBK + 3) & ~3;
+  const int tail_stage = (D % kGateBK) ? D / kGateBK : -1;
+  const int tail_cols = D % kGateBK;
   const int my_tiles = ((int)blockIdx.x < n_tiles) ? (n_tiles - 1 - (int)blockIdx.x) / (int)gridDim.x + 1 : 0;
   const int n_steps = my_tiles * nk;
 
-  // hidden: lane loads 64 contiguous bytes of token tgrp * 32 + lane % 32
+  // hidden: lane loads 64 contiguous bytes of token tgrp * 32 + lane % 32:
+  // chunk j holds columns 32 (lane / 32) + 8 j .. +7 of the stage
   const int h_voff = ((tgrp * 32 + (lane & 31)) * (int)ld + (lane >> 5) * 32) * 2;
+  bool h_dead[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) h_dead[j] = 32 * (lane >> 5) + 8 * j >= tail_cols;
   // W1 copies: copy j of this wave fills rows 8 (wave * W_DMA + j) .. +7;
   // lane l writes position l % 8 of row l / 8, which holds that row's
   // logical chunk gate_swz(row, l % 8).
   int w_src[W_DMA];
+  bool w_dead[W_DMA];  // the chunk lies past D in the partial stage
 #pragma unroll
   for (int j = 0; j < W_DMA; ++j) {
     const int r = (wave * W_DMA + j) * 8 + (lane >> 3);
-    w_src[j] = (r * D + gate_swz(r, lane & 7) * 8) * 2;
+    const int c = gate_swz(r, lane & 7);  // logical chunk: columns 8 c .. 8 c + 7
+    w_src[j] = (r * D + c * 8) * 2;
+    w_dead[j] = 8 * c >= tail_cols;
   }
   // W1 fragment of F block fb, k-step ks: row 32 fb + lane % 32, logical
   // chunk 4 (lane / 32) + ks; the swizzle term depends on the lane only.
@@ -111,12 +124,14 @@ __global__ __launch_bounds__(512, 1) void gate_bf16_kernel(
     const uint16_t* hb_ptr = rows > 0 ? hidden + tt0 * ld + kk : hidden;
     const __amdgpu_buffer_rsrc_t rh = __builtin_amdgcn_make_buffer_rsrc((void*)hb_ptr, (short)0, hb, kBufFlags);
     const __amdgpu_buffer_rsrc_t rw = __builtin_amdgcn_make_buffer_rsrc((void*)(W1 + kk), (short)0, wb, kBufFlags);
+    const bool tail = ld_k == tail_stage;  // uniform
 #pragma unroll
     for (int j = 0; j < W_DMA; ++j)
-      lds_load16(rw, sw + (wave * W_DMA + j) * 1024, w_src[j]);
+      lds_load16(rw, sw + (wave * W_DMA + j) * 1024, (tail && w_dead[j]) ? wb : w_src[j]);
 #pragma unroll
     for (int j = 0; j < 4; ++j)
-      h[j] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rh, h_voff + 16 * j, 0, 0));
+      h[j] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(
+          rh, (tail && h_dead[j]) ? hb : h_voff + 16 * j, 0, 0));
     if (++ld_k == nk) {
       ld_k = 0;
       ld_tile += gridDim.x;

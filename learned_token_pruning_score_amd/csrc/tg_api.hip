@@ -107,7 +107,7 @@ int tg_gate_score(const void* hidden, int64_t ld_hidden, int64_t T, int D, const
   if (T == 0) return TG_OK;
   if (!hidden || !W1 || !w2 || !scores) return TG_ERR_NULL;
   if (dtype == TG_BF16) {
-    if (D % 64 != 0 || !(F == 64 || F == 128 || F == 256)) return TG_ERR_UNSUPPORTED;
+    if (D % 8 != 0 || !(F == 64 || F == 128 || F == 256)) return TG_ERR_UNSUPPORTED;
     // a 256-row tile of hidden is addressed with 32-bit byte offsets
     if (ld_hidden >= (1 << 22) || (int64_t)F * D > (1 << 29)) return TG_ERR_UNSUPPORTED;
     if (!aligned16(hidden) || !aligned16(W1) || (ld_hidden * 2) % 16 != 0) return TG_ERR_ALIGN;

@@ -103,7 +103,9 @@ def test_gate_score_argument_checks():
     assert f(None, 2048, 10, 2048, FAKE, None, FAKE, 0.0, 256, 1, FAKE, None) == TG_ERR_NULL
     assert f(FAKE, 2048, 10, 2048, FAKE, None, None, 0.0, 256, 1, FAKE, None) == TG_ERR_NULL
     assert f(FAKE, 2048, 10, 2048, FAKE, None, FAKE, 0.0, 100, 1, FAKE, None) == TG_ERR_UNSUPPORTED
-    assert f(FAKE, 2048, 10, 1000, FAKE, None, FAKE, 0.0, 256, 1, FAKE, None) == TG_ERR_UNSUPPORTED
+    # bf16 needs D % 8 == 0 (whole 16-byte chunks); any D for fp32
+    assert f(FAKE, 2048, 10, 1004, FAKE, None, FAKE, 0.0, 256, 1, FAKE, None) == TG_ERR_UNSUPPORTED
+    assert f(FAKE, 2048, 10, 1, FAKE, None, FAKE, 0.0, 256, 1, FAKE, None) == TG_ERR_UNSUPPORTED
     assert f(FAKE + 2, 2048, 10, 2048, FAKE, None, FAKE, 0.0, 256, 1, FAKE, None) == TG_ERR_ALIGN
     assert f(FAKE, 2049 + 3, 10, 2048, FAKE, None, FAKE, 0.0, 256, 1, FAKE, None) == TG_ERR_ALIGN
     assert f(FAKE, 256, 10, 256, FAKE, None, FAKE, 0.0, 2000, 0, FAKE, None) == TG_ERR_UNSUPPORTED

@@ -263,11 +263,18 @@ def test_select_distinct_random_scores_large():
     # 64-token tiles), the last one with more tiles than CUs
     (40000, 256, 256, 8, torch.bfloat16), (40000, 192, 128, 0, torch.bfloat16),
     (20000, 128, 256, 0, torch.bfloat16), (9000, 64, 64, 0, torch.bfloat16),
+    # D % 64 != 0 (a partial last stage of 8..56 columns), with row padding
+    # that holds NaN so that a read past column D would show
+    (1000, 72, 256, 8, torch.bfloat16), (300, 8, 64, 0, torch.bfloat16),
+    (2000, 2040, 256, 24, torch.bfloat16), (777, 200, 128, 56, torch.bfloat16),
+    (70001, 1000, 256, 8, torch.bfloat16), (40000, 136, 128, 0, torch.bfloat16),
     (513, 256, 64, 8, torch.float32),
     (77, 100, 30, 3, torch.float32)])
 def test_gate_shapes(T, D, F, ld_pad, dtype):
-    rng = np.random.default_rng(T)
+    rng = np.random.default_rng(T + D)
     h = torch.from_numpy(rng.standard_normal((T, D + ld_pad)).astype(np.float32)).to(dtype)
+    if D % 64:
+        h[:, D:] = float("nan")
     W1 = torch.from_numpy((rng.standard_normal((F, D)) / math.sqrt(D)).astype(np.float32)).to(dtype)
     b1 = torch.from_numpy((0.1 * rng.standard_normal(F)).astype(np.float32))
     w2 = torch.from_numpy((rng.standard_normal(F) / math.sqrt(F)).astype(np.float32))
