@@ -22,6 +22,7 @@ from .tokengate import (  # noqa: F401
     gate_backward,
     gated_attention,
     gated_attention_backward,
+    gated_attention_backward_columns,
     linear_residual,
     plan,
     pruned_layer,

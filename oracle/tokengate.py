@@ -392,6 +392,54 @@ def gated_attention_backward(q, k, v, bias, gain, tau: float, cu_kept, dout,
     return dq, dk, dv, ds, dg, dtau
 
 
+def gated_attention_backward_columns(q, k, v, bias, gain, tau: float, cu_kept, dout, out, lse,
+                                     cols: Sequence[int]):
+    """dk, dv and the bias gradient of some key columns, given the forward's
+    output and lse (the inputs the backward receives).
+
+    Same formulas as ``gated_attention_backward`` ("What is token-gated
+    attention?"), written per key column j of prompt b: over the visible
+    queries i >= j of the prompt and the query heads h of j's KV group,
+    ``P_ij = exp(x_ij - lse_hi)`` with the given lse, ``D_i = dout_i . out_i``
+    with the given output, ``dx_ij = P_ij (dout_i . v_j - D_i)``;
+        dk_j = tau / sqrt(d) sum_(h, i) dx_ij q_i
+        dv_j = sum_(h, i) P_ij dout_i
+        ds_j = sum_h g_h sum_i dx_ij        (all heads)
+    ``out`` [Kt, Hq, d], ``lse`` [Hq, Kt].  Returns fp64 (dk [n, Hkv, d],
+    dv [n, Hkv, d], ds [n]) for the n columns in ``cols`` order.
+    """
+    Q, K, V, dO = _f64(q), _f64(k), _f64(v), _f64(dout)
+    O, L = _f64(out), _f64(lse)
+    Kt, Hq, d = Q.shape
+    Hkv = K.shape[1]
+    group = Hq // Hkv
+    s = np.zeros(Kt) if bias is None else _f64(bias)
+    g = None if gain is None else _f64(gain)
+    cu = _i64(cu_kept)
+    scale = float(tau) / math.sqrt(d)
+    cols = _i64(cols)
+    dk = np.zeros((cols.shape[0], Hkv, d))
+    dv = np.zeros((cols.shape[0], Hkv, d))
+    ds = np.zeros(cols.shape[0])
+    for n, j in enumerate(cols):
+        b = int(np.searchsorted(cu, j, side="right")) - 1
+        hi = int(cu[b + 1])
+        for h in range(Hq):
+            kv = h // group
+            Qi, dOi = Q[j:hi, h], dO[j:hi, h]
+            x = scale * (Qi @ K[j, kv])
+            if g is not None:
+                x = x + g[h] * s[j]
+            P = np.exp(x - L[h, j:hi])
+            D = np.sum(dOi * O[j:hi, h], axis=1)
+            dx = P * (dOi @ V[j, kv] - D)
+            dk[n, kv] += scale * (dx @ Qi)
+            dv[n, kv] += P @ dOi
+            if g is not None:
+                ds[n] += g[h] * float(dx.sum())
+    return dk, dv, ds
+
+
 def _dq_rows(q, k, v, bias, gain, tau, cu_kept, dout, rows):
     """dq of some query rows: the same formulas as gated_attention_backward,
     one row at a time."""

@@ -23,9 +23,11 @@ c = tau / sqrt(d):
 Full size (the 128k workload's 8448 kept rows, 16 heads, GPU forward then
 GPU backward): dq of sampled rows against the oracle's exact dq, the bar
 adding c sum_j P_ij |delta_i| |k_j| for the forward output's own error
-delta_i = dout_i . (out_i - o_i) at that row; and identities that hold at
-any size: sum_j dv_j = sum_(h in group, i) dout_i, sum_j ds_j = 0,
-sum q.dq = sum k.dk = tau dtau.
+delta_i = dout_i . (out_i - o_i) at that row; dk, dv and dbias of sampled key
+columns (tile edges and random) against the oracle's column form given the
+GPU forward's output and lse, with the bars above restricted to the column;
+and identities that hold at any size: sum_j dv_j = sum_(h in group, i)
+dout_i, sum_j ds_j = 0, sum q.dq = sum k.dk = tau dtau.
 """
 
 import math
@@ -226,6 +228,37 @@ def test_attn_bwd_full_size_128k():
             tol = c * ((E + 2.0 ** -8 * np.abs(dx)) @ np.abs(K)) + 2.0 ** -8 * np.abs(ref[i, h])
             err = np.abs(dq[i, h] - ref[i, h])
             assert np.all(err <= tol), f"dq row {i} head {h}: max err {err.max()}, bar {tol[np.argmax(err)]}"
+    # dk, dv and the bias gradient of sampled key columns, element by element,
+    # against the oracle's column form given the GPU forward's stored output
+    # and lse (what the backward receives); bars as in _scales, per column
+    cols = np.unique(np.concatenate([[0, 1, 63, 64, 127, 128, 4095, 4096, Kt - 65, Kt - 64, Kt - 2, Kt - 1],
+                                     np.random.default_rng(1).integers(0, Kt, 20)]))
+    lse64 = _f64(lse)
+    rk, rv, rs = oracle.gated_attention_backward_columns(q64, k64, v64, b64, gn, s.tau, cu, g64, o64,
+                                                         lse64, cols)
+    r = 2.0 ** -8
+    for n, j in enumerate(cols):
+        t_k = np.zeros((s.Hkv, s.d))
+        t_v = np.zeros((s.Hkv, s.d))
+        t_s = 0.0
+        for h in range(s.Hq):
+            kv = h // grp
+            Q, G, O = q64[j:, h], g64[j:, h], o64[j:, h]
+            x = c * (Q @ k64[j, kv]) + gn[h] * b64[j]
+            P = np.exp(x - lse64[h, j:])
+            dP, D = G @ v64[j, kv], np.sum(G * O, axis=1)
+            adx = np.abs(P * (dP - D))
+            E = P * ((2 * s.d + 8) * 2.0 ** -24 * (np.abs(G) @ np.abs(v64[j, kv]) + np.sum(np.abs(G) * np.abs(O), axis=1))
+                     + 2.0 ** -16 * (np.abs(dP) + np.abs(D)))
+            t_k[kv] += c * ((E + r * adx) @ np.abs(Q))
+            t_v[kv] += (r + 2.0 ** -16) * (P @ np.abs(G))
+            t_s += abs(gn[h]) * float(np.sum(E + 2.0 ** -16 * adx))
+        for name, got, ref_, bar in (("dk", dk[j], rk[n], t_k + r * np.abs(rk[n])),
+                                     ("dv", dv[j], rv[n], t_v + r * np.abs(rv[n])),
+                                     ("dbias", ds[j], rs[n], t_s + 1e-6)):
+            err = np.abs(got - ref_)
+            assert np.all(err <= bar), f"{name} column {j}: max err {np.max(err)}, bar {np.min(bar)}"
+    _note(f"  columns {len(cols)}: dk, dv, dbias element-wise within their bars")
     # identities that hold at any size
     for kv in range(s.Hkv):
         lhs = dv[:, kv].sum(axis=0)

@@ -165,6 +165,28 @@ def test_decode_long_splits():
     _note(f"  worst error / bar {w:.3f}")
 
 
+@pytest.mark.parametrize("n,Hq,Hkv,d,dtype", [
+    (65536, 16, 8, 128, torch.bfloat16),   # one long sequence at the 1.7B head shapes
+    (131072, 8, 4, 64, torch.float32),
+])
+def test_decode_long_splits_one_sequence(n, Hq, Hkv, d, dtype):
+    """One sequence long enough for 256-key splits (Hkv * n / 256 >= 2048
+    workgroups), d = 128 and fp32."""
+    _note(f"[decode] one sequence of {n} keys, {Hq}/{Hkv} heads, d={d}, {dtype}")
+    assert Hkv * (n // 256) >= 2048
+    g = torch.Generator().manual_seed(n + d)
+    kc, vc, bc = _cache(n, Hkv, d, dtype, g)
+    q = torch.randn((1, Hq, d), generator=g).to(dtype)
+    gain = torch.rand(Hq, generator=g) + 0.5
+    start, lens = np.array([0], dtype=np.int32), [n]
+    out, lse = tg.tg_decode_attn(q.to(DEV), kc.to(DEV), vc.to(DEV), bc.to(DEV), gain.to(DEV), 1.15,
+                                 torch.from_numpy(start).to(DEV), torch.tensor(lens, dtype=torch.int32, device=DEV),
+                                 n, lse=torch.empty((1, Hq), device=DEV))
+    torch.cuda.synchronize()
+    w = _check_decode(out, lse, q, kc, vc, bc, start, lens, gain, 1.15, dtype)
+    _note(f"  worst error / bar {w:.3f}")
+
+
 def test_decode_full_size_128k():
     """One decode step over the 128k workload's 8448 kept keys, 16 heads."""
     _note("[decode full] 8448 keys")

@@ -29,8 +29,9 @@ pytestmark = pytest.mark.gpu
 DEV = "cuda"
 ATTN_TOL = {torch.bfloat16: 2e-2, torch.float32: 1e-4}
 LSE_TOL = {torch.bfloat16: 1e-3, torch.float32: 1e-4}
-SAMPLE_ROWS = 48  # per prompt, for kept lengths above FULL_ROWS
+SAMPLE_ROWS = 256  # random rows per prompt, for kept lengths above FULL_ROWS
 FULL_ROWS = 3000
+WAVE_ROWS = 32  # query rows per wave in both bf16 attention schedules
 
 
 def _f64(t):
@@ -94,10 +95,21 @@ NAMES = ["tiny_fp32_512", "tiny_fp32_b2", "ragged_tiny_fp32", "ragged_small_bf16
          "qwen3_1p7b_16k", "qwen3_1p7b_32k", "ragged_8x_4k_32k", "qwen3_1p7b_128k"]
 
 
-def _rows(cu_kept):
+def _rows(cu_kept, boundaries=False):
+    """None (every row) for short prompts; else SAMPLE_ROWS random rows per
+    prompt plus its first and last, and with ``boundaries`` the first and last
+    row of every 32-row block of a prompt (each wave's rows: the rows on both
+    sides of every 64-key tile's diagonal and of every 128- and 256-row query
+    tile edge)."""
     if int(np.max(np.diff(cu_kept), initial=0)) <= FULL_ROWS:
         return None
-    return oracle.attention_rows_for_check(cu_kept, SAMPLE_ROWS, seed=0)
+    rows = [oracle.attention_rows_for_check(cu_kept, SAMPLE_ROWS, seed=0)]
+    if boundaries:
+        for b in range(len(cu_kept) - 1):
+            lo, hi = int(cu_kept[b]), int(cu_kept[b + 1])
+            first = np.arange(lo, hi, WAVE_ROWS)
+            rows += [first, np.minimum(first + WAVE_ROWS - 1, hi - 1)]
+    return np.unique(np.concatenate(rows))
 
 
 def _attn_check(o_gpu, lse_gpu, q, k, v, bias, gain, tau, cu_kept, dtype, rows):
@@ -158,12 +170,13 @@ def test_pipeline_parity(name):
 def test_attention_parity(name):
     c = case(name)
     s = c.w.spec
-    rows = _rows(c.gp.cu_kept_h)
     for l in range(s.layers):
+        # the first layer also checks every wave's first and last row
+        rows = _rows(c.gp.cu_kept_h, boundaries=(l == 0))
         L = c.layer(l)
         err = _attn_check(L["o"], L["lse"], L["q"], L["k"], L["v"], c.bk, _f64(L["gain"]),
                           s.tau, c.gp.cu_kept_h, c.w.dtype, rows)
-        _note(f"[{name}] layer {l}: max-abs {err:.2e}")
+        _note(f"[{name}] layer {l}: {'all' if rows is None else len(rows)} rows, max-abs {err:.2e}")
 
 
 @pytest.mark.parametrize("name", ["tiny_fp32_512", "ragged_small_bf16", "qwen3_1p7b_16k"])
@@ -426,10 +439,29 @@ def test_attention_properties_on_gpu():
     for b in range(3):
         r = int(cu[b])
         assert torch.max(torch.abs(oc[r] - v[r].float().repeat_interleave(2, dim=0))).item() <= 2 ** -7
-    # shifting every bias by c leaves O unchanged (both runs within the bf16 bar of the oracle)
+    # shifting every bias by c leaves O unchanged and moves each head's lse by
+    # g_h c.  Against the GPU's own unshifted run: lse within 1e-4 of
+    # lse + g_h c; O within 2e-3 plus what re-rounding can move (the two runs
+    # compute each p in fp32 from different arguments, so a p near a bf16
+    # rounding boundary may round the other way, one bf16 ulp, at most 2^-7
+    # of p: 2^-7 sum_j P_j |v_j| in all; then the output's own rounding, one
+    # bf16 ulp of the value); the mean difference below 1e-4 (a flip is rare);
+    # and both runs within the bf16 bar of the oracle
+    lse_t = torch.from_numpy(lse).float()
+    ulp = lambda x: torch.exp2(torch.floor(torch.log2(x.abs().clamp_min(2.0 ** -126))) - 7)  # noqa: E731
+    pv_abs, _ = oracle.gated_attention(_f64(q), _f64(k), np.abs(_f64(v)), bias, gain.astype(np.float64),
+                                       1.15, cu)
+    flip = torch.from_numpy(2.0 ** -7 * pv_abs).float()
     for c in [-7.5, 3.0]:
-        oc2, _ = tg.tg_gated_attn_fwd(*args(v, (bias + c).astype(np.float32)))
+        oc2, lse2 = tg.tg_gated_attn_fwd(*args(v, (bias + c).astype(np.float32)), want_lse=True)
         torch.cuda.synchronize()
         _attn_check(oc2.cpu(), None, q, k, v, (bias + c).astype(np.float32), gain.astype(np.float64),
                     1.15, cu, torch.bfloat16, None)
-        assert torch.max(torch.abs(oc2.cpu().float() - oc)).item() <= 2e-2
+        shift = torch.from_numpy((gain.astype(np.float64) * c)).float()[:, None]
+        d_l = torch.abs(lse2.cpu() - lse_t - shift)
+        assert d_l.max().item() <= 1e-4, d_l.max().item()
+        d_o = torch.abs(oc2.cpu().float() - oc)
+        assert torch.all(d_o <= 2e-3 + ulp(oc) + flip), (d_o - ulp(oc) - flip).max().item()
+        assert d_o.mean().item() <= 1e-4, d_o.mean().item()
+        _note(f"[shift {c}] lse max {d_l.max().item():.2e}, O max {d_o.max().item():.2e} "
+              f"mean {d_o.mean().item():.2e}")

@@ -752,6 +752,35 @@ def test_attention_backward_row_subset_matches_full():
     assert np.all(np.isnan(part[[1, 10]]))
 
 
+def test_attention_backward_columns_match_full_backward():
+    # the per-column form (given the forward's lse and output) equals the
+    # matrix form of the full backward, itself pinned against autograd
+    rng = np.random.default_rng(61)
+    lens = [7, 1, 12, 0, 5]
+    Hq, Hkv, d = 6, 2, 8
+    cu, q, k, v, bias, gain = _rand_attn(rng, lens, Hq, Hkv, d)
+    dout = rng.standard_normal(q.shape)
+    o, lse = oracle.gated_attention(q, k, v, bias, gain, 0.9, cu)
+    full = oracle.gated_attention_backward(q, k, v, bias, gain, 0.9, cu, dout)
+    cols = np.arange(int(cu[-1]))[::-1]
+    dk, dv, ds = oracle.gated_attention_backward_columns(q, k, v, bias, gain, 0.9, cu, dout, o, lse,
+                                                         cols)
+    assert np.allclose(dk, full[1][cols], rtol=0, atol=1e-12)
+    assert np.allclose(dv, full[2][cols], rtol=0, atol=1e-12)
+    assert np.allclose(ds, full[3][cols], rtol=0, atol=1e-12)
+    # no bias: ds is zero; a stored output different from o changes D only
+    dk0, dv0, ds0 = oracle.gated_attention_backward_columns(q, k, v, None, None, 0.9, cu, dout,
+                                                            *oracle.gated_attention(q, k, v, None, None, 0.9, cu), cols)
+    full0 = oracle.gated_attention_backward(q, k, v, None, None, 0.9, cu, dout)
+    assert np.allclose(dk0, full0[1][cols], rtol=0, atol=1e-12) and np.all(ds0 == 0)
+    o_st = o + 1e-3 * rng.standard_normal(o.shape)
+    full_st = oracle.gated_attention_backward(q, k, v, bias, gain, 0.9, cu, dout, out=o_st)
+    dk1, dv1, _ = oracle.gated_attention_backward_columns(q, k, v, bias, gain, 0.9, cu, dout, o_st, lse,
+                                                          cols)
+    assert np.allclose(dk1, full_st[1][cols], rtol=0, atol=1e-12)
+    assert np.allclose(dv1, full_st[2][cols], rtol=0, atol=1e-12)
+
+
 def test_attention_backward_stored_output_variant():
     # with the exact forward output stored, the variant is the plain backward;
     # a perturbed stored output shifts every dx_ij by -P_ij delta_i, which a
