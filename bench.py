@@ -7,7 +7,9 @@ token-gated causal GQA attention layers over the kept tokens.  Inputs are
 resident in HBM before the timed region; every step re-runs all of it.  The
 timed steps replay the step captured in a HIP graph (one launch per step);
 the same step launched eagerly is timed too, with per-phase events, for the
-per-kernel figures.
+per-kernel figures.  After the timed region, single steps each preceded by a
+1 GiB write that evicts L2 and the last-level cache give the cold-cache
+median (``cold_cache``), reported beside the back-to-back figure.
 
 Prints one JSON line (stdout).  Progress goes to stderr.
 """
@@ -52,6 +54,10 @@ def parse():
                         "step captured in a HIP graph, and the eager loop is reported beside them)")
     p.add_argument("--no-reference-points", action="store_true",
                    help="skip the reference timings taken after the timed region")
+    p.add_argument("--flushed-reps", type=int, default=20,
+                   help="after the timed region, time this many single steps, each after a 1 GiB "
+                        "write that evicts L2 and the last-level cache, and report their median "
+                        "beside the back-to-back figure (0: skip)")
     return p.parse_args()
 
 
@@ -434,6 +440,33 @@ def main():
     ms_per_step = graph_ms if graph_ms is not None else eager_ms
     value = w.T / (ms_per_step / 1e3)
 
+    # Cold-cache protocol: every rep writes 1 GiB (evicting L2 and the 256 MB
+    # last-level cache), then one step runs between events; the median of the
+    # reps is reported beside the back-to-back steps above (whose inputs stay
+    # partly cache-resident from step to step).
+    flushed = None
+    if args.flushed_reps > 0:
+        flush_buf = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+        one = (lambda: g.replay()) if graph_ms is not None else (lambda: step())  # noqa: E731
+        reps = []
+        for _ in range(args.flushed_reps):
+            flush_buf.fill_(1)
+            a = torch.cuda.Event(enable_timing=True)
+            b = torch.cuda.Event(enable_timing=True)
+            a.record(stream)
+            one()
+            b.record(stream)
+            torch.cuda.synchronize()
+            reps.append(a.elapsed_time(b))
+        del flush_buf
+        med = float(np.median(reps))
+        flushed = {"ms_per_step_median": med, "tokens_per_s": w.T / (med / 1e3),
+                   "reps": args.flushed_reps, "min_ms": float(np.min(reps)),
+                   "max_ms": float(np.max(reps)), "flush_bytes": 1 << 30,
+                   "timing": "hip_graph_replay" if graph_ms is not None else "eager"}
+        log(f"[bench] {args.flushed_reps} steps after a cache flush: median {med:.4f} ms/step, "
+            f"{w.T / (med / 1e3):.4g} tokens/s")
+
     work = algorithmic_work(w, Kt, gp.cu_kept_h)
     phases = None
     roof = None
@@ -506,6 +539,7 @@ def main():
         "cpu_baseline": cpu,
         "phases": phases,
         "timing": "hip_graph_replay" if graph_ms is not None else "eager",
+        "cold_cache": flushed,
         "eager_ms_per_step": eager_ms,
         "reference_points": refs,
     }

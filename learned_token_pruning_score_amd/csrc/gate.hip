@@ -44,7 +44,9 @@ __device__ __forceinline__ void lds_load16(__amdgpu_buffer_rsrc_t r, char* lds, 
 // hidden that is the j-th 16 bytes of the 64 contiguous bytes it loads, and
 // the W1 fragments follow the same column map, so the products sum over the
 // same columns as the definition, in another order.
-template <int NFB, int FS>  // F = 32 * NFB, split over FS waves per token group
+// TAIL: D % 64 != 0 (a partial last stage; a separate instantiation, so the
+// loads of full-width inputs carry no selects).
+template <int NFB, int FS, bool TAIL>  // F = 32 * NFB, split over FS waves per token group
 __global__ __launch_bounds__(512, 1) void gate_bf16_kernel(
     const uint16_t* __restrict__ hidden, int64_t ld, int64_t T, int D, int n_tiles,
     const uint16_t* __restrict__ W1, const float* __restrict__ b1,
@@ -124,7 +126,7 @@ __global__ __launch_bounds__(512, 1) void gate_bf16_kernel(
     const uint16_t* hb_ptr = rows > 0 ? hidden + tt0 * ld + kk : hidden;
     const __amdgpu_buffer_rsrc_t rh = __builtin_amdgcn_make_buffer_rsrc((void*)hb_ptr, (short)0, hb, kBufFlags);
     const __amdgpu_buffer_rsrc_t rw = __builtin_amdgcn_make_buffer_rsrc((void*)(W1 + kk), (short)0, wb, kBufFlags);
-    const bool tail = ld_k == tail_stage;  // uniform
+    const bool tail = TAIL && ld_k == tail_stage;  // uniform
 #pragma unroll
     for (int j = 0; j < W_DMA; ++j)
       lds_load16(rw, sw + (wave * W_DMA + j) * 1024, (tail && w_dead[j]) ? wb : w_src[j]);
@@ -307,8 +309,15 @@ hipError_t launch_gate_bf16(const void* hidden, int64_t ld, int64_t T, int D, co
   const dim3 grid((unsigned)min(n_tiles, n_cu));
   const auto* h = static_cast<const uint16_t*>(hidden);
   const auto* w = static_cast<const uint16_t*>(W1);
-#define TG_GATE_LAUNCH(NFB_, FS_) \
-  hipLaunchKernelGGL((gate_bf16_kernel<NFB_, FS_>), grid, dim3(512), 0, s, h, ld, T, D, n_tiles, w, b1, w2, b2, scores)
+#define TG_GATE_LAUNCH(NFB_, FS_)                                                                                  \
+  do {                                                                                                             \
+    if (D % 64)                                                                                                    \
+      hipLaunchKernelGGL((gate_bf16_kernel<NFB_, FS_, true>), grid, dim3(512), 0, s, h, ld, T, D, n_tiles, w, b1,  \
+                         w2, b2, scores);                                                                          \
+    else                                                                                                           \
+      hipLaunchKernelGGL((gate_bf16_kernel<NFB_, FS_, false>), grid, dim3(512), 0, s, h, ld, T, D, n_tiles, w, b1, \
+                         w2, b2, scores);                                                                          \
+  } while (0)
   if (F == 64) {
     if (fs == 1) TG_GATE_LAUNCH(2, 1); else TG_GATE_LAUNCH(2, 2);
   } else if (F == 128) {
