@@ -4,11 +4,13 @@
 // token-gated attention?": each kept token's score becomes its logit bias).
 //
 // Kept token t goes to row r = number of kept tokens before t, so rows follow
-// the original order prompt by prompt.  Three kernels:
+// the original order prompt by prompt.  Kernels:
 //   cmp_count  per chunk of kCmpChunk tokens: number of kept flags
 //   cmp_index  per chunk: its base row is the sum of the counts before it;
 //              a block scan of the flags gives each kept token its row, and
 //              the owning thread writes the row's source token
+//   (up to kFuseMaxT tokens one kernel, cmp_index_fused, does both: each
+//   workgroup counts the flags before its chunk itself)
 //   cmp_copy   one wave per kept row: the hidden row is copied byte-exactly
 //              in 16-byte units (or element by element when rows or
 //              pointers are not 16-byte aligned), every lane issuing all its
@@ -101,6 +103,79 @@ __global__ __launch_bounds__(kCmpThreads) void cmp_index(
   }
 }
 
+// Count and index in one kernel, for inputs of up to kFuseMaxT tokens: each
+// workgroup counts the kept flags before its chunk of kFuseChunk tokens
+// itself (16 flags per 16-byte load, every load of a thread in flight at
+// once), instead of summing per-chunk counts written by an earlier kernel.
+// The flag array must be 16-byte aligned (checked on the host).
+constexpr int kFuseThreads = 1024;
+constexpr int kFuseChunk = 4 * kFuseThreads;
+constexpr int64_t kFuseMaxT = (int64_t)1 << 18;
+constexpr int kFuseLoads = (int)(kFuseMaxT / 16 / kFuseThreads);  // 16-byte loads per thread at most
+
+// nonzero bytes of a 32-bit word (a flag is kept when nonzero)
+__device__ __forceinline__ int nz_bytes(unsigned w) {
+  return __popc((((w & 0x7F7F7F7Fu) + 0x7F7F7F7Fu) | w) & 0x80808080u);
+}
+
+__global__ __launch_bounds__(kFuseThreads) void cmp_index_fused(
+    const uint8_t* __restrict__ keep, int64_t T, int64_t Kt, int32_t* __restrict__ src_out) {
+  __shared__ int wsum[kFuseThreads / 64];
+  __shared__ int s_row0;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int64_t c0 = (int64_t)blockIdx.x * kFuseChunk;
+  // kept flags before the chunk (c0 / 16 whole 16-byte words)
+  const uint4* k4 = reinterpret_cast<const uint4*>(keep);
+  const int n16 = (int)(c0 / 16);
+  uint4 w[kFuseLoads];
+#pragma unroll
+  for (int j = 0; j < kFuseLoads; ++j) {
+    const int i = tid + j * kFuseThreads;
+    w[j] = i < n16 ? k4[i] : make_uint4(0u, 0u, 0u, 0u);
+  }
+  int pre = 0;
+#pragma unroll
+  for (int j = 0; j < kFuseLoads; ++j) pre += nz_bytes(w[j].x) + nz_bytes(w[j].y) + nz_bytes(w[j].z) + nz_bytes(w[j].w);
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) pre += __shfl_xor(pre, off);
+  if (lane == 0) wsum[wave] = pre;
+  __syncthreads();
+  if (tid == 0) {
+    int sum = 0;
+    for (int v = 0; v < kFuseThreads / 64; ++v) sum += wsum[v];
+    s_row0 = sum;
+  }
+  __syncthreads();
+  const int row0 = s_row0;
+  __syncthreads();  // wsum is reused below
+
+  const int64_t base = c0 + tid * 4;
+  int f[4];
+  int c = 0;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    f[j] = (base + j < T && keep[base + j]) ? 1 : 0;
+    c += f[j];
+  }
+  int incl = c;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const int y = __shfl_up(incl, off);
+    if (lane >= off) incl += y;
+  }
+  if (lane == 63) wsum[wave] = incl;
+  __syncthreads();
+  int wbase = 0;
+  for (int v = 0; v < wave; ++v) wbase += wsum[v];
+  int r = row0 + wbase + incl - c;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    if (!f[j]) continue;
+    if (r < Kt) src_out[r] = (int32_t)(base + j);  // flags beyond the stated Kt write nothing
+    ++r;
+  }
+}
+
 // MODE 1: 16-byte units; 0: 4-byte elements; 2: 2-byte elements.
 template <int MODE>
 __global__ __launch_bounds__(64 * kRowsPerCopyWG) void cmp_copy(
@@ -172,8 +247,13 @@ hipError_t launch_compact(const void* hidden, int64_t ld, int D, int elem_bytes,
   int32_t* src = reinterpret_cast<int32_t*>(static_cast<char*>(ws) + counts_bytes);
   const int row_bytes = D * elem_bytes;
   const int64_t ld_bytes = ld * elem_bytes;
-  hipLaunchKernelGGL(cmp_count, dim3(nchunks), dim3(kCmpThreads), 0, s, keep, T, counts);
-  hipLaunchKernelGGL(cmp_index, dim3(nchunks), dim3(kCmpThreads), 0, s, keep, T, counts, Kt, src);
+  if (T <= kFuseMaxT && ((uintptr_t)keep % 16) == 0) {
+    hipLaunchKernelGGL(cmp_index_fused, dim3((unsigned)((T + kFuseChunk - 1) / kFuseChunk)), dim3(kFuseThreads),
+                       0, s, keep, T, Kt, src);
+  } else {
+    hipLaunchKernelGGL(cmp_count, dim3(nchunks), dim3(kCmpThreads), 0, s, keep, T, counts);
+    hipLaunchKernelGGL(cmp_index, dim3(nchunks), dim3(kCmpThreads), 0, s, keep, T, counts, Kt, src);
+  }
   if (Kt > 0) {
     const dim3 grid((unsigned)((Kt + kRowsPerCopyWG - 1) / kRowsPerCopyWG));
     const dim3 block(64 * kRowsPerCopyWG);

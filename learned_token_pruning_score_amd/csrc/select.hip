@@ -208,6 +208,20 @@ __global__ __launch_bounds__(kThreads) void sel_pass(const float* __restrict__ s
   if (c.mode != 2) return;
   const int b = blockIdx.y;
   const int x = blockIdx.x;
+  const bool has_doc = x >= c.x_first && x <= c.x_last;  // uniform
+  const int d0 = max(c.c0, c.lo), d1 = min(c.c1, c.hi);
+  // The first round's scores do not depend on the digits picked so far:
+  // their loads are issued before the pick, so the two memory round trips
+  // overlap; the histogram is cleared before the pick's barriers too.
+  float v[kPer];
+  if (has_doc) {
+#pragma unroll
+    for (int j = 0; j < kPer; ++j) {
+      const int t = d0 + (int)threadIdx.x + j * kThreads;
+      v[j] = t < d1 ? scores[t] : 0.0f;
+    }
+    for (int i = threadIdx.x; i < kBins; i += kThreads) lh[i] = 0u;
+  }
   SelState s;
   if (P == 0) {
     s.prefix = 0u;
@@ -218,20 +232,19 @@ __global__ __launch_bounds__(kThreads) void sel_pass(const float* __restrict__ s
     s = pick_digit(P - 1, in, (P - 1) & 1 ? part1 : part0, c, &n_bin, wtot, s_res);
     if (x == c.x_first && threadIdx.x == 0) st[(size_t)(P - 1) * B + b] = s;
   }
-  if (x < c.x_first || x > c.x_last) return;  // no document token here
-  for (int i = threadIdx.x; i < kBins; i += kThreads) lh[i] = 0u;
+  if (!has_doc) return;  // no document token here
   __syncthreads();
-  const int d0 = max(c.c0, c.lo), d1 = min(c.c1, c.hi);
   constexpr unsigned fm = fixed_mask(P);
   constexpr int sh = digit_shift(P);
   constexpr unsigned dm = digit_mask(P);
   // kPer keys per thread and round, all loads issued before the first use
   for (int r0 = d0; r0 < d1; r0 += kPer * kThreads) {
-    float v[kPer];
+    if (r0 != d0) {
 #pragma unroll
-    for (int j = 0; j < kPer; ++j) {
-      const int t = r0 + (int)threadIdx.x + j * kThreads;
-      v[j] = t < d1 ? scores[t] : 0.0f;
+      for (int j = 0; j < kPer; ++j) {
+        const int t = r0 + (int)threadIdx.x + j * kThreads;
+        v[j] = t < d1 ? scores[t] : 0.0f;
+      }
     }
 #pragma unroll
     for (int j = 0; j < kPer; ++j) {
@@ -268,6 +281,17 @@ __global__ __launch_bounds__(kThreads) void sel_mark(const float* __restrict__ s
   int eq_keep = 0;   // equal keys kept (over the whole document)
   int eq_before = 0; // equal keys in the document's earlier chunks
   bool all_eq = true;
+  // the first round's scores, loaded before the pick (they do not depend on
+  // it), so the two memory round trips overlap
+  float v[kPer];
+  auto load_round = [&](int r0) __attribute__((always_inline)) {
+#pragma unroll
+    for (int j = 0; j < kPer; ++j) {
+      const int t = r0 + tid + j * kThreads;
+      v[j] = (t < c.c1 && t >= c.lo && t < c.hi) ? scores[t] : 0.0f;
+    }
+  };
+  if (c.mode == 2) load_round(c.c0);
   if (c.mode == 2) {
     unsigned n_eq;
     const SelState s = pick_digit(2, st[(size_t)B + b], part0, c, &n_eq, wtot, s_res);
@@ -286,14 +310,7 @@ __global__ __launch_bounds__(kThreads) void sel_mark(const float* __restrict__ s
   // score loads all issued before the first use; index order within a round
   // is (j, tid)
   for (int r0 = c.c0; r0 < c.c1; r0 += kPer * kThreads) {
-    float v[kPer];
-    if (c.mode == 2) {
-#pragma unroll
-      for (int j = 0; j < kPer; ++j) {
-        const int t = r0 + tid + j * kThreads;
-        v[j] = (t < c.c1 && t >= c.lo && t < c.hi) ? scores[t] : 0.0f;
-      }
-    }
+    if (c.mode == 2 && r0 != c.c0) load_round(r0);
 #pragma unroll
     for (int j = 0; j < kPer; ++j) {
       const int t = r0 + tid + j * kThreads;
