@@ -268,6 +268,9 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_bf16_kernel(
       for (int hh = 0; hh < 2; ++hh)
 #pragma unroll
         for (int j = 0; j < 8; ++j) pb[kb][hh][j] = (__bf16)s[kb][8 * hh + j];
+    // the whole softmax stays in this (vector ALU) interval: nothing of it
+    // may sink past the barrier into the wave's next (MFMA) interval
+    __builtin_amdgcn_sched_barrier(0);
   };
   // O^T += V^T P^T for the tile whose probabilities are in pb, V^T
   // fragments read VAHEAD MFMAs ahead.  A transposing LDS read
@@ -649,6 +652,9 @@ __global__ __launch_bounds__(512, 1) void attn_bf16_ks_kernel(
       for (int hh = 0; hh < 2; ++hh)
 #pragma unroll
         for (int j = 0; j < 8; ++j) pb[kb][hh][j] = (__bf16)s[kb][8 * hh + j];
+    // the whole softmax stays in this (vector ALU) interval: nothing of it
+    // may sink past the barrier into the wave's next (MFMA) interval
+    __builtin_amdgcn_sched_barrier(0);
   };
   auto pv = [&](int t) __attribute__((always_inline)) {
     const int gi = lane & 15, g = lane >> 4;
