@@ -85,6 +85,31 @@ __device__ __forceinline__ void proj_lds_load16(__amdgpu_buffer_rsrc_t r, char* 
   __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)lds, 16, voff, 0, 0, 0);
 }
 
+// LDS byte offset of a pointer into a __shared__ array.
+__device__ __forceinline__ uint32_t lds_off(const char* p) {
+  return (uint32_t)(uintptr_t)(__attribute__((address_space(3))) const char*)p;
+}
+
+// Four 16-byte LDS reads and the wait for them, in one asm block (so the
+// compiler neither reorders nor re-waits them).
+__device__ __forceinline__ void lds_read4_wait(const uint32_t (&a)[4], bf16x8 (&f)[4]) {
+  typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+  u32x4 r0, r1, r2, r3;
+  asm volatile(
+      "ds_read_b128 %0, %4\n\t"
+      "ds_read_b128 %1, %5\n\t"
+      "ds_read_b128 %2, %6\n\t"
+      "ds_read_b128 %3, %7\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(r0), "=&v"(r1), "=&v"(r2), "=&v"(r3)
+      : "v"(a[0]), "v"(a[1]), "v"(a[2]), "v"(a[3])
+      : "memory");
+  f[0] = __builtin_bit_cast(bf16x8, r0);
+  f[1] = __builtin_bit_cast(bf16x8, r1);
+  f[2] = __builtin_bit_cast(bf16x8, r2);
+  f[3] = __builtin_bit_cast(bf16x8, r3);
+}
+
 __device__ __forceinline__ uint2 pack_bf16x4(float a, float b, float c, float d) {
   const __bf16 e0 = (__bf16)a, e1 = (__bf16)b, e2 = (__bf16)c, e3 = (__bf16)d;
   uint2 pk;
@@ -509,12 +534,14 @@ __global__ __launch_bounds__(256) void proj_tail_kernel(ProjArgs g) {
     for (int ks = 0; ks < 4; ++ks) {
       if (64 * st + 16 * ks < kq) {
         const int c = 2 * ks + (lane >> 5);
-        bf16x8 f[4];
+        uint32_t ad[4];
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
           const int row = 32 * q + r;
-          f[q] = *reinterpret_cast<const bf16x8*>(buf + row * 128 + proj_swz(row, c) * 16);
+          ad[q] = lds_off(buf + row * 128 + proj_swz(row, c) * 16);
         }
+        bf16x8 f[4];
+        lds_read4_wait(ad, f);
         acc[0][0] = mfma32x32x16(f[0], f[2], acc[0][0]);
         acc[0][1] = mfma32x32x16(f[0], f[3], acc[0][1]);
         acc[1][0] = mfma32x32x16(f[1], f[2], acc[1][0]);
@@ -524,20 +551,22 @@ __global__ __launch_bounds__(256) void proj_tail_kernel(ProjArgs g) {
   };
   char* b0 = st0[wave];
   char* b1 = st1[wave];
+  // The fragment reads are inline asm that waits for its own LDS reads, so
+  // the compiler adds no wait for the buffer-to-LDS loads: the waits below
+  // are explicit and counted (16 loads per stage, issued in order), so a
+  // stage's loads stay in flight while the other stage is computed.
   issue(b0, 0);
   if (nst > 1) issue(b1, 1);
   for (int st = 0; st < nst; st += 2) {
+    if (st + 1 < nst) asm volatile("s_waitcnt vmcnt(16)" ::: "memory");
+    else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     compute(b0, st);
-    if (st + 2 < nst) {
-      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // reads of b0 done before it is refilled
-      issue(b0, st + 2);
-    }
+    if (st + 2 < nst) issue(b0, st + 2);  // compute's reads have completed
     if (st + 1 < nst) {
+      if (st + 2 < nst) asm volatile("s_waitcnt vmcnt(16)" ::: "memory");
+      else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
       compute(b1, st + 1);
-      if (st + 3 < nst) {
-        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-        issue(b1, st + 3);
-      }
+      if (st + 3 < nst) issue(b1, st + 3);
     }
   }
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
