@@ -163,7 +163,8 @@ int tg_select_topk(const float* scores, const int32_t* cu_seqlens,
  * tg_select_topk; the workspace is a static device array inside the library
  * (4 MiB, one copy per GPU, held until the process ends).  The call itself
  * allocates nothing: on its first use on a device it only looks up that
- * array's address.
+ * array's address (the array of the stream's device; of the current device
+ * for the null stream).
  * Limit: the tg_select_topk_workspace size of (B, T) must fit in 4 MiB when
  * T > 32768 (about B <= 190 prompts at any T; T <= 32768 needs no scratch),
  * else TG_ERR_WORKSPACE before any device work.

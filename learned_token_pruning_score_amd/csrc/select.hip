@@ -513,17 +513,30 @@ size_t select_scratch_bytes_needed(int B, int64_t T) {
   return (B == 0 || T == 0 || T <= kSingleMaxT) ? 0 : select_workspace_bytes(B, T);
 }
 
-hipError_t select_static_scratch(void** ptr) {
-  // resolved once per device, with that device current; concurrent first
-  // calls resolve and store the same address
+hipError_t select_static_scratch(hipStream_t stream, void** ptr) {
+  // The array of the device the stream belongs to (the current device for
+  // the null stream), resolved once per device with that device current;
+  // concurrent first calls resolve and store the same address.
   static std::atomic<void*> addr[64];
-  int dev = 0;
-  hipError_t e = hipGetDevice(&dev);
+  int cur = 0;
+  hipError_t e = hipGetDevice(&cur);
   if (e != hipSuccess) return e;
+  int dev = cur;
+  if (stream != nullptr) {
+    hipDevice_t sd = 0;
+    e = hipStreamGetDevice(stream, &sd);
+    if (e != hipSuccess) return e;
+    dev = (int)sd;
+  }
   if (dev < 0 || dev >= 64) return hipErrorInvalidDevice;
   void* p = addr[dev].load(std::memory_order_acquire);
   if (p == nullptr) {
+    if (dev != cur && (e = hipSetDevice(dev)) != hipSuccess) return e;
     e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (dev != cur) {
+      const hipError_t e2 = hipSetDevice(cur);
+      if (e == hipSuccess) e = e2;
+    }
     if (e != hipSuccess) return e;
     if (p == nullptr) return hipErrorInvalidSymbol;
     addr[dev].store(p, std::memory_order_release);

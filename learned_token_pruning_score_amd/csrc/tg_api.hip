@@ -158,7 +158,7 @@ int tg_select_topk_noalloc(const float* scores, const int32_t* cu_seqlens,
   if (T == 0) return TG_OK;
   void* ws = nullptr;
   if (need > 0) {
-    const hipError_t e = tg::select_static_scratch(&ws);
+    const hipError_t e = tg::select_static_scratch(as_stream(stream), &ws);
     if (e != hipSuccess) return TG_ERR_HIP;
   }
   return from_hip(tg::launch_select(scores, cu_seqlens, doc_begin, doc_end, budget, B, T, keep, ws,

@@ -57,7 +57,7 @@ size_t select_workspace_bytes(int B, int64_t T);
 // its address on the current device.
 size_t select_scratch_bytes_needed(int B, int64_t T);
 size_t select_static_scratch_capacity();
-hipError_t select_static_scratch(void** ptr);
+hipError_t select_static_scratch(hipStream_t stream, void** ptr);
 hipError_t launch_select(const float* scores, const int32_t* cu, const int32_t* db,
                          const int32_t* de, const int32_t* budget, int B, int64_t T,
                          uint8_t* keep, void* ws, hipStream_t s);

@@ -72,3 +72,20 @@ def test_noalloc_rejects_oversized_before_any_work():
     assert e.value.status == -7
     torch.cuda.synchronize()
     assert int(keep.min()) == 9 and int(keep.max()) == 9  # nothing written
+
+
+def test_noalloc_on_a_created_stream():
+    # the scratch is looked up for the stream's device (hipStreamGetDevice)
+    rng = np.random.default_rng(77)
+    T = 70000
+    s = rng.standard_normal(T).astype(np.float32)
+    cu, db, de, bud = [0, T], [0], [T - 100], [5000]
+    st = torch.from_numpy(s).to(DEV)
+    meta = [torch.tensor(np.asarray(a, np.int32), device=DEV) for a in (cu, db, de, bud)]
+    keep = torch.full((T,), 7, dtype=torch.uint8, device=DEV)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        tg.tg_select_topk_noalloc(st, *meta, keep=keep)
+    side.synchronize()
+    assert np.array_equal(keep.cpu().numpy(), oracle.select_topk(s, cu, db, de, bud))
