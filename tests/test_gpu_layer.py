@@ -14,7 +14,11 @@ Bars (written here; u = 2^-24 the fp32 unit roundoff, "bf16 term"
     E_g, E_u = 2 (D + 4) u S_g, S_u the accumulation bounds of the two dot
     products (|silu'| <= 1.1), 2^-19 for the exponential and reciprocal.
   * whole layer (bf16 intermediates rounded at every step): the relative
-    2-norm error of the layer's update y - x below 3e-2.
+    2-norm error of the layer's update y - x below 3e-2 against the fp64
+    oracle layer; and step by step, each intermediate element-wise at its
+    own step's bar against the oracle step fed the GPU's previous output
+    (q/k/v and attention at the bars of their own tests), with the in-place
+    pipeline layer bit-identical to the steps.
 Full size: the 128k-token workload's 8448 kept rows at the Qwen3-1.7B
 shapes (D 2048, Hq d 2048, I 6144), in the benchmark's launch
 configuration, on sampled rows.
@@ -209,3 +213,51 @@ def test_pruned_layer_chain(name):
     err = np.linalg.norm(upd - upd_ref) / np.linalg.norm(upd_ref)
     _note(f"  relative error of the layer update: {err:.2e}")
     assert err <= 3e-2
+
+
+@pytest.mark.parametrize("name", ["ragged_small_bf16", "ragged_tiny_fp32"])
+def test_pruned_layer_steps(name):
+    """The layer one call at a time, every intermediate in its own buffer:
+    each step checked element-wise against the oracle step fed the GPU's
+    previous output, at the bars above (q/k/v and attention at their own
+    tests' bars), and the in-place pipeline bit-identical to the steps."""
+    from test_gpu_parity import _attn_check
+    from test_gpu_qkv import THETA, _check_qkv
+    _note(f"[pruned layer, step by step] {name}")
+    w = synth.make_workload(name, seed=3)
+    s = w.spec
+    assert s.rope_theta == THETA
+    dt = w.dtype
+    gp = tg.GatedPrefill(w.cu_seqlens, w.doc_begin, w.doc_end, w.budget, s.D, dt)
+    gp.gate_and_select(w.hidden.to(DEV), w.W1.to(DEV), w.b1.to(DEV), w.w2.to(DEV), w.b2)
+    gp.rope(s.d, s.rope_theta)
+    Wqkv = synth.qkv_weights(name, 0, seed=3).to(DEV)
+    lw = {k: v.to(DEV) for k, v in synth.layer_weights(name, 0, seed=3).items()}
+    gain = torch.linspace(0.5, 2.0, s.Hq)
+    Kt, Hq, Hkv, d = gp.Kt, s.Hq, s.Hkv, s.d
+    x0 = gp.hidden_k.clone()
+    xn1 = tg.tg_rms_norm(x0, lw["w_in"], s.norm_eps)
+    qkv, q, k, v = tg.tg_qkv_rope(xn1, Wqkv, gp.rope_table, Hq, Hkv, d)
+    att, lse = gp.attend(q, k, v, gain.to(DEV), s.tau, lse=torch.empty((Hq, Kt), device=DEV))
+    x1 = tg.tg_linear_residual(att.view(Kt, Hq * d), lw["W_o"], x0)
+    xn2 = tg.tg_rms_norm(x1, lw["w_post"], s.norm_eps)
+    act = tg.tg_swiglu(xn2, lw["W_gate"], lw["W_up"])
+    y = tg.tg_linear_residual(act, lw["W_down"], x1)
+    torch.cuda.synchronize()
+    cpu = {n: t.cpu() for n, t in dict(x0=x0, xn1=xn1, qkv=qkv, q=q, k=k, v=v, att=att, lse=lse, x1=x1,
+                                       xn2=xn2, act=act, y=y).items()}
+    for xin, wn, xout in (("x0", "w_in", "xn1"), ("x1", "w_post", "xn2")):
+        ref = oracle.rms_norm(_f64(cpu[xin]), _f64(lw[wn]), s.norm_eps)
+        tol = _rel(dt) * np.abs(ref) + (s.D + 16) * U * np.abs(ref)
+        _assert_within(_f64(cpu[xout]), ref, tol, f"rms_norm {xout}")
+    _check_qkv(cpu["qkv"], cpu["xn1"], Wqkv.cpu(), gp.pos_k.cpu().numpy(), Hq, Hkv, d, dt)
+    _attn_check(cpu["att"], cpu["lse"], cpu["q"], cpu["k"], cpu["v"], gp.bias_s.cpu().numpy().astype(np.float64),
+                _f64(gain), s.tau, gp.cu_kept_h, dt, None)
+    _lr_check(cpu["x1"], cpu["att"].reshape(Kt, Hq * d), lw["W_o"].cpu(), cpu["x0"], dt)
+    _sw_check(cpu["act"], cpu["xn2"], lw["W_gate"].cpu(), lw["W_up"].cpu(), dt)
+    _lr_check(cpu["y"], cpu["act"], lw["W_down"].cpu(), cpu["x1"], dt)
+    # the pipeline's in-place layer runs the same launches on the same inputs
+    x_pipe = x0.clone()
+    y_pipe = gp.pruned_layer(Wqkv, lw, Hq, Hkv, d, gain.to(DEV), s.tau, s.norm_eps, x=x_pipe)
+    torch.cuda.synchronize()
+    assert torch.equal(y_pipe, y)
