@@ -183,7 +183,7 @@ def tg_gate_score(hidden: torch.Tensor, W1: torch.Tensor, b1: Optional[torch.Ten
     lib = load_library()
     T, D = hidden.shape
     F = W1.shape[0]
-    if hidden.stride(1) != 1 or not W1.is_contiguous() or W1.shape[1] != D:
+    if not _unit_cols(hidden) or not W1.is_contiguous() or W1.shape[1] != D:
         raise ValueError("hidden must have unit column stride and W1 must be [F, D] contiguous")
     if W1.dtype != hidden.dtype:
         raise TypeError("W1 and hidden must share a dtype")
@@ -260,7 +260,7 @@ def tg_compact(hidden: torch.Tensor, pos: Optional[torch.Tensor], scores: torch.
     T, D = hidden.shape
     B = doc_begin.shape[0]
     dev = hidden.device
-    if hidden.stride(1) != 1:
+    if not _unit_cols(hidden):
         raise ValueError("hidden must have unit column stride")
     if out is None:
         hk = torch.empty((Kt, D), dtype=hidden.dtype, device=dev)
@@ -299,7 +299,7 @@ def tg_gated_attn_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
     for name, t, H in (("q", q, Hq), ("k", k, Hkv), ("v", v, Hkv)):
         if t.dim() != 3 or t.shape[0] != Kt or t.shape[2] != d or t.shape[1] != H:
             raise ValueError(f"{name} has shape {tuple(t.shape)}")
-        if t.stride(2) != 1 or t.stride(1) != d:
+        if t.numel() and (t.stride(2) != 1 or t.stride(1) != d):
             raise ValueError(f"{name} must have heads contiguous inside a token")
         if t.dtype != q.dtype:
             raise TypeError("q, k, v must share a dtype")
@@ -348,7 +348,7 @@ def tg_qkv_rope(x: torch.Tensor, w_qkv: torch.Tensor, rope_table: torch.Tensor, 
     """
     _require_gpu()
     lib = load_library()
-    if x.dim() != 2 or x.stride(1) != 1:
+    if x.dim() != 2 or not _unit_cols(x):
         raise ValueError("x must be [Kt, D] with unit column stride")
     Kt, D = x.shape
     N = (Hq + 2 * Hkv) * d
@@ -358,7 +358,7 @@ def tg_qkv_rope(x: torch.Tensor, w_qkv: torch.Tensor, rope_table: torch.Tensor, 
         raise ValueError(f"rope_table has shape {tuple(rope_table.shape)}")
     if out is None:
         out = torch.empty((Kt, N), dtype=x.dtype, device=x.device)
-    elif out.dim() != 2 or out.shape[0] != Kt or out.shape[1] < N or out.stride(1) != 1:
+    elif out.dim() != 2 or out.shape[0] != Kt or out.shape[1] < N or not _unit_cols(out):
         raise ValueError(f"out has shape {tuple(out.shape)}")
     if out.dtype != x.dtype:
         raise TypeError("out must have the dtype of x")
@@ -372,8 +372,14 @@ def tg_qkv_rope(x: torch.Tensor, w_qkv: torch.Tensor, rope_table: torch.Tensor, 
     return out, q, k, v
 
 
+def _unit_cols(t: torch.Tensor) -> bool:
+    """Unit stride along the last dimension (any strides for an empty
+    tensor: it is never read)."""
+    return t.numel() == 0 or t.stride(-1) == 1
+
+
 def _rows2d(t: torch.Tensor, name: str) -> None:
-    if t.dim() != 2 or t.stride(1) != 1:
+    if t.dim() != 2 or not _unit_cols(t):
         raise ValueError(f"{name} must be 2-D with unit column stride")
 
 
@@ -511,7 +517,7 @@ def tg_gate_bwd(hidden_k: torch.Tensor, W1: torch.Tensor, b1: Optional[torch.Ten
     [Kt, D], dW1 [F, D] fp32, db1 [F] fp32, dw2 [F] fp32, db2 [1] fp32)."""
     _require_gpu()
     lib = load_library()
-    if hidden_k.dim() != 2 or hidden_k.stride(1) != 1:
+    if hidden_k.dim() != 2 or not _unit_cols(hidden_k):
         raise ValueError("hidden_k must be [Kt, D] with unit column stride")
     Kt, D = hidden_k.shape
     F = W1.shape[0]
