@@ -189,6 +189,29 @@ def test_attn_bwd_parity(lens, Hq, Hkv, d, dtype, with_bias):
         assert torch.equal(a, b)
 
 
+@pytest.mark.parametrize("seed", range(12))
+def test_attn_bwd_random(seed):
+    """Seeded random shapes: 1-4 prompts of 0-420 rows, GQA groups 1-8, d
+    64/128, bf16 and fp32, with and without the bias, tau 0.5-2."""
+    rng = np.random.default_rng(7000 + seed)
+    Hq, Hkv = [(4, 2), (8, 1), (6, 3), (2, 2), (16, 8)][int(rng.integers(0, 5))]
+    d = int(rng.choice([64, 128]))
+    dtype = torch.bfloat16 if rng.random() < 0.7 else torch.float32
+    with_bias = bool(rng.random() < 0.75)
+    lens = [int(x) for x in rng.integers(0, 421, int(rng.integers(1, 5)))]
+    if sum(lens) == 0:
+        lens[0] = 1
+    tau = float(rng.uniform(0.5, 2.0))
+    _note(f"[attn bwd random {seed}] lens={lens} Hq={Hq} Hkv={Hkv} d={d} {dtype} bias={with_bias} tau={tau:.3f}")
+    cu, q, k, v, dout, bias, gain = _inputs(lens, Hq, Hkv, d, dtype, seed=100 + seed, with_bias=with_bias)
+    o, lse = oracle.gated_attention(_f64(q), _f64(k), _f64(v), _f64(bias),
+                                    None if gain is None else _f64(gain), tau, cu)
+    out_st = torch.from_numpy(np.nan_to_num(o)).to(dtype)
+    lse_st = torch.from_numpy(np.nan_to_num(lse)).to(torch.float32)
+    grads = _run_stored(cu, q, k, v, dout, bias, gain, tau, out_st, lse_st)
+    _check_all(cu, q, k, v, dout, bias, gain, tau, grads, out_st, dtype)
+
+
 def test_attn_bwd_full_size_128k():
     """The 128k workload's kept rows (one prompt of 8448 rows), 16 heads."""
     name = "qwen3_1p7b_128k"

@@ -94,6 +94,39 @@ def test_decode_attn_parity(lens, Hq, Hkv, d, dtype, with_bias):
     _note(f"  worst error / bar {w:.3f}")
 
 
+@pytest.mark.parametrize("seed", range(12))
+def test_decode_attn_random(seed):
+    """Seeded random caches: 1-40 sequences of 1-3000 keys (some at split
+    boundaries), random gaps between them, GQA groups 1-8, d 64/128, bf16 and
+    fp32, with and without the bias, tau 0.5-2."""
+    rng = np.random.default_rng(8000 + seed)
+    Hq, Hkv = [(16, 8), (8, 1), (6, 3), (4, 4), (2, 1)][int(rng.integers(0, 5))]
+    d = int(rng.choice([64, 128]))
+    dtype = torch.bfloat16 if rng.random() < 0.7 else torch.float32
+    with_bias = bool(rng.random() < 0.75)
+    B = int(rng.integers(1, 41))
+    lens = [int(x) for x in rng.integers(1, 3001, B)]
+    for j in range(B):
+        if rng.random() < 0.15:
+            lens[j] = int(rng.choice([1, 128, 129, 255, 256, 257, 512]))
+    gaps = [int(x) for x in rng.integers(0, 50, B)]
+    start = np.cumsum([0] + [n + gp for n, gp in zip(lens[:-1], gaps[:-1])]).astype(np.int32)
+    rows = int(start[-1] + lens[-1] + gaps[-1])
+    tau = float(rng.uniform(0.5, 2.0))
+    _note(f"[decode random {seed}] B={B} max len {max(lens)} Hq={Hq} Hkv={Hkv} d={d} {dtype} bias={with_bias}")
+    g = torch.Generator().manual_seed(300 + seed)
+    kc, vc, bc = _cache(rows, Hkv, d, dtype, g)
+    q = torch.randn((B, Hq, d), generator=g).to(dtype)
+    gain = torch.rand(Hq, generator=g) * 1.5 + 0.5 if with_bias else None
+    out, lse = tg.tg_decode_attn(q.to(DEV), kc.to(DEV), vc.to(DEV), bc.to(DEV),
+                                 None if gain is None else gain.to(DEV), tau,
+                                 torch.from_numpy(start).to(DEV), torch.tensor(lens, dtype=torch.int32, device=DEV),
+                                 max(lens), lse=torch.empty((B, Hq), device=DEV))
+    torch.cuda.synchronize()
+    w = _check_decode(out, lse, q, kc, vc, bc if with_bias else torch.zeros_like(bc), start, lens, gain, tau, dtype)
+    _note(f"  worst error / bar {w:.3f}")
+
+
 def test_decode_steps_from_prefill_cache():
     """The ragged workload's kept layout: the prefill's kept k, v and bias
     scattered into a cache with room per sequence, then 5 decode steps each
