@@ -51,7 +51,7 @@ def _compile(src: str, verbose: bool, build_dir: str, extra) -> str:
 def build_library(verbose: bool = False, extra_flags=(), out_path: str = LIB_PATH) -> str:
     """Compile every HIP source and link the shared library; returns its path.
 
-    ``extra_flags`` are passed to every compile (e.g. ``-DTG_ATTN_WAVES=4``);
+    ``extra_flags`` are passed to every compile (e.g. ``-g``);
     ``out_path`` places the library elsewhere (objects go next to it).
     """
     build_dir = BUILD_DIR if out_path == LIB_PATH else os.path.splitext(out_path)[0] + "_obj"

@@ -354,14 +354,8 @@ __global__ __launch_bounds__(kThreads) void sel_mark(const float* __restrict__ s
 // sub-bins (chosen by lane % 4), which spreads the atomics of equal digits
 // in one wave over four addresses; the pick adds them back.
 constexpr int kSub = 4;
-#ifndef TG_SEL_SINGLE_MAX
-#define TG_SEL_SINGLE_MAX (1 << 15)
-#endif
-constexpr int64_t kSingleMaxT = TG_SEL_SINGLE_MAX;
-#ifndef TG_SEL_SINGLE_PER
-#define TG_SEL_SINGLE_PER 16
-#endif
-constexpr int kSPer = TG_SEL_SINGLE_PER;  // keys per thread and round, all loads in flight
+constexpr int64_t kSingleMaxT = (int64_t)1 << 15;
+constexpr int kSPer = 16;  // keys per thread and round, all loads in flight
 
 __global__ __launch_bounds__(kThreads) void sel_single(const float* __restrict__ scores,
                                                        const int32_t* cu, const int32_t* db,
