@@ -51,63 +51,6 @@ constexpr int kBufFlags = 0x00020000;
 constexpr int KAHEAD = 2;  // k-steps of K fragments read ahead of their MFMAs
 constexpr int VAHEAD = 3;  // V fragments read ahead of their MFMAs
 
-// Work order of the bf16 kernels.  Grid slot (y, z) has rank r = y + B z
-// in dispatch order (the head index x runs fastest).  With one prompt, rank
-// r is query tile n_qt - 1 - r: longest first.  With several, the prompts'
-// query tiles do not all exist (a prompt has ceil(len / BQ) of them), and a
-// slot whose tile does not exist exits at once; spread through the dispatch
-// order, such slots were measured to hold back the dispatch of the real
-// ones (about 176 of 256 CUs busy on a ragged batch).  So rank r maps to the
-// r-th existing (prompt, tile) pair in the order tile index descending, then
-// prompt ascending (still longest first: a tile's work depends on its index
-// only), and the ranks past the last pair take the empty slots.  Every wave
-// computes the same mapping (no barrier): S(t), the number of pairs with tile
-// index >= t, is a sum over the prompts of max(0, n_b - t), and the pair's
-// tile index is the largest t with S(t) > r.
-__device__ __forceinline__ int tiles_of(const int32_t* cu, int b, int BQ) {
-  return (cu[b + 1] - cu[b] + BQ - 1) / BQ;
-}
-__device__ __forceinline__ long long wave_sum_ll(long long v) {
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off);
-  return v;
-}
-__device__ __forceinline__ void work_item(const int32_t* __restrict__ cu, int B, int n_qt, int BQ,
-                                          long long r, int lane, int& b_out, int& t_out) {
-  const int nb0 = lane < B ? tiles_of(cu, lane, BQ) : 0;  // the first 64 prompts, kept in a register
-  auto S = [&](int t) -> long long {
-    long long s = max(0, nb0 - t);
-    for (int b0 = 64; b0 < B; b0 += 64)
-      if (b0 + lane < B) s += max(0, tiles_of(cu, b0 + lane, BQ) - t);
-    return wave_sum_ll(s);
-  };
-  t_out = -1;
-  b_out = 0;
-  if (S(0) <= r) return;  // past the last pair
-  int lo = 0, hi = n_qt;   // S(lo) > r >= S(hi)
-  while (hi - lo > 1) {
-    const int mid = (lo + hi) >> 1;
-    if (S(mid) > r) lo = mid;
-    else hi = mid;
-  }
-  long long j = r - S(lo + 1);  // rank among the prompts that have tile lo
-  for (int b0 = 0; b0 < B; b0 += 64) {
-    const int bb = b0 + lane;
-    const int nb = b0 == 0 ? nb0 : (bb < B ? tiles_of(cu, bb, BQ) : 0);
-    const bool has = bb < B && nb > lo;
-    const unsigned long long m = __ballot(has);
-    const int c = __popcll(m);
-    if (j < c) {
-      const int below = __popcll(m & ((1ull << lane) - 1ull));
-      const unsigned long long hit = __ballot(has && below == (int)j);
-      b_out = b0 + __ffsll((long long)hit) - 1;
-      t_out = lo;
-      return;
-    }
-    j -= c;
-  }
-}
-
 template <int HD, int NW>
 __global__ __launch_bounds__(NW * 64, 1) void attn_bf16_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,

@@ -188,16 +188,24 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(
   __shared__ __align__(16) float sS[kT];  // g_h log2(e) s_j of the tile's keys
 
   const int h = blockIdx.x;
-  const int b = blockIdx.y;
-  const int tile = n_qt - 1 - (int)blockIdx.z;  // longest first
-  const int lo = cu[b];
-  const int n = cu[b + 1] - lo;
-  const int q0 = tile * 128;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int G = lane >> 5;
-  float* tp = tau_part + (((int64_t)h * gridDim.y + b) * n_qt + tile) * 4;
-  if (q0 >= n) {
+  // longest first; with several prompts the existing (prompt, tile) pairs
+  // come first in the dispatch order (work_item)
+  const long long rank = (long long)blockIdx.y + (long long)gridDim.y * blockIdx.z;
+  int b = 0, tile = n_qt - 1 - (int)blockIdx.z;
+  if (gridDim.y > 1) {
+    work_item(cu, (int)gridDim.y, n_qt, 128, rank, lane, b, tile);
+    b = __builtin_amdgcn_readfirstlane(b);
+    tile = __builtin_amdgcn_readfirstlane(tile);
+  }
+  // the temperature partials are indexed by the slot, summed in slot order
+  float* tp = tau_part + ((int64_t)h * gridDim.y * n_qt + rank) * 4;
+  const int lo = cu[b];
+  const int n = cu[b + 1] - lo;
+  const int q0 = tile * 128;
+  if (tile < 0 || q0 >= n) {
     if (tid < 4) tp[tid] = 0.0f;
     return;
   }
@@ -367,14 +375,26 @@ __global__ __launch_bounds__(256, 2) void bwd_dkdv_kernel(
 
   const int h = blockIdx.x;
   const int kvh = h / group;
-  const int b = blockIdx.y;
-  const int tile = blockIdx.z;  // the first key tiles see the most queries: launched first
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  // the first key tiles see the most queries: launched first.  Key tile t
+  // of a prompt with n_b tiles sees n_b - t query-tile steps, so with
+  // several prompts work_item's order (index descending) over u = n_b - 1 -
+  // t puts the existing pairs first, most work first.
+  int b = 0, tile = blockIdx.z;
+  if (gridDim.y > 1) {
+    int u = 0;
+    work_item(cu, (int)gridDim.y, (int)gridDim.z, 128, (long long)blockIdx.y + (long long)gridDim.y * blockIdx.z,
+              lane, b, u);
+    b = __builtin_amdgcn_readfirstlane(b);
+    u = __builtin_amdgcn_readfirstlane(u);
+    if (u < 0) return;
+    tile = tiles_of(cu, b, 128) - 1 - u;
+  }
   const int lo = cu[b];
   const int n = cu[b + 1] - lo;
   const int k0w = tile * 128;
   if (k0w >= n) return;
-  const int tid = threadIdx.x, lane = tid & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int G = lane >> 5;
   const int kw = k0w + 32 * wave;
   const int my_k = kw + (lane & 31);

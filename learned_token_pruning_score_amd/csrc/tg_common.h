@@ -20,6 +20,62 @@ __device__ __forceinline__ f32x16 mfma32x32x16(bf16x8 a, bf16x8 b, f32x16 c) {
 
 __device__ __forceinline__ bf16x8 as_bf16x8(uint4 u) { return __builtin_bit_cast(bf16x8, u); }
 
+// Work order of the tiled attention kernels with several prompts.  Their
+// grid has a slot (y, z) for every prompt and every tile index up to the
+// longest prompt's tile count, of rank r = y + B z in dispatch order (the
+// head index x runs fastest), but prompt b has only n_b = ceil(len_b / BQ)
+// tiles.  A slot whose tile does not exist exits at once; spread through the
+// dispatch order, such slots were measured to hold back the dispatch of the
+// real ones (about 176 of 256 CUs busy on a ragged batch).  So rank r takes
+// the r-th existing (prompt, index) pair in the order index descending, then
+// prompt ascending, and the ranks past the last pair take the empty slots.
+// Every wave computes the same mapping (no barrier): S(t), the number of
+// pairs with index >= t, is a sum over the prompts of max(0, n_b - t), and
+// the pair's index is the largest t with S(t) > r.
+__device__ __forceinline__ int tiles_of(const int32_t* cu, int b, int BQ) {
+  return (cu[b + 1] - cu[b] + BQ - 1) / BQ;
+}
+__device__ __forceinline__ long long wave_sum_ll(long long v) {
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off);
+  return v;
+}
+__device__ __forceinline__ void work_item(const int32_t* __restrict__ cu, int B, int n_qt, int BQ,
+                                          long long r, int lane, int& b_out, int& t_out) {
+  const int nb0 = lane < B ? tiles_of(cu, lane, BQ) : 0;  // the first 64 prompts, kept in a register
+  auto S = [&](int t) -> long long {
+    long long s = max(0, nb0 - t);
+    for (int b0 = 64; b0 < B; b0 += 64)
+      if (b0 + lane < B) s += max(0, tiles_of(cu, b0 + lane, BQ) - t);
+    return wave_sum_ll(s);
+  };
+  t_out = -1;
+  b_out = 0;
+  if (S(0) <= r) return;  // past the last pair
+  int lo = 0, hi = n_qt;   // S(lo) > r >= S(hi)
+  while (hi - lo > 1) {
+    const int mid = (lo + hi) >> 1;
+    if (S(mid) > r) lo = mid;
+    else hi = mid;
+  }
+  long long j = r - S(lo + 1);  // rank among the prompts that have tile lo
+  for (int b0 = 0; b0 < B; b0 += 64) {
+    const int bb = b0 + lane;
+    const int nb = b0 == 0 ? nb0 : (bb < B ? tiles_of(cu, bb, BQ) : 0);
+    const bool has = bb < B && nb > lo;
+    const unsigned long long m = __ballot(has);
+    const int c = __popcll(m);
+    if (j < c) {
+      const int below = __popcll(m & ((1ull << lane) - 1ull));
+      const unsigned long long hit = __ballot(has && below == (int)j);
+      b_out = b0 + __ffsll((long long)hit) - 1;
+      t_out = lo;
+      return;
+    }
+    j -= c;
+  }
+}
+
 // Row of the 32x32 accumulator that register i of lane l holds.
 __device__ __forceinline__ int acc_row(int i, int lane) {
   return 8 * (i >> 2) + 4 * (lane >> 5) + (i & 3);

@@ -1,5 +1,5 @@
 """CPU model of the attention kernels' work order with several prompts
-(``work_item`` in csrc/attn.hip), checked against a sort.
+(``work_item`` in csrc/tg_common.h), checked against a sort.
 
 A grid slot of rank r (dispatch order) takes the r-th existing (prompt,
 query tile) pair in the order tile index descending, then prompt ascending;
