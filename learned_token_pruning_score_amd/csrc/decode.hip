@@ -131,6 +131,20 @@ __global__ __launch_bounds__(256) void decode_split_kernel(
   const int sub = lane % LPK;       // its 8 elements: [8 sub, 8 sub + 8)
   const int n = lens[b];
   const int64_t base = start[b];
+  if ((int64_t)split * KS >= n) {
+    // no key of the sequence in this split (ragged caches): the empty
+    // partial (max -inf, sum 0, o 0), without the loads and the loop
+    for (int idx = tid; idx < G * HD; idx += 256) {
+      const int g = idx / HD, e = idx - g * HD;
+      const int64_t ph = ((int64_t)b * Hq + kvh * G + g) * n_split + split;
+      part_o[ph * HD + e] = 0.0f;
+      if (e == 0) {
+        part_m[ph] = -INFINITY;
+        part_l[ph] = 0.0f;
+      }
+    }
+    return;
+  }
   // queries of the group, pre-scaled to log2 units
   float qv[G][8], gb[G];
 #pragma unroll
