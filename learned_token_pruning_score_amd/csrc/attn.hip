@@ -51,6 +51,51 @@ constexpr int kBufFlags = 0x00020000;
 constexpr int KAHEAD = 2;  // k-steps of K fragments read ahead of their MFMAs
 constexpr int VAHEAD = 3;  // V fragments read ahead of their MFMAs
 
+// One output row (query row l % 32 of the wave) from the O^T accumulators:
+// register i of block db holds head dimension 32 db + 8 (i / 4) + 4 G + i % 4
+// (G = lane / 32).  The blocks DB_LO <= db < DB_HI are scaled by inv, rounded
+// to bf16 and stored at op (the row's first head dimension).  The two lane
+// halves first swap 4-dimension runs, so that each lane holds 8 consecutive
+// dimensions: every row's 32 dimensions of a block leave as two 16-byte
+// stores of one lane pair (half the store instructions of 8-byte stores,
+// and twice the bytes of a row in each).  Every lane takes part in the
+// swaps; only `store` lanes write.
+template <int NDB>
+__device__ __forceinline__ void store_o_row(const f32x16 (&o)[NDB], int db_lo, int db_hi, float inv, int G,
+                                            bool store, uint16_t* op) {
+  auto pack2 = [&](float a, float b) __attribute__((always_inline)) {
+    return (unsigned)__builtin_bit_cast(uint16_t, (__bf16)(a * inv)) |
+           ((unsigned)__builtin_bit_cast(uint16_t, (__bf16)(b * inv)) << 16);
+  };
+  uint4 w[NDB][2];
+#pragma unroll
+  for (int db = 0; db < NDB; ++db) {
+    if (db < db_lo || db >= db_hi) continue;
+#pragma unroll
+    for (int p = 0; p < 2; ++p) {
+      // a: dimensions 16 p + 4 G .. +3 (register run 2 p), b: 16 p + 8 + 4 G .. +3
+      unsigned a[2], b[2], x0[2], x1[2];
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        a[j] = pack2(o[db][8 * p + 2 * j], o[db][8 * p + 2 * j + 1]);
+        b[j] = pack2(o[db][8 * p + 4 + 2 * j], o[db][8 * p + 4 + 2 * j + 1]);
+        // lanes < 32 receive the upper half's a, lanes >= 32 the lower half's b
+        const auto r = __builtin_amdgcn_permlane32_swap(a[j], b[j], false, false);
+        x0[j] = r[0];
+        x1[j] = r[1];
+      }
+      w[db][p] = G == 0 ? make_uint4(a[0], a[1], x1[0], x1[1]) : make_uint4(x0[0], x0[1], b[0], b[1]);
+    }
+  }
+  if (!store) return;
+#pragma unroll
+  for (int db = 0; db < NDB; ++db) {
+    if (db < db_lo || db >= db_hi) continue;
+#pragma unroll
+    for (int p = 0; p < 2; ++p) *reinterpret_cast<uint4*>(op + 32 * db + 16 * p + 8 * G) = w[db][p];
+  }
+}
+
 template <int HD, int NW>
 __global__ __launch_bounds__(NW * 64, 1) void attn_bf16_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
@@ -413,26 +458,10 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_bf16_kernel(
 
   if (!wave_active) return;
   const float l_tot = pair_sum(l_run);
-  if (my_q < n) {
-    const float inv = 1.0f / l_tot;
-    uint16_t* op = out + (int64_t)(lo + my_q) * ((int64_t)Hq * HD) + (int64_t)h * HD;
-#pragma unroll
-    for (int db = 0; db < NDB; ++db)
-#pragma unroll
-      for (int g4 = 0; g4 < 4; ++g4) {
-        const int d0 = db * 32 + 8 * g4 + 4 * G;
-        unsigned w[2];
-#pragma unroll
-        for (int j = 0; j < 2; ++j) {
-          const __bf16 e0 = (__bf16)(o[db][4 * g4 + 2 * j] * inv);
-          const __bf16 e1 = (__bf16)(o[db][4 * g4 + 2 * j + 1] * inv);
-          w[j] = (unsigned)__builtin_bit_cast(uint16_t, e0) |
-                 ((unsigned)__builtin_bit_cast(uint16_t, e1) << 16);
-        }
-        *reinterpret_cast<uint2*>(op + d0) = make_uint2(w[0], w[1]);
-      }
-    if (lse != nullptr && G == 0) lse[(int64_t)h * Kt + lo + my_q] = (m_run * qk_scale + __log2f(l_tot)) * kLn2;
-  }
+  const int q_row = min(my_q, n - 1);  // rows past the prompt store nothing
+  store_o_row(o, 0, NDB, 1.0f / l_tot, G, my_q < n, out + (int64_t)(lo + q_row) * ((int64_t)Hq * HD) + (int64_t)h * HD);
+  if (lse != nullptr && G == 0 && my_q < n)
+    lse[(int64_t)h * Kt + lo + my_q] = (m_run * qk_scale + __log2f(l_tot)) * kLn2;
 }
 
 // Key-split schedule (short inputs, where the query tile that sees every
@@ -773,7 +802,8 @@ __global__ __launch_bounds__(512, 1) void attn_bf16_ks_kernel(
   }
 
   // Merge: the odd-tile wave of each pair hands its partial state to the
-  // even-tile wave through LDS (the stages are no longer read).
+  // even-tile wave through LDS (the stages are no longer read).  (Both waves
+  // merging and each storing half of the head dimensions measured slower.)
   float* mO = reinterpret_cast<float*>(smem);  // [pair][db][i][lane]
   float* mM = mO + 4 * NDB * 16 * 64;          // [pair][lane]
   float* mL = mM + 4 * 64;
@@ -798,26 +828,11 @@ __global__ __launch_bounds__(512, 1) void attn_bf16_ks_kernel(
     for (int i2 = 0; i2 < 16; ++i2)
       o[db][i2] = o[db][i2] * a0 + mO[((pair * NDB + db) * 16 + i2) * 64 + lane] * a1;
   const float l_tot = pair_sum(l_run * a0 + l1 * a1);
-  if (my_q < n) {
-    const float inv = 1.0f / l_tot;
-    uint16_t* op = out + (int64_t)(lo + my_q) * ((int64_t)Hq * HD) + (int64_t)h * HD;
-#pragma unroll
-    for (int db = 0; db < NDB; ++db)
-#pragma unroll
-      for (int g4 = 0; g4 < 4; ++g4) {
-        const int d0 = db * 32 + 8 * g4 + 4 * G;
-        unsigned w[2];
-#pragma unroll
-        for (int j = 0; j < 2; ++j) {
-          const __bf16 e0 = (__bf16)(o[db][4 * g4 + 2 * j] * inv);
-          const __bf16 e1 = (__bf16)(o[db][4 * g4 + 2 * j + 1] * inv);
-          w[j] = (unsigned)__builtin_bit_cast(uint16_t, e0) |
-                 ((unsigned)__builtin_bit_cast(uint16_t, e1) << 16);
-        }
-        *reinterpret_cast<uint2*>(op + d0) = make_uint2(w[0], w[1]);
-      }
-    if (lse != nullptr && G == 0) lse[(int64_t)h * Kt + lo + my_q] = (m_all * qk_scale + __log2f(l_tot)) * kLn2;
-  }
+  const int q_row = min(my_q, n - 1);  // rows past the prompt store nothing
+  store_o_row(o, 0, NDB, 1.0f / l_tot, G, my_q < n,
+              out + (int64_t)(lo + q_row) * ((int64_t)Hq * HD) + (int64_t)h * HD);
+  if (lse != nullptr && G == 0 && my_q < n)
+    lse[(int64_t)h * Kt + lo + my_q] = (m_all * qk_scale + __log2f(l_tot)) * kLn2;
 }
 
 template <int HD>
