@@ -51,49 +51,15 @@ constexpr int kBufFlags = 0x00020000;
 constexpr int KAHEAD = 2;  // k-steps of K fragments read ahead of their MFMAs
 constexpr int VAHEAD = 3;  // V fragments read ahead of their MFMAs
 
-// One output row (query row l % 32 of the wave) from the O^T accumulators:
-// register i of block db holds head dimension 32 db + 8 (i / 4) + 4 G + i % 4
-// (G = lane / 32).  The blocks DB_LO <= db < DB_HI are scaled by inv, rounded
-// to bf16 and stored at op (the row's first head dimension).  The two lane
-// halves first swap 4-dimension runs, so that each lane holds 8 consecutive
-// dimensions: every row's 32 dimensions of a block leave as two 16-byte
-// stores of one lane pair (half the store instructions of 8-byte stores,
-// and twice the bytes of a row in each).  Every lane takes part in the
-// swaps; only `store` lanes write.
+// One output row (query row l % 32 of the wave) from the O^T accumulators
+// (block db holds head dimensions 32 db ..), scaled by inv, rounded to bf16
+// and stored at op (the row's first head dimension) with 16-byte stores
+// (store_row32_bf16); only `store` lanes write.
 template <int NDB>
-__device__ __forceinline__ void store_o_row(const f32x16 (&o)[NDB], int db_lo, int db_hi, float inv, int G,
-                                            bool store, uint16_t* op) {
-  auto pack2 = [&](float a, float b) __attribute__((always_inline)) {
-    return (unsigned)__builtin_bit_cast(uint16_t, (__bf16)(a * inv)) |
-           ((unsigned)__builtin_bit_cast(uint16_t, (__bf16)(b * inv)) << 16);
-  };
-  uint4 w[NDB][2];
+__device__ __forceinline__ void store_o_row(const f32x16 (&o)[NDB], float inv, int G, bool store, uint16_t* op) {
 #pragma unroll
-  for (int db = 0; db < NDB; ++db) {
-    if (db < db_lo || db >= db_hi) continue;
-#pragma unroll
-    for (int p = 0; p < 2; ++p) {
-      // a: dimensions 16 p + 4 G .. +3 (register run 2 p), b: 16 p + 8 + 4 G .. +3
-      unsigned a[2], b[2], x0[2], x1[2];
-#pragma unroll
-      for (int j = 0; j < 2; ++j) {
-        a[j] = pack2(o[db][8 * p + 2 * j], o[db][8 * p + 2 * j + 1]);
-        b[j] = pack2(o[db][8 * p + 4 + 2 * j], o[db][8 * p + 4 + 2 * j + 1]);
-        // lanes < 32 receive the upper half's a, lanes >= 32 the lower half's b
-        const auto r = __builtin_amdgcn_permlane32_swap(a[j], b[j], false, false);
-        x0[j] = r[0];
-        x1[j] = r[1];
-      }
-      w[db][p] = G == 0 ? make_uint4(a[0], a[1], x1[0], x1[1]) : make_uint4(x0[0], x0[1], b[0], b[1]);
-    }
-  }
-  if (!store) return;
-#pragma unroll
-  for (int db = 0; db < NDB; ++db) {
-    if (db < db_lo || db >= db_hi) continue;
-#pragma unroll
-    for (int p = 0; p < 2; ++p) *reinterpret_cast<uint4*>(op + 32 * db + 16 * p + 8 * G) = w[db][p];
-  }
+  for (int db = 0; db < NDB; ++db)
+    store_row32_bf16(op + 32 * db, G, store, [&](int i) __attribute__((always_inline)) { return o[db][i] * inv; });
 }
 
 template <int HD, int NW>
@@ -459,7 +425,7 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_bf16_kernel(
   if (!wave_active) return;
   const float l_tot = pair_sum(l_run);
   const int q_row = min(my_q, n - 1);  // rows past the prompt store nothing
-  store_o_row(o, 0, NDB, 1.0f / l_tot, G, my_q < n, out + (int64_t)(lo + q_row) * ((int64_t)Hq * HD) + (int64_t)h * HD);
+  store_o_row(o, 1.0f / l_tot, G, my_q < n, out + (int64_t)(lo + q_row) * ((int64_t)Hq * HD) + (int64_t)h * HD);
   if (lse != nullptr && G == 0 && my_q < n)
     lse[(int64_t)h * Kt + lo + my_q] = (m_run * qk_scale + __log2f(l_tot)) * kLn2;
 }
@@ -829,7 +795,7 @@ __global__ __launch_bounds__(512, 1) void attn_bf16_ks_kernel(
       o[db][i2] = o[db][i2] * a0 + mO[((pair * NDB + db) * 16 + i2) * 64 + lane] * a1;
   const float l_tot = pair_sum(l_run * a0 + l1 * a1);
   const int q_row = min(my_q, n - 1);  // rows past the prompt store nothing
-  store_o_row(o, 0, NDB, 1.0f / l_tot, G, my_q < n,
+  store_o_row(o, 1.0f / l_tot, G, my_q < n,
               out + (int64_t)(lo + q_row) * ((int64_t)Hq * HD) + (int64_t)h * HD);
   if (lse != nullptr && G == 0 && my_q < n)
     lse[(int64_t)h * Kt + lo + my_q] = (m_all * qk_scale + __log2f(l_tot)) * kLn2;

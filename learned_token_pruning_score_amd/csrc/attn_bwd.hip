@@ -107,19 +107,10 @@ __device__ __forceinline__ void to_b_operand(const float (&v)[2][16], bf16x8 (&p
       for (int j = 0; j < 8; ++j) pb[kb][hh][j] = (__bf16)v[kb][8 * hh + j];
 }
 
-__device__ __forceinline__ void store_bf16_rows(uint16_t* p, const f32x16& a, float mul, int G) {
-#pragma unroll
-  for (int g4 = 0; g4 < 4; ++g4) {
-    const int e0 = 8 * g4 + 4 * G;
-    unsigned w[2];
-#pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      const __bf16 x0 = (__bf16)(a[4 * g4 + 2 * j] * mul);
-      const __bf16 x1 = (__bf16)(a[4 * g4 + 2 * j + 1] * mul);
-      w[j] = (unsigned)__builtin_bit_cast(uint16_t, x0) | ((unsigned)__builtin_bit_cast(uint16_t, x1) << 16);
-    }
-    *reinterpret_cast<uint2*>(p + e0) = make_uint2(w[0], w[1]);
-  }
+// One row's 32 columns of an accumulator block, scaled by mul, as bf16 at p
+// (16-byte stores, store_row32_bf16); only `store` lanes write.
+__device__ __forceinline__ void store_bf16_rows(uint16_t* p, const f32x16& a, float mul, int G, bool store) {
+  store_row32_bf16(p, G, store, [&](int i) __attribute__((always_inline)) { return a[i] * mul; });
 }
 
 // Fixed-order wave sum (butterfly over the 64 lanes).
@@ -337,11 +328,10 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(
   }
   const float tw = wave_sum(tsum);
   if (lane == 0) tp[wave] = tw;
-  if (!q_ok) return;
   const float scale = tau * rsqrtf((float)HD);
-  uint16_t* dp_out = dq + ((int64_t)(lo + my_q) * Hq + h) * HD;
+  uint16_t* dp_out = dq + ((int64_t)(lo + min(my_q, n - 1)) * Hq + h) * HD;  // rows past the prompt store nothing
 #pragma unroll
-  for (int db = 0; db < NDB; ++db) store_bf16_rows(dp_out + 32 * db, acc[db], scale, G);
+  for (int db = 0; db < NDB; ++db) store_bf16_rows(dp_out + 32 * db, acc[db], scale, G, q_ok);
 }
 
 // ----------------------------------------------------------------- dk, dv
@@ -548,8 +538,8 @@ __global__ __launch_bounds__(256, 2) void bwd_dkdv_kernel(
     const float c = pair_sum(csum);
     if (k_ok && G == 0) colsum[(int64_t)h * Kt + lo + my_k] = c;
   }
-  if (!k_ok) return;
   if (part) {
+    if (!k_ok) return;
     float* pp = part + ((int64_t)h * Kt + lo + my_k) * HD;
 #pragma unroll
     for (int db = 0; db < NDB; ++db)
@@ -560,9 +550,9 @@ __global__ __launch_bounds__(256, 2) void bwd_dkdv_kernel(
     return;
   }
   const float scale = DK ? tau * rsqrtf((float)HD) : 1.0f;
-  uint16_t* op = dkv + ((int64_t)(lo + my_k) * Hkv + kvh) * HD;
+  uint16_t* op = dkv + ((int64_t)(lo + min(my_k, n - 1)) * Hkv + kvh) * HD;  // rows past the prompt store nothing
 #pragma unroll
-  for (int db = 0; db < NDB; ++db) store_bf16_rows(op + 32 * db, acc[db], scale, G);
+  for (int db = 0; db < NDB; ++db) store_bf16_rows(op + 32 * db, acc[db], scale, G, k_ok);
 }
 
 // out[r][kvh][e] = bf16(mul * sum_(hh < group) part[kvh group + hh][r][e]),

@@ -160,22 +160,21 @@ __device__ __forceinline__ void finish_pair(const ProjArgs& g, f32x16& a, f32x16
       }
     }
   }
-  if (t >= g.M) return;
+  // rows past M store nothing (the lanes of a row pair share t)
+  const bool ok = t < g.M;
+  const int64_t tr = ok ? t : 0;
+  const int G = lane >> 5;
   if (EPI == kEpiSwiglu) {
-    uint16_t* orow = g.out + t * g.ld_out + colA + hf;
-#pragma unroll
-    for (int i4 = 0; i4 < 4; ++i4)
-      *reinterpret_cast<uint2*>(orow + 8 * i4) =
-          pack_bf16x4(silu(a[4 * i4]) * b[4 * i4], silu(a[4 * i4 + 1]) * b[4 * i4 + 1],
-                      silu(a[4 * i4 + 2]) * b[4 * i4 + 2], silu(a[4 * i4 + 3]) * b[4 * i4 + 3]);
+    store_row32_bf16(g.out + tr * g.ld_out + colA, G, ok,
+                     [&](int i) __attribute__((always_inline)) { return silu(a[i]) * b[i]; });
     return;
   }
 #pragma unroll
   for (int s = 0; s < 2; ++s) {
     f32x16& v = s ? b : a;
-    const int col = (s ? colB : colA) + hf;
-    if (EPI == kEpiResid) {
-      const uint16_t* rrow = g.res + t * g.ld_res + col;
+    const int col = s ? colB : colA;
+    if (EPI == kEpiResid && ok) {
+      const uint16_t* rrow = g.res + t * g.ld_res + col + hf;
 #pragma unroll
       for (int i4 = 0; i4 < 4; ++i4) {
         const uint2 r = *reinterpret_cast<const uint2*>(rrow + 8 * i4);
@@ -185,10 +184,7 @@ __device__ __forceinline__ void finish_pair(const ProjArgs& g, f32x16& a, f32x16
         v[4 * i4 + 3] += bf16_hi(r.y);
       }
     }
-    uint16_t* orow = g.out + t * g.ld_out + col;
-#pragma unroll
-    for (int i4 = 0; i4 < 4; ++i4)
-      *reinterpret_cast<uint2*>(orow + 8 * i4) = pack_bf16x4(v[4 * i4], v[4 * i4 + 1], v[4 * i4 + 2], v[4 * i4 + 3]);
+    store_row32_bf16(g.out + tr * g.ld_out + col, G, ok, [&](int i) __attribute__((always_inline)) { return v[i]; });
   }
 }
 

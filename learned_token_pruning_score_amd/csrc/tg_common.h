@@ -20,6 +20,42 @@ __device__ __forceinline__ f32x16 mfma32x32x16(bf16x8 a, bf16x8 b, f32x16 c) {
 
 __device__ __forceinline__ bf16x8 as_bf16x8(uint4 u) { return __builtin_bit_cast(bf16x8, u); }
 
+// One row of a 32x32 accumulator block rounded to bf16 and stored at p[0..31]:
+// lane l holds row l % 32 and, in register i, column 8 (i / 4) + 4 G + i % 4
+// (G = l / 32); val(i) is the fp32 value of register i.  The two lane halves
+// first swap 4-column runs (v_permlane32_swap), so that each lane holds 8
+// consecutive columns and the row leaves in two 16-byte stores of one lane
+// pair: half the store instructions of 8-byte stores, each carrying twice
+// the bytes of a row (store instructions that touch 32 rows were measured
+// to cost kernel time).  Every lane takes part in the swaps; only `store`
+// lanes write.
+template <typename Val>
+__device__ __forceinline__ void store_row32_bf16(uint16_t* p, int G, bool store, Val val) {
+  auto pack2 = [&](int i) __attribute__((always_inline)) {
+    return (unsigned)__builtin_bit_cast(uint16_t, (__bf16)val(i)) |
+           ((unsigned)__builtin_bit_cast(uint16_t, (__bf16)val(i + 1)) << 16);
+  };
+  uint4 w[2];
+#pragma unroll
+  for (int pp = 0; pp < 2; ++pp) {
+    // u: columns 16 pp + 4 G .. +3 (registers 8 pp ..), v: 16 pp + 8 + 4 G .. +3
+    unsigned u[2], v[2], x0[2], x1[2];
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      u[j] = pack2(8 * pp + 2 * j);
+      v[j] = pack2(8 * pp + 4 + 2 * j);
+      // lanes < 32 receive the upper half's u, lanes >= 32 the lower half's v
+      const auto r = __builtin_amdgcn_permlane32_swap(u[j], v[j], false, false);
+      x0[j] = r[0];
+      x1[j] = r[1];
+    }
+    w[pp] = G == 0 ? make_uint4(u[0], u[1], x1[0], x1[1]) : make_uint4(x0[0], x0[1], v[0], v[1]);
+  }
+  if (!store) return;
+#pragma unroll
+  for (int pp = 0; pp < 2; ++pp) *reinterpret_cast<uint4*>(p + 16 * pp + 8 * G) = w[pp];
+}
+
 // Work order of the tiled attention kernels with several prompts.  Their
 // grid has a slot (y, z) for every prompt and every tile index up to the
 // longest prompt's tile count, of rank r = y + B z in dispatch order (the
