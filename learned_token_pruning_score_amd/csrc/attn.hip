@@ -164,9 +164,9 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_bf16_kernel(
     const int id = gtid + j * (NT / 2);
     h_off[j] = ((id / KCH) * (int)(grp == 0 ? ks : vs) + (id % KCH) * 8) * 2;
   }
-  uint4 hreg[HALF_T];
-  float breg = 0.0f;
-  auto prefetch_half = [&](int k0) __attribute__((always_inline)) {
+  uint4 hreg[HALF_T], hreg1[HALF_T];
+  float breg = 0.0f, breg1 = 0.0f;
+  auto load_into = [&](int k0, uint4 (&hr)[HALF_T], float& br) __attribute__((always_inline)) {
     // wave-uniform (kept in scalar registers, so the descriptors are too)
     const int rows = __builtin_amdgcn_readfirstlane(max(min(n - k0, kBK), 0));
     const uint16_t* base = grp == 0 ? kbase + (int64_t)k0 * ks : vbase + (int64_t)k0 * vs;
@@ -175,22 +175,24 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_bf16_kernel(
         (void*)base, (short)0, rows * stride * 2, kBufFlags);
 #pragma unroll
     for (int j = 0; j < HALF_T; ++j)
-      hreg[j] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, h_off[j], 0, 0));
+      hr[j] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, h_off[j], 0, 0));
     if (grp == 0 && bias_p != nullptr) {
       const __amdgpu_buffer_rsrc_t rb = __builtin_amdgcn_make_buffer_rsrc(
           (void*)(bias_p + k0), (short)0, rows * 4, kBufFlags);
-      breg = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rb, (gtid & (kBK - 1)) * 4, 0, 0));
+      br = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rb, (gtid & (kBK - 1)) * 4, 0, 0));
     }
   };
-  auto stage_half = [&](int buf) __attribute__((always_inline)) {
+  auto prefetch_half = [&](int k0) __attribute__((always_inline)) { load_into(k0, hreg, breg); };
+  auto stage_from = [&](int buf, const uint4 (&hr)[HALF_T], float br) __attribute__((always_inline)) {
 #pragma unroll
     for (int j = 0; j < HALF_T; ++j) {
       const int id = gtid + j * (NT / 2);
-      if (grp == 0) sK[buf][(id / KCH) * KROW + (id % KCH)] = hreg[j];
-      else sV[buf][(id / KCH) * VROW + (id % KCH)] = hreg[j];
+      if (grp == 0) sK[buf][(id / KCH) * KROW + (id % KCH)] = hr[j];
+      else sV[buf][(id / KCH) * VROW + (id % KCH)] = hr[j];
     }
-    if (grp == 0 && gtid < kBK) sB[buf][gtid] = has_bias ? breg * cmul : 0.0f;
+    if (grp == 0 && gtid < kBK) sB[buf][gtid] = has_bias ? br * cmul : 0.0f;
   };
+  auto stage_half = [&](int buf) __attribute__((always_inline)) { stage_from(buf, hreg, breg); };
 
   // Scores S^T = K Q^T + bias of one tile into s, two interleaved MFMA
   // chains; the K fragments are read KAHEAD k-steps ahead.
@@ -351,16 +353,21 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_bf16_kernel(
     stage_half(buf_of(t));
     prefetch_half((t + 1) * kBK);
   };
+  // tile 1, loaded with tile 0 into registers of its own
+  auto stage_first = [&]() __attribute__((always_inline)) {
+    stage_from(buf_of(1), hreg1, breg1);
+    prefetch_half(2 * kBK);
+  };
   prefetch_half(0);
+  load_into(kBK, hreg1, breg1);
   stage_half(0);
-  prefetch_half(kBK);
   __syncthreads();
   int t = 0;
   if (grp == 0) {
     if (t_diag >= 0) {
       qk(0);
       __syncthreads();
-      stage_next(1);
+      stage_first();
       if (t_diag == 0) softmax(0, std::true_type{});
       else softmax(0, std::false_type{});
       __syncthreads();
@@ -390,12 +397,13 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_bf16_kernel(
     }
     for (; t < n_loop; ++t) {
       __syncthreads();
-      stage_next(t + 1);
+      if (t == 0) stage_first();
+      else stage_next(t + 1);
       __syncthreads();
     }
   } else {
     if (t_diag >= 0) {
-      stage_next(1);
+      stage_first();
       __syncthreads();
       qk(0);
       __syncthreads();
@@ -416,7 +424,8 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_bf16_kernel(
       ++t;
     }
     for (; t < n_loop; ++t) {
-      stage_next(t + 1);
+      if (t == 0) stage_first();
+      else stage_next(t + 1);
       __syncthreads();
       __syncthreads();
     }
