@@ -289,6 +289,19 @@ def reference_points(tg, w, gp, layers, outs, hidden, W1, b1, w2, stream, dev):
     return r
 
 
+def attn_kernel_name(dtype, Hq, d, Kt, n_cu):
+    """The attention kernel a launch of this shape runs (the library's rule:
+    fp32 on the vector-ALU path; bf16 on the key-split kernel when the
+    256-row query tiles number fewer than twice the CUs, else the 256-row
+    kernel)."""
+    import torch
+    if dtype == torch.float32:
+        return f"attn_f32_kernel<{d}>"
+    if Hq * ((Kt + 255) // 256) < 2 * n_cu:
+        return f"attn_bf16_ks_kernel<{d}>"
+    return f"attn_bf16_kernel<{d}, 8>"
+
+
 def cpu_baseline(w, q_layers, cu_kept, Kt):
     """The fp64 oracle on a bounded sample of the same workload, scaled to the
     whole step: gate, top-K and compaction on all tokens; attention for one
@@ -495,11 +508,11 @@ def main():
         }
         achieved = work["attn_flop_per_layer"] / (attn_avg / 1e3) / 1e12
         traffic = None
+        kname = attn_kernel_name(w.dtype, s.Hq, s.d, Kt, torch.cuda.get_device_properties(0).multi_processor_count)
         if s.name == "qwen3_1p7b_128k":
             traffic = measured_traffic(
-                "attn_bf16_kernel<128, 8>",
-                os.path.join(ROOT, "learned_token_pruning_score_amd", "csrc", "attn.hip"))
-        roof = {"bound": "mfma", "kernel": "attn_bf16_kernel<128, 8>",
+                kname, os.path.join(ROOT, "learned_token_pruning_score_amd", "csrc", "attn.hip"))
+        roof = {"bound": "mfma", "kernel": kname,
                 "achieved": achieved, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                 "frac": achieved / PEAK_BF16_TFLOPS, "traffic": traffic,
                 "traffic_unit": "HBM bytes per launch (FETCH_SIZE + WRITE_SIZE, copy-calibrated)",
