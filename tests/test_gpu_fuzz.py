@@ -27,7 +27,7 @@ pytestmark = pytest.mark.gpu
 DEV = "cuda"
 ATTN_TOL = {torch.bfloat16: 2e-2, torch.float32: 1e-4}
 LSE_TOL = {torch.bfloat16: 1e-3, torch.float32: 1e-4}
-N_CASES = 40
+N_CASES = 120
 
 
 def _f64(t):
