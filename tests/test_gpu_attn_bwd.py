@@ -212,6 +212,24 @@ def test_attn_bwd_random(seed):
     _check_all(cu, q, k, v, dout, bias, gain, tau, grads, out_st, dtype)
 
 
+def test_attn_bwd_many_prompts():
+    """100 prompts (three empty): the query- and key-parallel passes map
+    their slots over the prompts 64 at a time, so the second group is
+    exercised; every gradient element is checked."""
+    rng = np.random.default_rng(99)
+    lens = [int(x) for x in rng.integers(0, 200, 100)]
+    lens[0] = lens[64] = lens[99] = 0
+    lens[80] = 300
+    _note(f"[attn bwd many] {len(lens)} prompts, {sum(lens)} rows")
+    cu, q, k, v, dout, bias, gain = _inputs(lens, 4, 2, 64, torch.bfloat16, seed=77, with_bias=True)
+    tau = 0.9
+    o, lse = oracle.gated_attention(_f64(q), _f64(k), _f64(v), _f64(bias), _f64(gain), tau, cu)
+    out_st = torch.from_numpy(np.nan_to_num(o)).to(torch.bfloat16)
+    lse_st = torch.from_numpy(np.nan_to_num(lse)).to(torch.float32)
+    grads = _run_stored(cu, q, k, v, dout, bias, gain, tau, out_st, lse_st)
+    _check_all(cu, q, k, v, dout, bias, gain, tau, grads, out_st, torch.bfloat16)
+
+
 def test_attn_bwd_full_size_128k():
     """The 128k workload's kept rows (one prompt of 8448 rows), 16 heads."""
     name = "qwen3_1p7b_128k"

@@ -411,6 +411,24 @@ def test_attention_ragged_edges_long_batch(d, Hq, Hkv, long_len):
                     None if gg is None else gg.astype(np.float64), tau, cu, torch.bfloat16, rows)
 
 
+# More prompts than one wave's lanes (100): the 256-row kernel's dispatch
+# order counts each tile index's prompts 64 at a time (a ballot per group of
+# 64 prompts), so the second group and its empty prompts are exercised here;
+# every row is checked.
+def test_attention_many_prompts():
+    rng = np.random.default_rng(4242)
+    lens = [int(x) for x in rng.integers(0, 260, 100)]
+    lens[3] = lens[64] = lens[99] = 0
+    lens[70] = 511
+    cu, q, k, v, bias, gain = _attn_inputs(rng, lens, 16, 8, 128, torch.bfloat16)
+    assert 16 * ((int(cu[-1]) + 255) // 256) >= 512  # the 256-row kernel, not the key-split one
+    cud = torch.from_numpy(cu).to(DEV)
+    o, lse = tg.tg_gated_attn_fwd(q.to(DEV), k.to(DEV), v.to(DEV), torch.from_numpy(bias).to(DEV),
+                                  torch.from_numpy(gain).to(DEV), 1.15, cud, max(lens), want_lse=True)
+    torch.cuda.synchronize()
+    _attn_check(o.cpu(), lse.cpu(), q, k, v, bias, gain.astype(np.float64), 1.15, cu, torch.bfloat16, None)
+
+
 def test_attention_properties_on_gpu():
     rng = np.random.default_rng(5)
     lens = [700, 1, 1500]
