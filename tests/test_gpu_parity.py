@@ -411,17 +411,19 @@ def test_attention_ragged_edges_long_batch(d, Hq, Hkv, long_len):
                     None if gg is None else gg.astype(np.float64), tau, cu, torch.bfloat16, rows)
 
 
-# More prompts than one wave's lanes (100): the 256-row kernel's dispatch
-# order counts each tile index's prompts 64 at a time (a ballot per group of
-# 64 prompts), so the second group and its empty prompts are exercised here;
-# every row is checked.
-def test_attention_many_prompts():
-    rng = np.random.default_rng(4242)
-    lens = [int(x) for x in rng.integers(0, 260, 100)]
+# More prompts than one wave's lanes (100): both bf16 kernels' dispatch order
+# counts each tile index's prompts 64 at a time (a ballot per group of 64
+# prompts), so the second group and its empty prompts are exercised here, on
+# the 256-row kernel (longer prompts) and on the key-split one (short
+# prompts); every row is checked.
+@pytest.mark.parametrize("max_len,big", [(260, True), (40, False)])
+def test_attention_many_prompts(max_len, big):
+    rng = np.random.default_rng(4242 + max_len)
+    lens = [int(x) for x in rng.integers(0, max_len, 100)]
     lens[3] = lens[64] = lens[99] = 0
-    lens[70] = 511
+    lens[70] = 2 * max_len - 9
     cu, q, k, v, bias, gain = _attn_inputs(rng, lens, 16, 8, 128, torch.bfloat16)
-    assert 16 * ((int(cu[-1]) + 255) // 256) >= 512  # the 256-row kernel, not the key-split one
+    assert (16 * ((int(cu[-1]) + 255) // 256) >= 512) == big  # which kernel runs
     cud = torch.from_numpy(cu).to(DEV)
     o, lse = tg.tg_gated_attn_fwd(q.to(DEV), k.to(DEV), v.to(DEV), torch.from_numpy(bias).to(DEV),
                                   torch.from_numpy(gain).to(DEV), 1.15, cud, max(lens), want_lse=True)
