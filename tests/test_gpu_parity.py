@@ -431,6 +431,36 @@ def test_attention_many_prompts(max_len, big):
     _attn_check(o.cpu(), lse.cpu(), q, k, v, bias, gain.astype(np.float64), 1.15, cu, torch.bfloat16, None)
 
 
+# Seeded random large batches (1-12 prompts up to 12000 rows, GQA shapes,
+# d 64/128, bf16): mostly the 256-row kernel; every prompt's first and last
+# 40 rows, each 256-row tile's first and last row and 300 random rows.
+@pytest.mark.parametrize("seed", range(8))
+def test_attention_large_random(seed):
+    rng = np.random.default_rng(31000 + seed)
+    Hq, Hkv = [(16, 8), (8, 1), (32, 8), (12, 4)][int(rng.integers(0, 4))]
+    d = int(rng.choice([64, 128]))
+    B = int(rng.integers(1, 13))
+    lens = [int(x) for x in rng.integers(0, 12001, B)]
+    if sum(lens) < 256:
+        lens[0] = 5000
+    print(f"[attn large {seed}] heads {Hq}/{Hkv} d={d} lens {lens}", flush=True)
+    cu, q, k, v, bias, gain = _attn_inputs(rng, lens, Hq, Hkv, d, torch.bfloat16)
+    Kt = int(cu[-1])
+    rows = [rng.integers(0, Kt, 300)]
+    for b in range(B):
+        lo, hi = int(cu[b]), int(cu[b + 1])
+        if hi > lo:
+            t0 = np.arange(lo, hi, 256)
+            rows += [np.arange(lo, min(hi, lo + 40)), np.arange(max(lo, hi - 40), hi), t0, np.minimum(t0 + 255, hi - 1)]
+    rows = np.unique(np.concatenate(rows))
+    tau = float(rng.uniform(0.6, 1.6))
+    o, lse = tg.tg_gated_attn_fwd(q.to(DEV), k.to(DEV), v.to(DEV), torch.from_numpy(bias).to(DEV),
+                                  torch.from_numpy(gain).to(DEV), tau, torch.from_numpy(cu).to(DEV), max(lens),
+                                  want_lse=True)
+    torch.cuda.synchronize()
+    _attn_check(o.cpu(), lse.cpu(), q, k, v, bias, gain.astype(np.float64), tau, cu, torch.bfloat16, rows)
+
+
 def test_attention_properties_on_gpu():
     rng = np.random.default_rng(5)
     lens = [700, 1, 1500]
