@@ -140,6 +140,9 @@ def reference_points(tg, w, gp, layers, outs, hidden, W1, b1, w2, stream, dev):
         gate MLP's backward from the kept rows' bias gradient;
       * one decode step over the kept rows as a kept-only KV cache (one new
         query per prompt), with the bytes of cached keys and values it reads;
+      * one GPU's share of an 8-way split (KV heads a multiple of 8): the
+        gate on an eighth of the tokens and the attention of an eighth of the
+        KV heads (with their query heads) over all the kept rows;
       * what the chip reaches here on plain library work: a bf16 GEMM of
         8192^3 and a 1 GiB device copy."""
     import torch
@@ -245,6 +248,28 @@ def reference_points(tg, w, gp, layers, outs, hidden, W1, b1, w2, stream, dev):
     r["gate_bwd_us"] = t * 1e3
     r["gate_bwd_TFLOPs"] = 6.0 * Kt * s.D * s.F / (t / 1e3) / 1e12
     del dbias, wsg
+
+    # one GPU's share of an 8-way split of the step: the gate on an eighth of
+    # the tokens (rows shard with no exchange) and the attention of an eighth
+    # of the KV heads (heads shard with no exchange once the kept rows are
+    # gathered)
+    if s.Hkv % 8 == 0:
+        grp = s.Hq // s.Hkv * (s.Hkv // 8)  # the query heads of one GPU's KV heads
+        kv8 = s.Hkv // 8
+        T8 = w.T // 8
+        gate8 = lambda: tg.tg_gate_score(hidden[:T8], W1, b1, w2, w.b2, scores=gp.scores[:T8])  # noqa: E731
+        gate8()
+        t = time_launches(gate8, stream, reps=5, n=5)
+        r["shard8_gate_us"] = t * 1e3
+        r["shard8_gate_GBps"] = (T8 * s.D * hidden.element_size() + 4 * T8) / (t / 1e3) / 1e9
+        o1 = torch.empty((gp.Kt, grp, s.d), dtype=q.dtype, device=dev)
+        attn1 = lambda: tg.tg_gated_attn_fwd(q[:, :grp], k[:, :kv8], v[:, :kv8], gp.bias_s, gain[:grp], s.tau,  # noqa: E731
+                                             gp.cu_kept, gp.max_kept_len, out=o1)
+        attn1()
+        t = time_launches(attn1, stream, reps=5, n=5)
+        r["shard8_attn_us"] = t * 1e3
+        r["shard8_attn_TFLOPs"] = work["attn_flop_per_layer"] / 8 / (t / 1e3) / 1e12
+        del o1
 
     flush_buf = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
     flush = lambda: flush_buf.fill_(1)  # noqa: E731
