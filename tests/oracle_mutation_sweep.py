@@ -64,6 +64,20 @@ MUTS = [
  ("            x = scale * (K[lo:lo + n, kv] @ Q[b, h]) + g[h] * s[lo:lo + n]", "            x = scale * (K[lo:lo + n, kv] @ Q[b, h])"),
  ("            lse[b, h] = m + math.log(e.sum())", "            lse[b, h] = math.log(e.sum())"),
  ("        lo, n = int(start[b]), int(lens[b])\n        if n == 0:\n            continue\n        for h in range(Hq):\n            kv = h // group\n            x = scale * (K[lo:lo + n, kv]", "        lo, n = int(start[b]), int(lens[b]) - 1\n        if n <= 0:\n            continue\n        for h in range(Hq):\n            kv = h // group\n            x = scale * (K[lo:lo + n, kv]"),
+ # more selection / compaction
+ ("        keep[lo:hi] = 1\n", ""),
+ ("    kept_idx = np.nonzero(keep)[0].astype(np.int64)", "    kept_idx = np.nonzero(keep)[0].astype(np.int64)[::-1]"),
+ ("    hidden_k = np.asarray(hidden)[kept_idx]", "    hidden_k = np.asarray(hidden)[kept_idx - 1]"),
+ # more layer
+ ("    v = y[:, (Hq + Hkv) * d:].reshape(n, Hkv, d)", "    v = y[:, Hq * d:(Hq + Hkv) * d].reshape(n, Hkv, d)"),
+ ("    return apply_rope(q, pos, theta), apply_rope(k, pos, theta), v", "    return apply_rope(q, np.arange(n), theta), apply_rope(k, np.arange(n), theta), v"),
+ ("    o, _ = gated_attention(q, k, v, bias, gain, tau, cu_kept, rows=rows)", "    o, _ = gated_attention(q, k, v, None, None, tau, cu_kept, rows=rows)"),
+ # more backward
+ ("            dq[lo:hi, h] = scale * (dx @ Kh)", "            dq[lo:hi, h] = dx @ Kh"),
+ ("        visible = np.arange(n)[None, :] <= np.arange(n)[:, None]\n        sb = s[lo:hi]", "        visible = np.arange(n)[None, :] < np.arange(n)[:, None] + (np.arange(n)[:, None] == 0)\n        sb = s[lo:hi]"),
+ # more decode
+ ("            kv = h // group\n            x = scale * (K[lo:lo + n, kv] @ Q[b, h])", "            kv = h % K.shape[1]\n            x = scale * (K[lo:lo + n, kv] @ Q[b, h])"),
+ ("            o[b, h] = e @ V[lo:lo + n, kv] / e.sum()", "            o[b, h] = e @ V[lo:lo + n, kv] / n"),
  # sampling
  ("    return np.floor(f * (de - db)).astype(np.int64)", "    return np.rint(f * (de - db)).astype(np.int64)"),
  ("    f = float(min_frac) + (float(max_frac) - float(min_frac)) * uu", "    f = float(min_frac) + float(max_frac) * uu"),
