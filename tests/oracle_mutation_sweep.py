@@ -78,6 +78,18 @@ MUTS = [
  # more decode
  ("            kv = h // group\n            x = scale * (K[lo:lo + n, kv] @ Q[b, h])", "            kv = h % K.shape[1]\n            x = scale * (K[lo:lo + n, kv] @ Q[b, h])"),
  ("            o[b, h] = e @ V[lo:lo + n, kv] / e.sum()", "            o[b, h] = e @ V[lo:lo + n, kv] / n"),
+ # backward, column form and dq rows
+ ("            dk[n, kv] += scale * (dx @ Qi)", "            dk[n, kv] += dx @ Qi"),
+ ("            dv[n, kv] += P @ dOi", "            dv[n, kv] += dx @ dOi"),
+ ("            P = np.exp(x - L[h, j:hi])", "            P = np.exp(x - L[h, j])"),
+ ("                ds[n] += g[h] * float(dx.sum())", "                ds[n] += float(dx.sum())"),
+ ("            Qi, dOi = Q[j:hi, h], dO[j:hi, h]", "            Qi, dOi = Q[j + 1:hi, h], dO[j + 1:hi, h]"),
+ ("            dq[i, h] = scale * (dx @ Kh)", "            dq[i, h] = scale * (dx @ Vh)"),
+ ("            Kh, Vh = K[lo:i + 1, kv], V[lo:i + 1, kv]", "            Kh, Vh = K[lo:i, kv], V[lo:i, kv]"),
+ # gate backward
+ ("    return da @ W, da.T @ H, da.sum(axis=0), z.T @ g, float(g.sum())", "    return da @ (2.0 * W), da.T @ H, da.sum(axis=0), z.T @ g, float(g.sum())"),
+ ("    return da @ W, da.T @ H, da.sum(axis=0), z.T @ g, float(g.sum())", "    return da @ W, da.T @ H, da.sum(axis=0), z.T @ g, float(g.sum()) + 1.0"),
+ ("    a = H @ W.T\n    if b1 is not None:\n        a = a + _f64(b1)[None, :]\n    sig", "    a = H @ W.T\n    sig"),
  # sampling
  ("    return np.floor(f * (de - db)).astype(np.int64)", "    return np.rint(f * (de - db)).astype(np.int64)"),
  ("    f = float(min_frac) + (float(max_frac) - float(min_frac)) * uu", "    f = float(min_frac) + float(max_frac) * uu"),
