@@ -139,7 +139,8 @@ def reference_points(tg, w, gp, layers, outs, hidden, W1, b1, w2, stream, dev):
         gain and temperature gradients) on the step's kept rows, and the
         gate MLP's backward from the kept rows' bias gradient;
       * one decode step over the kept rows as a kept-only KV cache (one new
-        query per prompt), with the bytes of cached keys and values it reads;
+        query per prompt), with the bytes of cached keys and values it reads,
+        and the scatter of the kept k, v and bias into such a cache;
       * one GPU's share of an 8-way split (KV heads a multiple of 8): the
         gate on an eighth of the tokens and the attention of an eighth of the
         KV heads (with their query heads) over all the kept rows;
@@ -236,6 +237,18 @@ def reference_points(tg, w, gp, layers, outs, hidden, W1, b1, w2, stream, dev):
     r["decode_step_us"] = t * 1e3
     r["decode_step_GBps"] = 2.0 * Kt * s.Hkv * s.d * q.element_size() / (t / 1e3) / 1e9
     del lens, qd, wsd, outd
+    # the prefill's kept k, v and bias into a cache with room for 16 new
+    # tokens per sequence (read and written once)
+    startc = (torch.from_numpy(gp.cu_kept_h[:-1].astype(np.int64)) + 16 * torch.arange(gp.B)).to(torch.int32).to(dev)
+    kcache = torch.empty((Kt + 16 * gp.B, s.Hkv, s.d), dtype=q.dtype, device=dev)
+    vcache = torch.empty_like(kcache)
+    bcache = torch.empty(Kt + 16 * gp.B, dtype=torch.float32, device=dev)
+    scat = lambda: tg.tg_kv_scatter(k, v, gp.bias_s, gp.cu_kept, kcache, vcache, bcache, startc)  # noqa: E731
+    scat()
+    t = time_launches(scat, stream, reps=5, n=5)
+    r["kv_scatter_us"] = t * 1e3
+    r["kv_scatter_GBps"] = (4.0 * Kt * s.Hkv * s.d * q.element_size() + 8.0 * Kt) / (t / 1e3) / 1e9
+    del startc, kcache, vcache, bcache
 
     # gate MLP backward from the kept rows' bias gradient
     dbias = torch.randn(Kt, device=dev)

@@ -8,7 +8,8 @@
 // Cache layout (per pruned layer): rows [rows, Hkv, d] for k and v with
 // token strides, a bias per row (fp32); sequence b owns rows start[b] ..
 // start[b] + len[b] - 1, with room after them for the tokens it generates.
-//   kv_scatter   prefill's compacted rows (ragged by cu_kept) into the cache.
+//   kv_scatter   prefill's compacted rows (ragged by cu_kept) into the cache,
+//                in 16-byte units when alignment and strides allow.
 //   kv_append    each step's new k, v at row start[b] + pos[b], bias 0.
 //   decode_split one workgroup of 4 waves per (sequence, KV head, split of 128
 //                keys, 256 once the grid holds about 8 workgroups per CU): a
@@ -92,6 +93,31 @@ __global__ __launch_bounds__(256) void kv_scatter_kernel(const T* __restrict__ k
   const int64_t dst = (int64_t)start[lo] + (r - cu[lo]);
   kc[dst * ks + e] = k[r * sks + e];
   vc[dst * vs + e] = v[r * svs + e];
+  if (e == 0) bc[dst] = bias ? bias[r] : 0.0f;
+}
+
+// The same copy in 16-byte units (pointers 16-byte aligned, strides and the
+// row's Hkv * d elements a whole number of 16-byte units): thread i moves
+// unit i % row_units of kept row i / row_units, all in bytes.
+__global__ __launch_bounds__(256) void kv_scatter16_kernel(const char* __restrict__ k, const char* __restrict__ v,
+                                                           int64_t sks, int64_t svs, const float* __restrict__ bias,
+                                                           const int32_t* __restrict__ cu, int B, int64_t Kt,
+                                                           int row_units, char* __restrict__ kc, char* __restrict__ vc,
+                                                           int64_t ks, int64_t vs, float* __restrict__ bc,
+                                                           const int32_t* __restrict__ start) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i >= Kt * row_units) return;
+  const int64_t r = i / row_units;
+  const int64_t e = (i - r * row_units) * 16;
+  int lo = 0, hi = B;  // prompt b with cu[b] <= r < cu[b + 1]
+  while (hi - lo > 1) {
+    const int mid = (lo + hi) / 2;
+    if (cu[mid] <= r) lo = mid;
+    else hi = mid;
+  }
+  const int64_t dst = (int64_t)start[lo] + (r - cu[lo]);
+  *reinterpret_cast<uint4*>(kc + dst * ks + e) = *reinterpret_cast<const uint4*>(k + r * sks + e);
+  *reinterpret_cast<uint4*>(vc + dst * vs + e) = *reinterpret_cast<const uint4*>(v + r * svs + e);
   if (e == 0) bc[dst] = bias ? bias[r] : 0.0f;
 }
 
@@ -326,6 +352,18 @@ hipError_t launch_kv_scatter(const void* k, const void* v, int64_t sks, int64_t 
                              void* vc, int64_t ks, int64_t vs, float* bc, const int32_t* start, hipStream_t s) {
   const int64_t total = Kt * Hkv * d;
   if (total == 0) return hipSuccess;
+  const int64_t row_bytes = (int64_t)Hkv * d * elem_bytes;
+  const auto a16 = [](const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; };
+  if (row_bytes % 16 == 0 && (sks * elem_bytes) % 16 == 0 && (svs * elem_bytes) % 16 == 0 &&
+      (ks * elem_bytes) % 16 == 0 && (vs * elem_bytes) % 16 == 0 && a16(k) && a16(v) && a16(kc) && a16(vc)) {
+    const int row_units = (int)(row_bytes / 16);
+    const int64_t n = Kt * row_units;
+    hipLaunchKernelGGL(kv_scatter16_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s,
+                       static_cast<const char*>(k), static_cast<const char*>(v), sks * elem_bytes, svs * elem_bytes,
+                       bias, cu, B, Kt, row_units, static_cast<char*>(kc), static_cast<char*>(vc), ks * elem_bytes,
+                       vs * elem_bytes, bc, start);
+    return hipGetLastError();
+  }
   const dim3 grid((unsigned)((total + 255) / 256));
   if (elem_bytes == 2)
     hipLaunchKernelGGL(kv_scatter_kernel<uint16_t>, grid, dim3(256), 0, s, static_cast<const uint16_t*>(k),

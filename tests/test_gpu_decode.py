@@ -127,6 +127,59 @@ def test_decode_attn_random(seed):
     _note(f"  worst error / bar {w:.3f}")
 
 
+@pytest.mark.parametrize("dtype,d,pad_src,pad_dst,offset", [
+    (torch.bfloat16, 128, 0, 0, 0),   # 16-byte units
+    (torch.bfloat16, 64, 8, 16, 0),   # padded rows, still whole 16-byte units
+    (torch.bfloat16, 128, 4, 0, 0),   # source rows 8 bytes past a unit: element copy
+    (torch.bfloat16, 64, 0, 0, 1),    # cache one element off 16-byte alignment: element copy
+    (torch.float32, 64, 0, 4, 0),     # fp32, 16-byte units
+    (torch.float32, 128, 1, 0, 0),    # fp32, source stride 4 bytes past a unit: element copy
+])
+def test_kv_scatter_layouts(dtype, d, pad_src, pad_dst, offset):
+    """tg_kv_scatter against the cache built on the host, bit for bit, for
+    the 16-byte copy and the element copy it falls back to."""
+    rng = np.random.default_rng(d + pad_src + pad_dst + offset)
+    Hkv = 4
+    lens = [int(x) for x in rng.integers(0, 300, 7)]
+    lens[2] = 0
+    cu = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
+    Kt, B = int(cu[-1]), len(lens)
+    room = 5
+    start = (cu[:-1] + np.arange(B) * room).astype(np.int32)
+    rows = Kt + B * room
+    row = Hkv * d
+    g = torch.Generator().manual_seed(3)
+    ksrc = torch.randn((Kt, row + pad_src), generator=g).to(dtype)
+    vsrc = torch.randn((Kt, row + pad_src), generator=g).to(dtype)
+    bias = torch.randn(Kt, generator=g)
+    view = lambda t: t.as_strided((Kt, Hkv, d), (row + pad_src, d, 1))  # noqa: E731  token rows of row + pad_src
+    k, v = view(ksrc), view(vsrc)
+    kd, vd = view(ksrc.to(DEV)), view(vsrc.to(DEV))
+    n_el = rows * (row + pad_dst) + offset
+    kbuf = torch.full((n_el,), 7, dtype=dtype, device=DEV)
+    vbuf = torch.full((n_el,), 7, dtype=dtype, device=DEV)
+    kc = kbuf[offset:].as_strided((rows, Hkv, d), (row + pad_dst, d, 1))
+    vc = vbuf[offset:].as_strided((rows, Hkv, d), (row + pad_dst, d, 1))
+    bc = torch.full((rows,), 9.0, device=DEV)
+    tg.tg_kv_scatter(kd, vd, bias.to(DEV), torch.from_numpy(cu).to(DEV), kc, vc, bc, torch.from_numpy(start).to(DEV))
+    torch.cuda.synchronize()
+    Kh = torch.full((rows, Hkv, d), 7, dtype=dtype)
+    Vh = torch.full((rows, Hkv, d), 7, dtype=dtype)
+    Bh = torch.full((rows,), 9.0)
+    for b in range(B):
+        n = lens[b]
+        Kh[start[b]:start[b] + n] = k[cu[b]:cu[b + 1]]
+        Vh[start[b]:start[b] + n] = v[cu[b]:cu[b + 1]]
+        Bh[start[b]:start[b] + n] = bias[cu[b]:cu[b + 1]]
+    bits = torch.int16 if dtype == torch.bfloat16 else torch.int32
+    assert torch.equal(kc.cpu().view(bits), Kh.view(bits))
+    assert torch.equal(vc.cpu().view(bits), Vh.view(bits))
+    assert torch.equal(bc.cpu(), Bh)
+    if pad_dst:  # the padding between cache rows is untouched
+        pad = kbuf.cpu()[offset:].reshape(rows, row + pad_dst)[:, row:]
+        assert torch.all(pad.float() == 7.0)
+
+
 def test_decode_steps_from_prefill_cache():
     """The ragged workload's kept layout: the prefill's kept k, v and bias
     scattered into a cache with room per sequence, then 5 decode steps each
