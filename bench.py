@@ -127,8 +127,9 @@ def reference_points(tg, w, gp, layers, outs, hidden, W1, b1, w2, stream, dev):
         temperature switched off (gain = NULL, tau = 1), as a ratio;
       * the dense comparator: full-length causal GQA attention (no pruning, no
         bias) at 32768 tokens with the same head shapes;
-      * gate and attention launches after a 1 GiB write that evicts L2 and
-        the last-level cache (the timed step runs them back to back);
+      * gate, top-K, compaction and attention launches, each after a 1 GiB
+        write that evicts L2 and the last-level cache (the timed step runs
+        them back to back);
       * a whole pruned layer on the kept rows, beside the step (seeded
         weights of the layer's shapes): the rotary table of the kept rows'
         positions, and per layer RMSNorm, the fused q/k/v projection with the
@@ -287,7 +288,14 @@ def reference_points(tg, w, gp, layers, outs, hidden, W1, b1, w2, stream, dev):
     flush_buf = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
     flush = lambda: flush_buf.fill_(1)  # noqa: E731
     gate = lambda: tg.tg_gate_score(hidden, W1, b1, w2, w.b2, scores=gp.scores)  # noqa: E731
+    sel = lambda: tg.tg_select_topk(gp.scores, gp.cu_seqlens, gp.doc_begin, gp.doc_end, gp.budget,  # noqa: E731
+                                    keep=gp.keep, workspace=gp.ws_select)
+    cmp = lambda: tg.tg_compact(hidden, None, gp.scores, gp.keep, gp.cu_seqlens, gp.doc_begin,  # noqa: E731
+                                gp.doc_end, gp.Kt, out=(gp.hidden_k, gp.pos_k, gp.bias_s, gp.kept_idx),
+                                workspace=gp.ws_compact)
     r["gate_us_after_cache_flush"] = time_launches(gate, stream, reps=7, n=1, before=flush) * 1e3
+    r["select_us_after_cache_flush"] = time_launches(sel, stream, reps=7, n=1, before=flush) * 1e3
+    r["compact_us_after_cache_flush"] = time_launches(cmp, stream, reps=7, n=1, before=flush) * 1e3
     r["attn_us_after_cache_flush"] = time_launches(gated, stream, reps=7, n=1, before=flush) * 1e3
     del flush_buf
 
